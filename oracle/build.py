@@ -1,0 +1,29 @@
+"""Build the fp64 CPU oracle (test infrastructure) into oracle/liboracle.so.
+
+Plain gcc, -O2, no fast-math and no floating-point contraction, so every
+operation in ssm_oracle.c is one IEEE fp64 rounding. OpenMP only spreads
+independent (row, head) units over threads.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "ssm_oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off",
+           "-fno-fast-math", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-o", tmp, SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))
