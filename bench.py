@@ -1,0 +1,420 @@
+"""Benchmark of the GDN single-token decode step on one MI355X.
+
+Headline: state GB/s (and % of the 8 TB/s HBM peak) and us/step of
+gdn_decode_step at B=256 rows over a 264-slot pool (H=16, HV=32, K=V=128,
+bf16 activations, fp32 state), inputs resident in HBM. A step is one
+gdn_decode_step call; consecutive steps rotate over several state pools so
+the 256 MB Infinity Cache cannot hold the state between steps.
+
+The same JSON line also carries the latency-to-bandwidth sweep (B = 1, 16,
+64, 256 under HIP-graph replay of one call per pool), the buffered variant
+(B=64, L = 1/8/16, exact cycle mean), the fused KDA step (T=64, 96 heads),
+a same-size stream-copy ceiling, the roofline entry of the dominant kernel
+and the fp64 oracle's rate on the host cores.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+  python bench.py --profile-pass     # short run for rocprofv3 counter passes
+  python bench.py --summarize-counters FETCH_DIR WRITE_DIR --out profiles/X.txt
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 * 2 ** 20
+KERNEL_SOURCES = ["ssm_recurrent_decode_gated_amd/csrc/gdn_decode.hip",
+                  "ssm_recurrent_decode_gated_amd/csrc/ssmd_device.h"]
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "gdn_b256_of264_hbm_counters.txt")
+METRIC = "state GB/s (% of HBM peak) and µs/step, GDN decode HV=32 K=V=128, B=1/16/256"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------ byte models
+def gdn_state_bytes(B, HV, V, K):
+    """State traffic of one packed step: each named head is read and written once."""
+    return 2 * B * HV * V * K * 4
+
+
+def gdn_alg_bytes(B, H, HV, K, V, act=2, outb=2):
+    """All algorithmic bytes of one packed launch: state read+write, mixed_qkv,
+    a, b, A_log, dt_bias, slot indices and the output."""
+    return (gdn_state_bytes(B, HV, V, K) + B * (2 * H * K + HV * V) * act + 2 * B * HV * act
+            + 2 * HV * 4 + B * 4 + B * HV * V * outb)
+
+
+# ------------------------------------------------------------ helpers
+def _events_ms(fn, reps, stream):
+    import torch
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(reps):
+        fn()
+    e.record(stream)
+    e.synchronize()
+    return s.elapsed_time(e)
+
+
+def _pools_for(pool_bytes, min_total=4 * MALL_BYTES, cap=64):
+    return max(2, min(cap, -(-min_total // pool_bytes)))
+
+
+class GDNSetup:
+    """Device-resident inputs of one GDN workload, with M state pools."""
+
+    def __init__(self, w, pools, dev, out_dtype="bf16"):
+        import torch
+        import workloads as W
+        self.w = w
+        self.P = W.gdn_params(w)
+        self.x = W.gdn_step_inputs(w)
+        self.idx = W.slot_indices(w)
+        st = W.gdn_state(w)
+        self.state_host = st
+        d = {k: v.to(dev) for k, v in self.x.items()}
+        self.qkv, self.a, self.b = d["qkv"], d["a"], d["b"]
+        self.A_log, self.dt_bias = self.P["A_log"].to(dev), self.P["dt_bias"].to(dev)
+        self.idx_d = self.idx.to(dev)
+        first = st.to(dev)
+        self.pools = [first] + [first.clone() for _ in range(pools - 1)]
+        self.out = torch.empty(w.B, 1, w.HV, w.V, dtype=W.DTYPES[out_dtype], device=dev)
+
+    def call(self, i):
+        import ssm_recurrent_decode_gated_amd as S
+        S.gdn_decode_step(self.qkv, self.a, self.b, self.A_log, self.dt_bias, self.pools[i % len(self.pools)],
+                          self.idx_d, self.out)
+
+
+def graph_time_us(calls, reps, stream):
+    """us per call for a HIP graph holding `calls` (one launch each), replayed."""
+    import torch
+    for c in calls:  # warm (and first-touch) outside the capture
+        c()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = _events_ms(g.replay, reps, torch.cuda.current_stream())
+    return ms * 1e3 / (reps * len(calls))
+
+
+# ------------------------------------------------------------ legs
+def headline(dev, steps, warmup):
+    import torch
+    import workloads as W
+    w = W.GDN_B256
+    pool_bytes = w.num_slots * w.HV * w.V * w.K * 4
+    M = _pools_for(pool_bytes)
+    su = GDNSetup(w, M, dev)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        su.call(i)
+    torch.cuda.synchronize()
+    it = iter(range(10 ** 9))
+    ms = _events_ms(lambda: su.call(next(it)), steps, stream)
+    torch.cuda.synchronize()
+    us = ms * 1e3 / steps
+    sb = gdn_state_bytes(w.B, w.HV, w.V, w.K)
+    ab = gdn_alg_bytes(w.B, w.H, w.HV, w.K, w.V)
+    return {"w": w, "pools": M, "us": us, "state_gbs": sb / us / 1e3, "alg_gbs": ab / us / 1e3,
+            "alg_bytes": ab, "state_bytes": sb, "setup": su}
+
+
+def sweep(dev, batches=(1, 16, 64, 256), reps=50):
+    import workloads as W
+    import torch
+    res = {}
+    for B in batches:
+        w = W.gdn_sweep(B)
+        pool_bytes = w.num_slots * w.HV * w.V * w.K * 4
+        M = _pools_for(pool_bytes)
+        su = GDNSetup(w, M, dev)
+        us = graph_time_us([lambda i=i: su.call(i) for i in range(M)], reps, torch.cuda.current_stream())
+        sb = gdn_state_bytes(B, w.HV, w.V, w.K)
+        res[f"B{B}"] = {"us_per_step": round(us, 3), "state_GBps": round(sb / us / 1e3, 1),
+                        "pct_hbm_peak": round(100 * sb / us / 1e3 / HBM_PEAK_GBS, 2), "pools": M}
+        del su
+        torch.cuda.empty_cache()
+    return res
+
+
+def copy_ceiling(dev, nbytes=2 * 2 ** 30, reps=20):
+    import torch
+    import ssm_recurrent_decode_gated_amd as S
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).normal_()
+    dst = torch.empty_like(src)
+    S.ssmd_stream_copy(src, dst)
+    torch.cuda.synchronize()
+    ms = _events_ms(lambda: S.ssmd_stream_copy(src, dst), reps, torch.cuda.current_stream())
+    gbs = 2 * nbytes * reps / (ms * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_moved_per_copy": 2 * nbytes, "GBps": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+
+
+def buffered(dev, Ls=(1, 8, 16), reps=30):
+    import torch
+    import ssm_recurrent_decode_gated_amd as S
+    import workloads as W
+    w = W.GDN_B64_CHAIN
+    pool_bytes = w.num_slots * w.HV * w.V * w.K * 4
+    M = _pools_for(pool_bytes)
+    su = GDNSetup(w, M, dev)
+    out = {}
+    for L in Ls:
+        rings = [{"d": torch.zeros(w.num_slots, w.HV, L, w.V, dtype=torch.bfloat16, device=dev),
+                  "k": torch.zeros(w.num_slots, w.H, L, w.K, dtype=torch.bfloat16, device=dev),
+                  "g": torch.zeros(w.num_slots, w.HV, L, device=dev)} for _ in range(M)]
+        wps = [torch.full((w.B,), p, dtype=torch.int32, device=dev) for p in range(L)]
+
+        def call(i, p):
+            r = rings[i]
+            S.gdn_decode_step_buffered(su.qkv, su.a, su.b, su.A_log, su.dt_bias, su.pools[i], su.idx_d,
+                                       su.out, r["d"], r["k"], r["g"], wps[p])
+        # one cycle on every pool: L launches per pool, phases 0..L-1 in order
+        calls = [lambda i=i, p=p: call(i, p) for p in range(L) for i in range(M)]
+        us = graph_time_us(calls, reps, torch.cuda.current_stream())
+        per_phase = {}
+        for p in sorted({0, (L - 1) // 2, L - 1}):
+            per_phase[p] = round(graph_time_us([lambda i=i, p=p: call(i, p) for i in range(M)], reps,
+                                               torch.cuda.current_stream()), 3)
+        state_b = w.B * w.HV * w.V * w.K * 4 * (1 + 1.0 / L)
+        out[f"L{L}"] = {"cycle_mean_us": round(us, 3), "phase_us": per_phase,
+                        "state_GBps": round(state_b / us / 1e3, 1),
+                        "state_bytes_ratio_vs_packed": round((1 + 1.0 / L) / 2, 5)}
+        del rings
+    del su
+    torch.cuda.empty_cache()
+    return out
+
+
+def kda(dev, reps=30):
+    import torch
+    import ssm_recurrent_decode_gated_amd as S
+    import workloads as W
+    w = W.KDA_T64
+    d = W.kda_inputs(w)
+    pool_bytes = w.num_slots * w.H * w.D * w.D * 4
+    M = _pools_for(pool_bytes)
+    first = d["state"].to(dev)
+    pools = [first] + [first.clone() for _ in range(M - 1)]
+    cs = [d["conv_state"].to(dev) for _ in range(M)]
+    dd = {k: d[k].to(dev) for k in ("x", "conv_weight", "raw_g", "raw_beta", "gate", "norm_weight", "idx")}
+    out = torch.empty(w.T, w.H, w.D, dtype=torch.bfloat16, device=dev)
+
+    def call(i):
+        S.kda_decode_step(dd["x"], dd["conv_weight"], None, cs[i], dd["raw_g"], dd["raw_beta"], None, None,
+                          pools[i], dd["idx"], out, output_gate=dd["gate"], norm_weight=dd["norm_weight"])
+    us = graph_time_us([lambda i=i: call(i) for i in range(M)], reps, torch.cuda.current_stream())
+    sb = w.T * w.H * w.D * w.D * 4 * 2
+    del pools, cs
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "us_per_step": round(us, 3), "state_GBps": round(sb / us / 1e3, 1),
+            "pct_hbm_peak": round(100 * sb / us / 1e3 / HBM_PEAK_GBS, 2), "pools": M}
+
+
+def cpu_baseline(su, target_s=10.0):
+    """The fp64 oracle, as it stands, on the host cores: the full B=256 step
+    repeated (state evolving) until about target_s seconds have passed."""
+    import numpy as np
+    import oracle as O
+    w = su.w
+    ref = su.state_host.double().numpy().copy()
+    q, a, b = O.f64(su.x["qkv"]), O.f64(su.x["a"]), O.f64(su.x["b"])
+    idx = su.idx.numpy().astype(np.int32)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        O.gdn_step(q, a, b, su.P["A_log"], su.P["dt_bias"], ref, idx, H=w.H, HV=w.HV, K=w.K, V=w.V)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+    sb = gdn_state_bytes(w.B, w.HV, w.V, w.K) * n
+    return {"value": round(sb / el / 1e9, 3), "unit": "GB/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"full B=256-of-264 step (H=16, HV=32, K=V=128) repeated {n} times in {el:.1f} s; "
+                      "fp32-state byte model"}
+
+
+def counters_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since it was taken."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    kv = {}
+    for line in open(COUNTERS_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        copy_kib = float(kv["copy_bytes"]) / 1024
+        ff = copy_kib / float(kv["copy_fetch_kib"])
+        wf = copy_kib / float(kv["copy_write_kib"])
+        return float(kv["gdn_fetch_kib"]) * 1024 * ff + float(kv["gdn_write_kib"]) * 1024 * wf
+    except (KeyError, ValueError, ZeroDivisionError):
+        return None
+
+
+# ------------------------------------------------------------ rocprofv3 helpers
+def profile_pass():
+    """A few launches of the headline kernel and one copy of known size."""
+    import torch
+    import ssm_recurrent_decode_gated_amd as S
+    import workloads as W
+    dev = torch.device("cuda:0")
+    su = GDNSetup(W.GDN_B256, 2, dev)
+    for i in range(6):
+        su.call(i)
+    n = 1 << 30
+    src = torch.ones(n // 4, device=dev)
+    dst = torch.empty_like(src)
+    S.ssmd_stream_copy(src, dst)
+    torch.cuda.synchronize()
+    print(f"profile pass done: 6 x gdn_decode_step B=256, 1 x stream copy of {n} bytes", flush=True)
+
+
+def _read_counter_csv(d, counter):
+    import csv
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    per = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r.get("Counter_Name") != counter:
+                continue
+            name = r.get("Kernel_Name", "")
+            key = "gdn" if "gdn_decode_kernel" in name else ("copy" if "stream_copy_kernel" in name else None)
+            if key:
+                per.setdefault(key, {}).setdefault(r.get("Dispatch_Id"), 0.0)
+                per[key][r.get("Dispatch_Id")] += float(r["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in per.items()}
+
+
+def summarize_counters(fetch_dir, write_dir, out, command):
+    f = _read_counter_csv(fetch_dir, "FETCH_SIZE")
+    w = _read_counter_csv(write_dir, "WRITE_SIZE")
+    import workloads as W
+    wl = W.GDN_B256
+    alg = gdn_alg_bytes(wl.B, wl.H, wl.HV, wl.K, wl.V)
+    copy_bytes = 1 << 30
+    ff, wf = copy_bytes / 1024 / f["copy"], copy_bytes / 1024 / w["copy"]
+    traffic = f["gdn"] * 1024 * ff + w["gdn"] * 1024 * wf
+    lines = [
+        "# rocprofv3 HBM counters, gdn_decode_kernel at B=256 of 264 slots (H=16 HV=32 K=V=128, bf16 act)",
+        f"# command: {command}",
+        "# values are KiB per dispatch, averaged over dispatches; the copy kernel moves copy_bytes each way",
+        f"kernel_source_sha256 = {kernel_source_hash()}",
+        f"gdn_fetch_kib = {f['gdn']:.1f}",
+        f"gdn_write_kib = {w['gdn']:.1f}",
+        f"copy_bytes = {copy_bytes}",
+        f"copy_fetch_kib = {f['copy']:.1f}",
+        f"copy_write_kib = {w['copy']:.1f}",
+        f"# fetch scale {ff:.4f}, write scale {wf:.4f}",
+        f"# scaled HBM traffic per gdn launch = {traffic / 1e6:.2f} MB; algorithmic = {alg / 1e6:.2f} MB "
+        f"(ratio {traffic / alg:.4f})",
+    ]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+# ------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="headline only (no sweep/buffered/KDA/copy)")
+    ap.add_argument("--profile-pass", action="store_true")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--out", default=COUNTERS_FILE)
+    ap.add_argument("--command", default="")
+    args = ap.parse_args()
+
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.out, args.command)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the decode step has no cross-GPU exchange and this build "
+              "runs on a single MI355X; --gpus above 1 is not supported.", file=sys.stderr)
+        sys.exit(1)
+    if args.profile_pass:
+        profile_pass()
+        return
+
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    import ssm_recurrent_decode_gated_amd as S
+    S.load_library()
+
+    torch.cuda.synchronize()
+    h = headline(dev, args.steps, args.warmup)
+    torch.cuda.synchronize()
+    extra = {"eager_us_per_step": round(h["us"], 3)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(h["setup"])
+    del h["setup"]
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        extra["copy_ceiling"] = copy_ceiling(dev)
+        extra["graph_sweep"] = sweep(dev)
+        extra["buffered_b64"] = buffered(dev)
+        extra["kda_t64_h96"] = kda(dev)
+        extra["pct_of_copy_ceiling"] = round(100 * h["state_gbs"] / extra["copy_ceiling"]["GBps"], 2)
+    w = h["w"]
+    traffic = counters_traffic()
+    line = {
+        "metric": METRIC,
+        "value": round(h["state_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["us"] / 1e3, 6),
+        "us_per_step": round(h["us"], 3),
+        "pct_hbm_peak": round(100 * h["state_gbs"] / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded randn, the pages' distributions)",
+        "config": {"workload": w.name, "B": w.B, "num_slots": w.num_slots, "H": w.H, "HV": w.HV, "K": w.K,
+                   "V": w.V, "act_dtype": w.act, "out_dtype": w.out, "state_dtype": "f32",
+                   "state_pools_rotated": h["pools"], "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(h["alg_gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(h["alg_gbs"] / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "algorithmic_bytes_per_launch": h["alg_bytes"], "kernel": "gdn_decode_kernel"},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

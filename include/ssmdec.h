@@ -1,0 +1,210 @@
+/*
+ * ssmdec.h -- C ABI of the MI355X (gfx950) single-token recurrent decode
+ * library for gated linear-attention layers: the gated delta rule (GDN /
+ * DeltaNet / KDA) over an fp32 state pool, updated in place.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [REPLAY] "Microbenchmark: buffered output-only GDN decode (ReplaySSM
+ *            Part A) vs. the existing packed GDN decode kernel"
+ *   [KDA]    "Microbenchmark for the fused Kimi-K3 KDA decode kernel on ROCm"
+ *   [LOG]    "Optimization Log: Qwen3.5-27B Dense on B200"
+ *   [MBU]    "Triton decode kernel + MBU analysis"
+ *
+ * Conventions for every call:
+ *   - Every pointer argument is a DEVICE pointer (memory of the current HIP
+ *     device), except where stated. The caller allocates and owns all
+ *     buffers; the library never allocates, frees or keeps a workspace.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream). No
+ *     call synchronises, reads device memory on the host or allocates, so
+ *     every call can be captured into a HIP graph.
+ *   - Arguments are validated on the host before anything is launched. On
+ *     error nothing is launched, the call returns a negative SSMD_ERR_* code
+ *     and ssmd_last_error() describes it.
+ *   - Out-of-range slot indices are not errors: they mark padded rows, which
+ *     read and write nothing (their `out` rows are left as they were). Two
+ *     active rows naming the same slot in one call is a precondition
+ *     violation with an undefined result.
+ *   - Activation tensors (dtype SSMD_BF16 / SSMD_F16 / SSMD_F32) must be
+ *     aligned to 4 elements (8 bytes for 16-bit types, 16 for fp32), with row
+ *     strides that are multiples of 4 elements; fp32 states must be 16-byte
+ *     aligned.
+ *   - Calls are reentrant; the only global state is the thread-local error
+ *     string.
+ */
+#ifndef SSMDEC_H
+#define SSMDEC_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define SSMD_OK 0
+#define SSMD_ERR_NULL_ARG (-1)    /* a required pointer is NULL */
+#define SSMD_ERR_BAD_SHAPE (-2)   /* sizes, strides or alignment are inconsistent */
+#define SSMD_ERR_BAD_DTYPE (-3)   /* unknown dtype or activation code */
+#define SSMD_ERR_UNSUPPORTED (-4) /* head size not compiled in */
+#define SSMD_ERR_LAUNCH (-5)      /* the HIP runtime refused the launch */
+
+/* element types */
+#define SSMD_F32 0
+#define SSMD_BF16 1
+#define SSMD_F16 2
+
+/* gate activation of the output gated RMSNorm */
+#define SSMD_ACT_SILU 0
+#define SSMD_ACT_SIGMOID 1
+
+/*
+ * gdn_decode_step -- one packed GDN decode step for B rows.
+ *
+ * Defines ([REPLAY] module docstring, `_make_static`, `_bench_cfg`; [LOG]
+ * "Kernel 4: Fused DeltaNet Recurrent", Math): for every row b whose slot
+ * s = ssm_state_indices[b] is in [0, num_slots), and every value head hv
+ * (q/k head h = hv / (HV/H)):
+ *   q, k  = the h-th K-slices of the q and k blocks of mixed_qkv[b];
+ *   v     = the hv-th V-slice of its v block;
+ *   if use_qk_l2norm: q <- q / sqrt(|q|^2 + l2norm_eps), same for k;
+ *   q    <- scale * q;
+ *   g     = -exp(A_log[hv]) * softplus(a[b,hv] + dt_bias[hv]);
+ *   beta  = sigmoid(b[b,hv]);
+ *   S     = state[s, hv]                (V x K, row = value index)
+ *   S    <- exp(g) S;  delta = beta (v - S k);  S <- S + delta k^T;  o = S q;
+ *   if norm_gate: o <- o / sqrt(mean(o^2) + norm_eps) * w * act(norm_gate[b,hv])
+ *                 (w = norm_weight, or ones when NULL; act per norm_act);
+ *   out[b, 0, hv, :] = o (rounded to out_dtype, RNE).
+ *
+ * Arguments and layouts (row-major):
+ *   mixed_qkv  [B, row stride qkv_row_stride >= 2*H*K + HV*V] act_dtype:
+ *              q heads (H*K) | k heads (H*K) | v heads (HV*V)
+ *   a, b       [B, HV] act_dtype gate logits (contiguous)
+ *   A_log      [HV] fp32;  dt_bias [HV] fp32
+ *   state      [num_slots, HV, V, K] fp32, updated in place
+ *   ssm_state_indices [B] int32
+ *   out        [B, 1, HV, V] out_dtype
+ *   norm_gate  [B, HV, V] act_dtype or NULL (no output norm)
+ *   norm_weight [V] fp32 or NULL (ones)
+ *   K in {16, 32, 64, 128, 256}; 1 <= V <= 1024; HV % H == 0; B >= 0 (B == 0
+ *   is a no-op).
+ */
+int gdn_decode_step(const void* mixed_qkv, int64_t qkv_row_stride,
+                    const void* a, const void* b,
+                    const float* A_log, const float* dt_bias,
+                    float* state, int32_t num_slots,
+                    const int32_t* ssm_state_indices,
+                    void* out,
+                    int32_t B, int32_t H, int32_t HV, int32_t K, int32_t V,
+                    int32_t act_dtype, int32_t out_dtype,
+                    float scale, int32_t use_qk_l2norm, float l2norm_eps,
+                    const void* norm_gate, const float* norm_weight,
+                    float norm_eps, int32_t norm_act,
+                    hipStream_t stream);
+
+/*
+ * gdn_decode_step_buffered -- the GDN step with the state written back only
+ * once every L steps ([REPLAY] module docstring, `_bench_cfg`,
+ * `_state_bytes_per_step`, `_amortize`).
+ *
+ * The pool `state` holds a checkpoint. Per row b with phase p = write_pos[b]
+ * (0 <= p < L; other values pad the row), the ring holds the records of
+ * phases 0..p-1 of the current cycle:
+ *   d_cache [num_slots, HV, L, V] act_dtype  -- that step's delta
+ *   k_cache [num_slots, H,  L, K] act_dtype  -- that step's normalised key
+ *                                               (one per q/k head)
+ *   g_cache [num_slots, HV, L]    fp32       -- that step's log decay g
+ * The call computes this step's output exactly as gdn_decode_step would from
+ * the state S_{p-1} obtained by replaying records 0..p-1 on the checkpoint
+ * (S <- exp(g_j) S + d_j k_j^T), appends this step's record at position p
+ * (delta and k rounded RNE to act_dtype, g as fp32), and, only when
+ * p == L-1, writes the folded state S_p back to `state`. write_pos is read
+ * only: the caller advances it to (p + 1) % L between calls. With L == 1 the
+ * call computes what gdn_decode_step computes. Ring entries past p are
+ * don't-care; a zeroed ring with write_pos = 0 is a cold start.
+ * All other arguments are those of gdn_decode_step.
+ */
+int gdn_decode_step_buffered(const void* mixed_qkv, int64_t qkv_row_stride,
+                             const void* a, const void* b,
+                             const float* A_log, const float* dt_bias,
+                             float* state, int32_t num_slots,
+                             const int32_t* ssm_state_indices,
+                             void* out,
+                             int32_t B, int32_t H, int32_t HV, int32_t K, int32_t V,
+                             int32_t act_dtype, int32_t out_dtype,
+                             float scale, int32_t use_qk_l2norm, float l2norm_eps,
+                             const void* norm_gate, const float* norm_weight,
+                             float norm_eps, int32_t norm_act,
+                             void* d_cache, void* k_cache, float* g_cache,
+                             const int32_t* write_pos, int32_t L,
+                             hipStream_t stream);
+
+/*
+ * kda_decode_step -- the fused KDA decode op: causal conv1d update + SiLU,
+ * per-key-channel gated delta rule, sigmoid-gated RMSNorm, in one launch
+ * ([KDA] module docstring, `triton_chain` and `fused`, `_gated_rmsnorm`;
+ * [LOG] "Kernel 5: Fused Causal Conv1d Update").
+ *
+ * Per token t with slot s = state_indices[t] in [1, num_slots) (slot 0 is the
+ * NULL block and is skipped, as are out-of-range slots), channel
+ * c < C = 3*H*D:
+ *   window = [conv_state[s, c, 0..W-2], x[t, c]]  (oldest first)
+ *   y[c]   = silu(sum_j conv_weight[c, j] window[j] + conv_bias[c])
+ *   conv_state[s, c, :] <- window[1..W-1]
+ * y = [q | k | v], each [H, D]. Per head h:
+ *   if use_qk_l2norm: q, k L2-normalised (eps l2norm_eps); q <- scale * q;
+ *   g[i]  = lower_bound * sigmoid(exp(A_log[h]) * (raw_g[t,h,i] + dt_bias[h*D+i]))
+ *           (A_log / dt_bias NULL = 0, giving lower_bound * sigmoid(raw_g));
+ *   beta  = sigmoid(raw_beta[t, h]);
+ *   S = state[s, h] (D x D, row = value index):
+ *   S <- S diag(exp(g)); delta = beta (v - S k); S <- S + delta k^T; o = S q;
+ *   if output_gate: o <- o / sqrt(mean(o^2) + norm_eps) * w * sigmoid(output_gate[t,h])
+ *   out[t, h, :] = o (bf16 when out_dtype = SSMD_BF16, etc.)
+ *
+ *   x            [T, C] act_dtype (contiguous)
+ *   conv_weight  [C, W] fp32; conv_bias [C] fp32 or NULL
+ *   conv_state   logical [num_slots, C, W-1] act_dtype at element strides
+ *                (cs_slot_stride, cs_chan_stride, cs_tap_stride): the SD
+ *                layout [num_slots, W-1, C] has strides ((W-1)*C, 1, C),
+ *                the DS layout [num_slots, C, W-1] has (C*(W-1), W-1, 1)
+ *   raw_g        [T, H, D] act_dtype; raw_beta [T, H] act_dtype
+ *   A_log [H] fp32 or NULL; dt_bias [H*D] fp32 or NULL
+ *   state        [num_slots, H, D, D] fp32, in place
+ *   out          [T, H, D] out_dtype
+ *   output_gate  [T, H, D] act_dtype or NULL (no norm); norm_weight [D] fp32 or NULL
+ *   D in {16, 32, 64, 128, 256}; 2 <= W <= 8; T >= 0.
+ */
+int kda_decode_step(const void* x,
+                    const float* conv_weight, const float* conv_bias,
+                    void* conv_state, int64_t cs_slot_stride,
+                    int64_t cs_chan_stride, int64_t cs_tap_stride,
+                    const void* raw_g, const void* raw_beta,
+                    const float* A_log, const float* dt_bias,
+                    float lower_bound,
+                    float* state, int32_t num_slots,
+                    const int32_t* state_indices,
+                    void* out,
+                    const void* output_gate, const float* norm_weight,
+                    float norm_eps,
+                    int32_t T, int32_t H, int32_t D, int32_t W,
+                    int32_t act_dtype, int32_t out_dtype,
+                    float scale, int32_t use_qk_l2norm, float l2norm_eps,
+                    hipStream_t stream);
+
+/* Message for the last non-zero status returned on this thread ("" if none). */
+const char* ssmd_last_error(void);
+
+/*
+ * ssmd_stream_copy -- measurement aid: copies `bytes` (a multiple of 16) from
+ * src to dst with the same 128-bit load/store pattern as the decode kernels.
+ * A read-once/write-once stream of equal sizes gives the practical HBM
+ * ceiling a decode step (equal state read and write) can be compared with.
+ */
+int ssmd_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSMDEC_H */

@@ -1,0 +1,24 @@
+"""MI355X (gfx950) single-token recurrent decode for gated linear-attention
+layers: the gated delta rule (GDN / DeltaNet / KDA) over an fp32 state pool.
+
+The compute lives in libssmdec.so (hand-written HIP kernels behind the C ABI
+of include/ssmdec.h); this package is its thin ctypes binding. Importing it
+does not load the library; the first call does, and fails loudly if the
+library has not been built.
+"""
+from ._binding import (  # noqa: F401
+    ACT_CODE,
+    DTYPE_CODE,
+    EXPORTS,
+    LIB_PATH,
+    SsmdError,
+    gdn_decode_step,
+    gdn_decode_step_buffered,
+    kda_decode_step,
+    load_library,
+    ssmd_last_error,
+    ssmd_stream_copy,
+)
+
+__all__ = ["gdn_decode_step", "gdn_decode_step_buffered", "kda_decode_step", "ssmd_last_error",
+           "ssmd_stream_copy", "SsmdError", "load_library"]

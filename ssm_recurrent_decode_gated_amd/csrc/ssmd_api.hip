@@ -1,0 +1,275 @@
+// ssmd_api.hip -- the extern "C" entry points declared in include/ssmdec.h:
+// host-side validation, launch-shape choice, and the stream-copy
+// measurement aid. Nothing here touches device memory from the host,
+// synchronises or allocates.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "ssmd_device.h"
+#include "ssmd_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return SSMD_OK;
+}
+
+bool valid_dtype(int d) { return d == SSMD_F32 || d == SSMD_BF16 || d == SSMD_F16; }
+int dtype_bytes(int d) { return d == SSMD_F32 ? 4 : 2; }
+bool head_size_ok(int k) { return k == 16 || k == 32 || k == 64 || k == 128 || k == 256; }
+bool aligned(const void* p, int bytes) { return ((uintptr_t)p % (uintptr_t)bytes) == 0; }
+
+// Launch shape for the state-streaming kernels. Defaults: 4 waves per block;
+// enough row groups per wave that a 128-row head is one pass per wave.
+// SSMD_TUNE="rg,wpb,nt" overrides them (read once), for shape sweeps.
+ssmd::Launch launch_for(int K) {
+  static int tuned = -1;
+  static ssmd::Launch override_l{0, 0, 0};
+  if (tuned < 0) {
+    const char* e = getenv("SSMD_TUNE");
+    int rg = 0, wpb = 0, nt = 0;
+    tuned = (e && sscanf(e, "%d,%d,%d", &rg, &wpb, &nt) == 3 && (rg == 1 || rg == 2 || rg == 4) &&
+             wpb >= 1 && wpb <= 8) ? 1 : 0;
+    if (tuned) override_l = ssmd::Launch{rg, wpb, nt};
+  }
+  if (tuned == 1) return override_l;
+  switch (K) {
+    case 16: return ssmd::Launch{1, 4, 0};
+    case 32: return ssmd::Launch{2, 4, 0};
+    case 64: return ssmd::Launch{4, 4, 0};
+    case 128: return ssmd::Launch{4, 4, 0};
+    default: return ssmd::Launch{2, 4, 0};  // 256
+  }
+}
+
+int launch_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SSMD_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Checks shared by the two GDN entry points. Returns SSMD_OK or an error.
+int check_gdn(const char* fn, const void* qkv, int64_t stride, const void* a, const void* b,
+              const float* A_log, const float* dt_bias, const float* state, int32_t num_slots,
+              const int32_t* idx, const void* out, int32_t B, int32_t H, int32_t HV, int32_t K,
+              int32_t V, int32_t act, int32_t odt, const void* norm_gate, int32_t norm_act) {
+  if (B < 0) return fail(SSMD_ERR_BAD_SHAPE, "%s: B = %d < 0", fn, B);
+  if (H < 1 || HV < 1 || HV % H)
+    return fail(SSMD_ERR_BAD_SHAPE, "%s: need H >= 1, HV >= 1 and HV %% H == 0 (H=%d HV=%d)", fn, H, HV);
+  if (!head_size_ok(K)) return fail(SSMD_ERR_UNSUPPORTED, "%s: K = %d not in {16,32,64,128,256}", fn, K);
+  if (V < 1 || V > 1024) return fail(SSMD_ERR_BAD_SHAPE, "%s: V = %d outside [1, 1024]", fn, V);
+  if (num_slots < 1) return fail(SSMD_ERR_BAD_SHAPE, "%s: num_slots = %d < 1", fn, num_slots);
+  if (!valid_dtype(act) || !valid_dtype(odt))
+    return fail(SSMD_ERR_BAD_DTYPE, "%s: bad act/out dtype (%d, %d)", fn, act, odt);
+  if (norm_act != SSMD_ACT_SILU && norm_act != SSMD_ACT_SIGMOID)
+    return fail(SSMD_ERR_BAD_DTYPE, "%s: bad norm_act %d", fn, norm_act);
+  if (B == 0) return SSMD_OK;
+  if (!qkv || !a || !b || !A_log || !dt_bias || !state || !idx || !out)
+    return fail(SSMD_ERR_NULL_ARG, "%s: a required pointer is NULL", fn);
+  const int64_t need = 2LL * H * K + (int64_t)HV * V;
+  if (stride < need || stride % 4)
+    return fail(SSMD_ERR_BAD_SHAPE, "%s: qkv_row_stride %lld must be >= %lld and a multiple of 4", fn,
+                (long long)stride, (long long)need);
+  if (!aligned(qkv, 4 * dtype_bytes(act)))
+    return fail(SSMD_ERR_BAD_SHAPE, "%s: mixed_qkv must be %d-byte aligned", fn, 4 * dtype_bytes(act));
+  if (!aligned(state, 16)) return fail(SSMD_ERR_BAD_SHAPE, "%s: state must be 16-byte aligned", fn);
+  if ((int64_t)B * HV * ((V + 7) / 8) >= (1LL << 31))
+    return fail(SSMD_ERR_BAD_SHAPE, "%s: B*HV too large for one launch", fn);
+  (void)norm_gate;
+  return SSMD_OK;
+}
+
+ssmd::GdnParams gdn_params(const void* qkv, int64_t stride, const void* a, const void* b,
+                           const float* A_log, const float* dt_bias, float* state, int32_t num_slots,
+                           const int32_t* idx, void* out, int32_t B, int32_t H, int32_t HV, int32_t K,
+                           int32_t V, int32_t act, int32_t odt, float scale, int32_t use_l2,
+                           float l2eps, const void* norm_gate, const float* norm_w, float norm_eps,
+                           int32_t norm_act) {
+  ssmd::GdnParams p{};
+  p.qkv = qkv;
+  p.qkv_stride = stride;
+  p.a = a;
+  p.b = b;
+  p.A_log = A_log;
+  p.dt_bias = dt_bias;
+  p.state = state;
+  p.num_slots = num_slots;
+  p.idx = idx;
+  p.out = out;
+  p.B = B;
+  p.H = H;
+  p.HV = HV;
+  p.K = K;
+  p.V = V;
+  p.act_dt = act;
+  p.out_dt = odt;
+  p.scale = scale;
+  p.use_l2 = use_l2 ? 1 : 0;
+  p.l2eps = l2eps;
+  p.norm_gate = norm_gate;
+  p.norm_w = norm_w;
+  p.norm_eps = norm_eps;
+  p.norm_act = norm_act;
+  return p;
+}
+
+// ------------------------------------------------------------- stream copy
+__global__ __launch_bounds__(256) void stream_copy_kernel(const ssmd::f4* __restrict__ src,
+                                                          ssmd::f4* __restrict__ dst, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    ssmd::f4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
+    dst[i] = v0;
+    dst[i + stride] = v1;
+    dst[i + 2 * stride] = v2;
+    dst[i + 3 * stride] = v3;
+  }
+  for (; i < n; i += stride) dst[i] = src[i];
+}
+
+}  // namespace
+
+namespace ssmd {
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t st) {
+  const int64_t n = bytes / 16;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 256 * 32) blocks = 256 * 32;
+  stream_copy_kernel<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(static_cast<const f4*>(src),
+                                                                  static_cast<f4*>(dst), n);
+  return hipGetLastError();
+}
+}  // namespace ssmd
+
+extern "C" {
+
+const char* ssmd_last_error(void) { return g_err; }
+
+int gdn_decode_step(const void* mixed_qkv, int64_t qkv_row_stride, const void* a, const void* b,
+                    const float* A_log, const float* dt_bias, float* state, int32_t num_slots,
+                    const int32_t* ssm_state_indices, void* out, int32_t B, int32_t H, int32_t HV,
+                    int32_t K, int32_t V, int32_t act_dtype, int32_t out_dtype, float scale,
+                    int32_t use_qk_l2norm, float l2norm_eps, const void* norm_gate,
+                    const float* norm_weight, float norm_eps, int32_t norm_act, hipStream_t stream) {
+  int rc = check_gdn("gdn_decode_step", mixed_qkv, qkv_row_stride, a, b, A_log, dt_bias, state,
+                     num_slots, ssm_state_indices, out, B, H, HV, K, V, act_dtype, out_dtype,
+                     norm_gate, norm_act);
+  if (rc) return rc;
+  if (B == 0) return ok();
+  ssmd::GdnParams p = gdn_params(mixed_qkv, qkv_row_stride, a, b, A_log, dt_bias, state, num_slots,
+                                 ssm_state_indices, out, B, H, HV, K, V, act_dtype, out_dtype, scale,
+                                 use_qk_l2norm, l2norm_eps, norm_gate, norm_weight, norm_eps, norm_act);
+  return launch_status(ssmd::launch_gdn(p, launch_for(K), stream), "gdn_decode_step");
+}
+
+int gdn_decode_step_buffered(const void* mixed_qkv, int64_t qkv_row_stride, const void* a,
+                             const void* b, const float* A_log, const float* dt_bias, float* state,
+                             int32_t num_slots, const int32_t* ssm_state_indices, void* out,
+                             int32_t B, int32_t H, int32_t HV, int32_t K, int32_t V,
+                             int32_t act_dtype, int32_t out_dtype, float scale,
+                             int32_t use_qk_l2norm, float l2norm_eps, const void* norm_gate,
+                             const float* norm_weight, float norm_eps, int32_t norm_act,
+                             void* d_cache, void* k_cache, float* g_cache, const int32_t* write_pos,
+                             int32_t L, hipStream_t stream) {
+  const char* fn = "gdn_decode_step_buffered";
+  int rc = check_gdn(fn, mixed_qkv, qkv_row_stride, a, b, A_log, dt_bias, state, num_slots,
+                     ssm_state_indices, out, B, H, HV, K, V, act_dtype, out_dtype, norm_gate, norm_act);
+  if (rc) return rc;
+  if (L < 1 || L > 64) return fail(SSMD_ERR_BAD_SHAPE, "%s: L = %d outside [1, 64]", fn, L);
+  const ssmd::Launch l = launch_for(K);
+  const int rpt = norm_gate ? V : l.wpb * l.rg * (64 / (K >= 32 ? 8 : K / 4));
+  const size_t lds = sizeof(float) * ((size_t)(L - 1) * ((size_t)K + (size_t)rpt) + 3 * (size_t)(L - 1) + 1);
+  if (lds > 60 * 1024)
+    return fail(SSMD_ERR_UNSUPPORTED, "%s: ring staging needs %zu bytes of LDS (> 60 KiB); lower L", fn, lds);
+  if (B == 0) return ok();
+  if (!d_cache || !k_cache || !g_cache || !write_pos)
+    return fail(SSMD_ERR_NULL_ARG, "%s: a ring pointer is NULL", fn);
+  ssmd::GdnParams p = gdn_params(mixed_qkv, qkv_row_stride, a, b, A_log, dt_bias, state, num_slots,
+                                 ssm_state_indices, out, B, H, HV, K, V, act_dtype, out_dtype, scale,
+                                 use_qk_l2norm, l2norm_eps, norm_gate, norm_weight, norm_eps, norm_act);
+  p.d_cache = d_cache;
+  p.k_cache = k_cache;
+  p.g_cache = g_cache;
+  p.write_pos = write_pos;
+  p.L = L;
+  return launch_status(ssmd::launch_gdn_buffered(p, l, stream), fn);
+}
+
+int kda_decode_step(const void* x, const float* conv_weight, const float* conv_bias, void* conv_state,
+                    int64_t cs_slot_stride, int64_t cs_chan_stride, int64_t cs_tap_stride,
+                    const void* raw_g, const void* raw_beta, const float* A_log, const float* dt_bias,
+                    float lower_bound, float* state, int32_t num_slots, const int32_t* state_indices,
+                    void* out, const void* output_gate, const float* norm_weight, float norm_eps,
+                    int32_t T, int32_t H, int32_t D, int32_t W, int32_t act_dtype, int32_t out_dtype,
+                    float scale, int32_t use_qk_l2norm, float l2norm_eps, hipStream_t stream) {
+  const char* fn = "kda_decode_step";
+  if (T < 0) return fail(SSMD_ERR_BAD_SHAPE, "%s: T = %d < 0", fn, T);
+  if (H < 1) return fail(SSMD_ERR_BAD_SHAPE, "%s: H = %d < 1", fn, H);
+  if (!head_size_ok(D)) return fail(SSMD_ERR_UNSUPPORTED, "%s: D = %d not in {16,32,64,128,256}", fn, D);
+  if (W < 2 || W > 8) return fail(SSMD_ERR_BAD_SHAPE, "%s: conv width W = %d outside [2, 8]", fn, W);
+  if (num_slots < 1) return fail(SSMD_ERR_BAD_SHAPE, "%s: num_slots = %d < 1", fn, num_slots);
+  if (!valid_dtype(act_dtype) || !valid_dtype(out_dtype))
+    return fail(SSMD_ERR_BAD_DTYPE, "%s: bad act/out dtype (%d, %d)", fn, act_dtype, out_dtype);
+  if (cs_slot_stride < 1 || cs_chan_stride < 1 || cs_tap_stride < 1)
+    return fail(SSMD_ERR_BAD_SHAPE, "%s: conv-state strides must be positive", fn);
+  if ((int64_t)T * H >= (1LL << 31)) return fail(SSMD_ERR_BAD_SHAPE, "%s: T*H too large", fn);
+  if (T == 0) return ok();
+  if (!x || !conv_weight || !conv_state || !raw_g || !raw_beta || !state || !state_indices || !out)
+    return fail(SSMD_ERR_NULL_ARG, "%s: a required pointer is NULL", fn);
+  if (!aligned(raw_g, 4 * dtype_bytes(act_dtype)) || !aligned(state, 16))
+    return fail(SSMD_ERR_BAD_SHAPE, "%s: raw_g must be %d-byte and state 16-byte aligned", fn,
+                4 * dtype_bytes(act_dtype));
+  ssmd::KdaParams p{};
+  p.x = x;
+  p.conv_w = conv_weight;
+  p.conv_b = conv_bias;
+  p.conv_state = conv_state;
+  p.cs_slot = cs_slot_stride;
+  p.cs_chan = cs_chan_stride;
+  p.cs_tap = cs_tap_stride;
+  p.raw_g = raw_g;
+  p.raw_beta = raw_beta;
+  p.A_log = A_log;
+  p.dt_bias = dt_bias;
+  p.lower_bound = lower_bound;
+  p.state = state;
+  p.num_slots = num_slots;
+  p.idx = state_indices;
+  p.out = out;
+  p.gate = output_gate;
+  p.norm_w = norm_weight;
+  p.norm_eps = norm_eps;
+  p.T = T;
+  p.H = H;
+  p.D = D;
+  p.W = W;
+  p.act_dt = act_dtype;
+  p.out_dt = out_dtype;
+  p.scale = scale;
+  p.use_l2 = use_qk_l2norm ? 1 : 0;
+  p.l2eps = l2norm_eps;
+  return launch_status(ssmd::launch_kda(p, launch_for(D), stream), fn);
+}
+
+int ssmd_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+  if (!src || !dst) return fail(SSMD_ERR_NULL_ARG, "ssmd_stream_copy: NULL pointer");
+  if (bytes < 0 || bytes % 16) return fail(SSMD_ERR_BAD_SHAPE, "ssmd_stream_copy: bytes must be a multiple of 16");
+  if (!aligned(src, 16) || !aligned(dst, 16))
+    return fail(SSMD_ERR_BAD_SHAPE, "ssmd_stream_copy: pointers must be 16-byte aligned");
+  if (bytes == 0) return ok();
+  return launch_status(ssmd::launch_stream_copy(src, dst, bytes, stream), "ssmd_stream_copy");
+}
+
+}  // extern "C"

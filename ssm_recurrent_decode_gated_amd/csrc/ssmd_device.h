@@ -1,0 +1,135 @@
+// ssmd_device.h -- device-side building blocks shared by the decode kernels
+// (gfx950 / CDNA4, wave64): element conversion, lane-group reductions over
+// DPP, and the row-group lane layout used to stream fp32 state rows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssmdec.h"
+
+namespace ssmd {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// fp32 -> bf16 round-to-nearest-even; NaN stays NaN (quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);  // RNE
+}
+
+// Load 4 consecutive activation elements (element offset `off`, a multiple of
+// 4 from a suitably aligned base) as fp32. `dt` is uniform across the wave.
+__device__ __forceinline__ void load_act4(const void* base, int64_t off, int dt, float out[4]) {
+  if (dt == SSMD_F32) {
+    f4 v = *reinterpret_cast<const f4*>(static_cast<const float*>(base) + off);
+    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+  } else {
+    uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + off);
+    if (dt == SSMD_BF16) {
+      out[0] = __uint_as_float(v.x << 16);
+      out[1] = __uint_as_float(v.x & 0xffff0000u);
+      out[2] = __uint_as_float(v.y << 16);
+      out[3] = __uint_as_float(v.y & 0xffff0000u);
+    } else {
+      out[0] = f16_bits_to_f32(v.x & 0xffffu);
+      out[1] = f16_bits_to_f32(v.x >> 16);
+      out[2] = f16_bits_to_f32(v.y & 0xffffu);
+      out[3] = f16_bits_to_f32(v.y >> 16);
+    }
+  }
+}
+
+__device__ __forceinline__ float load_act1(const void* base, int64_t off, int dt) {
+  if (dt == SSMD_F32) return static_cast<const float*>(base)[off];
+  uint32_t h = static_cast<const uint16_t*>(base)[off];
+  return dt == SSMD_BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
+}
+
+__device__ __forceinline__ void store_act1(void* base, int64_t off, int dt, float v) {
+  if (dt == SSMD_F32) {
+    static_cast<float*>(base)[off] = v;
+  } else {
+    static_cast<uint16_t*>(base)[off] = dt == SSMD_BF16 ? f32_to_bf16_bits(v) : f32_to_f16_bits(v);
+  }
+}
+
+// ------------------------------------------------------------- math
+__device__ __forceinline__ float softplus_f(float x) { return x > 20.f ? x : log1pf(expf(x)); }
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
+__device__ __forceinline__ float silu_f(float x) { return x * sigmoid_f(x); }
+
+// ------------------------------------------------------------- reductions
+// DPP lane moves within a row of 16 lanes (gfx9 encodings).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <- lane 7-i within 8
+constexpr int DPP_ROW_MIRROR = 0x140;  // lane i <- lane 15-i within 16
+
+// Sum over aligned groups of LPR lanes (LPR in {2,4,8,16}); every lane of the
+// group receives the group total.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(LPR == 2 || LPR == 4 || LPR == 8 || LPR == 16, "lane group");
+  x += dpp_mov<DPP_XOR1>(x);
+  if constexpr (LPR >= 4) x += dpp_mov<DPP_XOR2>(x);
+  if constexpr (LPR >= 8) x += dpp_mov<DPP_HALF_MIRROR>(x);
+  if constexpr (LPR >= 16) x += dpp_mov<DPP_ROW_MIRROR>(x);
+  return x;
+}
+
+// Sum over the whole wave (64 lanes); every lane receives the total.
+__device__ __forceinline__ float wave_sum(float x) {
+  x = group_sum<16>(x);
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// ------------------------------------------------------------- row layout
+// A head's state is V rows of K fp32 (row = value index). A row is split
+// over LPR lanes; lane c of a row owns the float4 columns c, c+LPR, c+2*LPR,
+// ... so each wave-wide 128-bit access covers (64/LPR) rows x 16*LPR
+// contiguous bytes. q and k fragments follow the same columns, so they are
+// lane constants for the whole head.
+template <int K>
+struct RowLayout {
+  static_assert(K == 16 || K == 32 || K == 64 || K == 128 || K == 256, "head size");
+  static constexpr int LPR = K >= 32 ? 8 : K / 4;  // lanes per row
+  static constexpr int NV = K / (4 * LPR);         // float4 per lane per row
+  static constexpr int RPI = 64 / LPR;             // rows per wave-wide access
+  __device__ static __forceinline__ int col(int c, int j) { return 4 * (c + LPR * j); }
+};
+
+template <bool NT>
+__device__ __forceinline__ f4 ld4(const float* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
+  else return *reinterpret_cast<const f4*>(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ void st4(float* p, f4 v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<f4*>(p));
+  else *reinterpret_cast<f4*>(p) = v;
+}
+
+}  // namespace ssmd

@@ -1,0 +1,79 @@
+// ssmd_internal.h -- parameter blocks passed from the validated C entry points
+// to the kernel launchers. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssmd {
+
+struct GdnParams {
+  const void* qkv;
+  int64_t qkv_stride;
+  const void* a;
+  const void* b;
+  const float* A_log;
+  const float* dt_bias;
+  float* state;
+  int32_t num_slots;
+  const int32_t* idx;
+  void* out;
+  int32_t B, H, HV, K, V;
+  int32_t act_dt, out_dt;
+  float scale;
+  int32_t use_l2;
+  float l2eps;
+  const void* norm_gate;
+  const float* norm_w;
+  float norm_eps;
+  int32_t norm_act;
+  // buffered form only
+  void* d_cache;
+  void* k_cache;
+  float* g_cache;
+  const int32_t* write_pos;
+  int32_t L;
+};
+
+struct KdaParams {
+  const void* x;
+  const float* conv_w;
+  const float* conv_b;
+  void* conv_state;
+  int64_t cs_slot, cs_chan, cs_tap;
+  const void* raw_g;
+  const void* raw_beta;
+  const float* A_log;
+  const float* dt_bias;
+  float lower_bound;
+  float* state;
+  int32_t num_slots;
+  const int32_t* idx;
+  void* out;
+  const void* gate;
+  const float* norm_w;
+  float norm_eps;
+  int32_t T, H, D, W;
+  int32_t act_dt, out_dt;
+  float scale;
+  int32_t use_l2;
+  float l2eps;
+};
+
+// Launch shape of the state-streaming kernels, chosen on the host.
+struct Launch {
+  int rg;   // row groups per wave per pass (rows per wave pass = rg * 64 / LPR)
+  int wpb;  // waves per workgroup
+  int nt;   // non-temporal state loads/stores
+};
+
+// Launchers: return a hipError_t from the launch.
+hipError_t launch_gdn(const GdnParams& p, const Launch& l, hipStream_t s);
+hipError_t launch_gdn_buffered(const GdnParams& p, const Launch& l, hipStream_t s);
+hipError_t launch_kda(const KdaParams& p, const Launch& l, hipStream_t s);
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+
+// Compiled head sizes / row-group choices (checked on the host).
+bool gdn_supported(int K, int rg);
+
+}  // namespace ssmd

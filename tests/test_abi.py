@@ -1,0 +1,141 @@
+"""The C-ABI library without a GPU: it loads next to torch's HIP runtime,
+exports every function include/ssmdec.h declares, and rejects bad arguments
+on the host with the documented status codes before any HIP call. None of
+these calls launches anything.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import ssm_recurrent_decode_gated_amd as S
+from ssm_recurrent_decode_gated_amd import _binding as Bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssmdec.h")
+
+OK, NULL_ARG, BAD_SHAPE, BAD_DTYPE, UNSUPPORTED = 0, -1, -2, -3, -4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(\w+)\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(Bd.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = S.load_library()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_single_hip_runtime_in_process():
+    S.load_library()
+    maps = open("/proc/self/maps").read()
+    hip = {m for m in re.findall(r"\S*libamdhip64\S*", maps)}
+    assert len(hip) == 1, hip
+
+
+def _gdn(L, **kw):
+    """Call gdn_decode_step with fake (never dereferenced) pointers."""
+    a = dict(qkv=0x10000, stride=8192, a=0x20000, b=0x30000, A_log=0x40000, dt_bias=0x50000,
+             state=0x60000, num_slots=16, idx=0x70000, out=0x80000, B=16, H=16, HV=32, K=128, V=128,
+             act=1, odt=1, scale=0.088, l2=1, l2eps=1e-6, ng=None, nw=None, neps=1e-5, nact=0)
+    a.update(kw)
+    return L.gdn_decode_step(a["qkv"], a["stride"], a["a"], a["b"], a["A_log"], a["dt_bias"], a["state"],
+                             a["num_slots"], a["idx"], a["out"], a["B"], a["H"], a["HV"], a["K"], a["V"],
+                             a["act"], a["odt"], a["scale"], a["l2"], a["l2eps"], a["ng"], a["nw"],
+                             a["neps"], a["nact"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qkv=None), NULL_ARG),
+    (dict(state=None), NULL_ARG),
+    (dict(idx=None), NULL_ARG),
+    (dict(HV=24, H=16), BAD_SHAPE),
+    (dict(H=0), BAD_SHAPE),
+    (dict(K=48), UNSUPPORTED),
+    (dict(K=512), UNSUPPORTED),
+    (dict(V=0), BAD_SHAPE),
+    (dict(V=2048), BAD_SHAPE),
+    (dict(num_slots=0), BAD_SHAPE),
+    (dict(B=-1), BAD_SHAPE),
+    (dict(act=7), BAD_DTYPE),
+    (dict(odt=-1), BAD_DTYPE),
+    (dict(nact=3), BAD_DTYPE),
+    (dict(stride=8191), BAD_SHAPE),
+    (dict(stride=8190), BAD_SHAPE),
+    (dict(qkv=0x10002), BAD_SHAPE),      # bf16 activations need 8-byte alignment
+    (dict(act=0, qkv=0x10008), BAD_SHAPE),  # fp32 activations need 16-byte alignment
+    (dict(state=0x60004), BAD_SHAPE),
+])
+def test_gdn_host_validation(kw, code):
+    L = S.load_library()
+    assert _gdn(L, **kw) == code
+    assert S.ssmd_last_error() != ""
+
+
+def test_gdn_empty_batch_is_a_noop():
+    L = S.load_library()
+    assert _gdn(L, B=0, qkv=None, state=None, idx=None, out=None) == OK
+    assert S.ssmd_last_error() == ""
+
+
+def test_buffered_host_validation():
+    L = S.load_library()
+
+    def call(L_=8, d=0x90000, wp=0xA0000, K=128, B=4):
+        return L.gdn_decode_step_buffered(0x10000, 8192, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000, 16,
+                                          0x70000, 0x80000, B, 16, 32, K, 128, 1, 1, 0.088, 1, 1e-6, None,
+                                          None, 1e-5, 0, d, 0xB0000, 0xC0000, wp, L_, None)
+    assert call(L_=0) == BAD_SHAPE
+    assert call(L_=65) == BAD_SHAPE
+    assert call(d=None) == NULL_ARG
+    assert call(wp=None) == NULL_ARG
+    assert call(K=48) == UNSUPPORTED
+    assert call(B=0, d=None, wp=None) == OK
+
+
+def test_kda_host_validation():
+    L = S.load_library()
+
+    def call(T=64, H=96, D=128, W=4, x=0x10000, cs=(216 * 128 * 3, 1, 36864), act=1, state=0x60000):
+        return L.kda_decode_step(x, 0x20000, None, 0x30000, cs[0], cs[1], cs[2], 0x40000, 0x50000, None, None,
+                                 -5.0, state, 72, 0x70000, 0x80000, 0x90000, None, 1e-5, T, H, D, W, act, 1,
+                                 0.088, 1, 1e-6, None)
+    assert call(D=96) == UNSUPPORTED
+    assert call(W=1) == BAD_SHAPE
+    assert call(W=9) == BAD_SHAPE
+    assert call(H=0) == BAD_SHAPE
+    assert call(T=-1) == BAD_SHAPE
+    assert call(x=None) == NULL_ARG
+    assert call(act=5) == BAD_DTYPE
+    assert call(cs=(0, 1, 1)) == BAD_SHAPE
+    assert call(state=0x60008) == BAD_SHAPE
+    assert call(T=0, x=None) == OK
+
+
+def test_stream_copy_host_validation():
+    L = S.load_library()
+    assert L.ssmd_stream_copy(None, 0x1000, 16, None) == NULL_ARG
+    assert L.ssmd_stream_copy(0x1000, 0x2000, 15, None) == BAD_SHAPE
+    assert L.ssmd_stream_copy(0x1008, 0x2000, 16, None) == BAD_SHAPE
+    assert L.ssmd_stream_copy(0x1000, 0x2000, 0, None) == OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    t = torch.zeros(4, 4)
+    with pytest.raises(ValueError, match="device"):
+        S.gdn_decode_step(t, t, t, t, t, torch.zeros(1, 1, 4, 4), t, t)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(Bd, "_LIB", None)
+    monkeypatch.setattr(Bd, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        Bd.load_library()

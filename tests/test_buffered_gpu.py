@@ -1,0 +1,149 @@
+"""GPU parity of gdn_decode_step_buffered against the fp64 oracle.
+
+Single calls take the ring as an input (seeded records), so each phase is
+checked on its own, with rows at different phases in one launch: outputs to
+1e-4, the appended record (delta and key rounded to bf16, g as fp32), the
+folded state on flush rows, and untouched checkpoints and ring positions on
+the others. Chained runs follow the oracle's own bf16 ring over several
+cycles to the chained tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import ssm_recurrent_decode_gated_amd as S
+import workloads as W
+from tests._helpers import CHAIN_TOL, FP32_TOL, assert_mixed, need_gpu, to_np64, ulp16
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _assert_ring16(got, ref, what):
+    """A stored 16-bit record may differ from the oracle's by one ulp where the
+    exact value sits at a rounding midpoint between the two; nowhere else."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    diff = np.abs(got - ref)
+    assert (diff <= ulp16(ref, 7) * 1.0000001).all(), f"{what}: record off by more than one ulp"
+    assert (diff == 0).mean() > 0.99, f"{what}: too many records differ ({(diff != 0).mean():.3%})"
+
+
+def _call(w, x, P, st_d, idx, ring_d, wp, out, norm=False):
+    kw = {}
+    if norm:
+        kw = dict(norm_gate=x["norm_gate"].to(DEV), norm_weight=x["norm_weight"].to(DEV))
+    S.gdn_decode_step_buffered(x["qkv"].to(DEV), x["a"].to(DEV), x["b"].to(DEV), P["A_log"].to(DEV),
+                               P["dt_bias"].to(DEV), st_d, idx.to(DEV), out, ring_d["d_cache"],
+                               ring_d["k_cache"], ring_d["g_cache"], wp.to(DEV), **kw)
+
+
+CASES = [
+    # name, B, H, HV, K, V, L, phases, norm
+    ("k128_L8_mixed_phases", 6, 2, 4, 128, 128, 8, [0, 3, 7, 5, 1, 6], False),
+    ("k128_L16_norm", 4, 2, 4, 128, 128, 16, [15, 0, 9, 14], True),
+    ("k64_v40_L5", 5, 1, 3, 64, 40, 5, [4, 2, 0, 1, 3], False),
+    ("k16_v16_L3", 3, 2, 2, 16, 16, 3, [2, 1, 0], False),
+    ("k128_L1", 3, 2, 4, 128, 128, 1, [0, 0, 0], False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_buffered_single_call_every_phase(case):
+    need_gpu()
+    name, B, H, HV, K, V, L, phases, norm = case
+    w = W.GDNWorkload("buf_" + name, B=B, H=H, HV=HV, K=K, V=V, num_slots=B + 2, out="f32", idx="perm")
+    P, idx, x = W.gdn_params(w), W.slot_indices(w), W.gdn_step_inputs(w, norm=norm)
+    st = W.gdn_state(w)
+    ring = W.gdn_ring(w, L)
+    wp = torch.tensor(phases, dtype=torch.int32)
+    st_d = st.to(DEV)
+    ring_d = {k: v.to(DEV) for k, v in ring.items()}
+    out = torch.full((B, 1, HV, V), float("nan"), device=DEV)
+    _call(w, x, P, st_d, idx, ring_d, wp, out, norm)
+    ref_st = st.double().numpy().copy()
+    ref_ring = {k: v.double().numpy().copy() for k, v in ring.items()}
+    kw = dict(norm_gate=x["norm_gate"], norm_weight=x["norm_weight"]) if norm else {}
+    ro = O.gdn_step_buffered(x["qkv"], x["a"], x["b"], P["A_log"], P["dt_bias"], ref_st, idx,
+                             ref_ring["d_cache"], ref_ring["k_cache"], ref_ring["g_cache"], wp, L,
+                             H=H, HV=HV, K=K, V=V, ring_fmt=O.FMT_BF16, **kw)
+    torch.cuda.synchronize()
+    assert_mixed(out.reshape(B, HV, V), ro, FP32_TOL, "output")
+    got_st = st_d.cpu()
+    got = {k: to_np64(v) for k, v in ring_d.items()}
+    G = HV // H
+    for b in range(B):
+        s, p = int(idx[b]), phases[b]
+        if p == L - 1:
+            assert_mixed(got_st[s], ref_st[s], FP32_TOL, f"flushed state row {b}")
+        else:
+            assert torch.equal(got_st[s], st[s]), f"non-flush row {b} wrote the checkpoint"
+        _assert_ring16(got["d_cache"][s, :, p], ref_ring["d_cache"][s, :, p], f"delta record row {b}")
+        _assert_ring16(got["k_cache"][s, :, p], ref_ring["k_cache"][s, :, p], f"key record row {b}")
+        np.testing.assert_allclose(got["g_cache"][s, :, p], ref_ring["g_cache"][s, :, p], rtol=1e-5)
+        others = [j for j in range(L) if j != p]
+        np.testing.assert_array_equal(got["d_cache"][s, :, others], ring["d_cache"][s, :, others].double().numpy())
+        np.testing.assert_array_equal(got["k_cache"][s, :, others], ring["k_cache"][s, :, others].double().numpy())
+        np.testing.assert_array_equal(got["g_cache"][s, :, others], ring["g_cache"][s, :, others].double().numpy())
+    for s in set(range(w.num_slots)) - set(idx.tolist()):
+        assert torch.equal(got_st[s], st[s])
+        for k in ring:
+            np.testing.assert_array_equal(got[k][s], ring[k][s].double().numpy())
+    assert G >= 1
+
+
+@pytest.mark.parametrize("L", [1, 8, 16])
+def test_buffered_chain_matches_oracle(L):
+    """B=64, H=16, HV=32, K=V=128 (the long-horizon workload) for 3 full
+    cycles from a zeroed ring at write_pos 0, the host advancing write_pos.
+    The oracle follows rows 5 and 40 with its own bf16 ring."""
+    need_gpu()
+    w = W.GDN_B64_CHAIN
+    P, idx = W.gdn_params(w), W.slot_indices(w)
+    st = W.gdn_state(w)
+    st_d = st.to(DEV)
+    ring_d = {"d_cache": torch.zeros(w.num_slots, w.HV, L, w.V, dtype=torch.bfloat16, device=DEV),
+              "k_cache": torch.zeros(w.num_slots, w.H, L, w.K, dtype=torch.bfloat16, device=DEV),
+              "g_cache": torch.zeros(w.num_slots, w.HV, L, device=DEV)}
+    rows = [5, 40]
+    ref = st[rows].double().numpy().copy()
+    rr = {"d": np.zeros((2, w.HV, L, w.V)), "k": np.zeros((2, w.H, L, w.K)), "g": np.zeros((2, w.HV, L))}
+    sub = np.arange(2, dtype=np.int32)
+    out = torch.empty(w.B, 1, w.HV, w.V, device=DEV)
+    Pd = {k: v.to(DEV) for k, v in P.items()}
+    for t in range(3 * L if L > 1 else 8):
+        x = W.gdn_step_inputs(w, 5000 + t)
+        p = t % L
+        wp = torch.full((w.B,), p, dtype=torch.int32)
+        S.gdn_decode_step_buffered(x["qkv"].to(DEV), x["a"].to(DEV), x["b"].to(DEV), Pd["A_log"],
+                                   Pd["dt_bias"], st_d, idx.to(DEV), out, ring_d["d_cache"],
+                                   ring_d["k_cache"], ring_d["g_cache"], wp.to(DEV))
+        ro = O.gdn_step_buffered(x["qkv"][rows], x["a"][rows], x["b"][rows], P["A_log"], P["dt_bias"], ref,
+                                 sub, rr["d"], rr["k"], rr["g"], np.full(2, p, np.int32), L,
+                                 H=w.H, HV=w.HV, K=w.K, V=w.V, ring_fmt=O.FMT_BF16)
+        assert_mixed(out[rows].reshape(2, w.HV, w.V), ro, CHAIN_TOL, f"output step {t} (phase {p})")
+        if p == L - 1:
+            assert_mixed(st_d[rows], ref, CHAIN_TOL, f"checkpoint after step {t}")
+
+
+def test_buffered_L1_equals_packed_on_gpu():
+    """With L = 1 every call is a flush of an empty ring: the buffered kernel
+    must compute the packed step."""
+    need_gpu()
+    w = W.GDN_B16
+    P, idx, x = W.gdn_params(w), W.slot_indices(w), W.gdn_step_inputs(w)
+    st = W.gdn_state(w)
+    s1, s2 = st.to(DEV), st.to(DEV)
+    o1 = torch.empty(w.B, 1, w.HV, w.V, device=DEV)
+    o2 = torch.empty_like(o1)
+    S.gdn_decode_step(x["qkv"].to(DEV), x["a"].to(DEV), x["b"].to(DEV), P["A_log"].to(DEV),
+                      P["dt_bias"].to(DEV), s1, idx.to(DEV), o1)
+    ring_d = {"d_cache": torch.zeros(w.num_slots, w.HV, 1, w.V, dtype=torch.bfloat16, device=DEV),
+              "k_cache": torch.zeros(w.num_slots, w.H, 1, w.K, dtype=torch.bfloat16, device=DEV),
+              "g_cache": torch.zeros(w.num_slots, w.HV, 1, device=DEV)}
+    _call(w, x, P, s2, idx, ring_d, torch.zeros(w.B, dtype=torch.int32), o2)
+    torch.cuda.synchronize()
+    ref = to_np64(s1)
+    assert_mixed(s2, ref, 1e-6, "state")
+    assert_mixed(o2, to_np64(o1), 1e-6, "output")

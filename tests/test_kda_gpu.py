@@ -1,0 +1,112 @@
+"""GPU parity of kda_decode_step (fused conv1d update + KDA delta rule +
+sigmoid-gated RMSNorm) against the fp64 oracle: outputs and states to the
+fp32 tolerance (16-bit outputs to one ulp), the rolled conv state bit for bit
+(it holds raw inputs), and skipped tokens (slot 0 = NULL block, out of range)
+touching nothing."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import ssm_recurrent_decode_gated_amd as S
+import workloads as W
+from tests._helpers import FP32_TOL, assert_16bit, assert_mixed, need_gpu
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _run_both(w, d, *, with_norm=True, A_log=None, dt_bias=None, conv_bias=None, out_dtype=torch.bfloat16):
+    H, D, T = w.H, w.D, w.T
+    cs_d = d["conv_state"].to(DEV)
+    assert cs_d.stride() == d["conv_state"].stride()
+    st_d = d["state"].to(DEV)
+    out = torch.full((T, H, D), 7.0, dtype=out_dtype, device=DEV)
+    S.kda_decode_step(d["x"].to(DEV), d["conv_weight"].to(DEV),
+                      None if conv_bias is None else conv_bias.to(DEV), cs_d, d["raw_g"].to(DEV),
+                      d["raw_beta"].to(DEV), None if A_log is None else A_log.to(DEV),
+                      None if dt_bias is None else dt_bias.to(DEV), st_d, d["idx"].to(DEV), out,
+                      output_gate=d["gate"].to(DEV) if with_norm else None,
+                      norm_weight=d["norm_weight"].to(DEV) if with_norm else None,
+                      lower_bound=w.lower_bound, norm_eps=w.norm_eps)
+    cs_ref = d["conv_state"].double().numpy().copy()  # logical [slots, C, W-1], contiguous copy
+    st_ref = d["state"].double().numpy().copy()
+    ro = O.kda_decode(d["x"], d["conv_weight"], conv_bias, cs_ref, d["raw_g"], d["raw_beta"], st_ref, d["idx"],
+                      H=H, D=D, A_log=A_log, dt_bias=dt_bias, lower_bound=w.lower_bound,
+                      gate=d["gate"] if with_norm else None,
+                      norm_weight=d["norm_weight"] if with_norm else None, norm_eps=w.norm_eps)
+    torch.cuda.synchronize()
+    return out, st_d.cpu(), cs_d.cpu(), ro, st_ref, cs_ref
+
+
+def _active(idx, num_slots):
+    return [t for t, s in enumerate(idx.tolist()) if 0 < s < num_slots]
+
+
+@pytest.mark.parametrize("layout", ["SD", "DS"])
+def test_kda_t64_h96_full_size(layout):
+    """T=64 tokens, 96 heads x 128, conv width 4, slots 1..64 of 72, bf16
+    activations, gate -5 sigmoid(a), sigmoid-gated RMSNorm with eps 1e-5."""
+    need_gpu()
+    w = W.KDA_T64
+    d = W.kda_inputs(w, layout=layout)
+    out, st, cs, ro, st_ref, cs_ref = _run_both(w, d)
+    assert_16bit(out, ro, FP32_TOL, "output")
+    slots = d["idx"].tolist()
+    assert_mixed(st[slots], st_ref[slots], FP32_TOL, "state of named slots")
+    np.testing.assert_array_equal(cs.double().numpy(), cs_ref)
+    for s in set(range(w.num_slots)) - set(slots):
+        assert torch.equal(st[s], d["state"][s]), f"unnamed slot {s} changed"
+
+
+def test_kda_skips_null_slot_and_out_of_range():
+    need_gpu()
+    w = W.KDAWorkload("kda_skip", T=5, H=3, D=128, num_slots=6)
+    d = W.kda_inputs(w)
+    d["idx"] = torch.tensor([2, 0, 5, 6, -3], dtype=torch.int32)
+    out, st, cs, ro, st_ref, cs_ref = _run_both(w, d)
+    for t in (1, 3, 4):
+        assert (out[t].float().cpu() == 7.0).all(), f"skipped token {t} wrote output"
+    act = _active(d["idx"], w.num_slots)
+    assert_16bit(out[act], ro[act], FP32_TOL, "active outputs")
+    np.testing.assert_array_equal(cs.double().numpy(), cs_ref)
+    for s in (0, 1, 3, 4):
+        assert torch.equal(st[s], d["state"][s])
+
+
+SMALL = [
+    # name, T, H, D, W, act dtype, out dtype, norm, A_log/dt_bias, conv bias
+    ("d64_w3_f32_gates", 6, 4, 64, 3, "f32", torch.float32, False, True, True),
+    ("d32_w4_bf16_norm_bias", 5, 2, 32, 4, "bf16", torch.bfloat16, True, False, True),
+    ("d16_w2_f16", 7, 3, 16, 2, "f16", torch.float16, True, True, False),
+    ("d256_w4_bf16", 3, 2, 256, 4, "bf16", torch.float32, True, False, False),
+    ("d128_w4_nonorm", 4, 5, 128, 4, "bf16", torch.bfloat16, False, False, False),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_kda_shapes_dtypes_options(case):
+    """Every head size, conv widths 2-4, fp32/f16 activations (the conv state
+    then is that dtype too), conv bias, norm on/off, and the A_log / dt_bias
+    gate form (a reading of the pages; parity against the oracle only)."""
+    need_gpu()
+    name, T, H, D, Wd, act, outd, norm, gates, bias = case
+    w = W.KDAWorkload("kda_" + name, T=T, H=H, D=D, W=Wd, num_slots=T + 3)
+    d = W.kda_inputs(w, layout="DS" if T % 2 else "SD")
+    if act != "bf16":
+        for k in ("x", "raw_g", "raw_beta", "gate", "conv_state"):
+            d[k] = d[k].to(W.DTYPES[act])
+    g = W.generator(0, name, "extra")
+    A_log = W.normal((H,), 0.3, "f32", g) if gates else None
+    dt_bias = W.normal((H * D,), 0.1, "f32", g) if gates else None
+    conv_bias = W.normal((3 * H * D,), 0.5, "f32", g) if bias else None
+    out, st, cs, ro, st_ref, cs_ref = _run_both(w, d, with_norm=norm, A_log=A_log, dt_bias=dt_bias,
+                                                conv_bias=conv_bias, out_dtype=outd)
+    act_t = _active(d["idx"], w.num_slots)
+    if outd == torch.float32:
+        assert_mixed(out[act_t].cpu(), ro[act_t], FP32_TOL, "output")
+    else:
+        assert_16bit(out[act_t], ro[act_t], FP32_TOL, "output")
+    slots = d["idx"].tolist()
+    assert_mixed(st[slots], st_ref[slots], FP32_TOL, "state")
+    np.testing.assert_array_equal(cs.double().numpy(), cs_ref)
