@@ -24,9 +24,9 @@
  *     read and write nothing (their `out` rows are left as they were). Two
  *     active rows naming the same slot in one call is a precondition
  *     violation with an undefined result.
- *   - Activation tensors (dtype SSMD_BF16 / SSMD_F16 / SSMD_F32) must be
- *     aligned to 4 elements (8 bytes for 16-bit types, 16 for fp32), with row
- *     strides that are multiples of 4 elements; fp32 states must be 16-byte
+ *   - Activation tensors (dtype SSMD_BF16 / SSMD_F16 / SSMD_F32) have no
+ *     alignment requirement beyond their element size; rows aligned to 4
+ *     elements take a faster vector-load path. fp32 states must be 16-byte
  *     aligned.
  *   - Calls are reentrant; the only global state is the thread-local error
  *     string.

@@ -27,35 +27,39 @@ _ip = ctypes.POINTER(ctypes.c_int32)
 _i, _d, _l = ctypes.c_int, ctypes.c_double, ctypes.c_long
 
 
+def configure(L: ctypes.CDLL) -> ctypes.CDLL:
+    """Declare the C signatures of an oracle library handle."""
+    L.orc_softplus.argtypes = [_d]
+    L.orc_sigmoid.argtypes = [_d]
+    L.orc_silu.argtypes = [_d]
+    L.orc_round_fmt.argtypes = [_d, _i]
+    L.orc_kda_gate.argtypes = [_d, _d, _d, _d]
+    for f in ("orc_softplus", "orc_sigmoid", "orc_silu", "orc_round_fmt", "orc_kda_gate"):
+        getattr(L, f).restype = _d
+    L.orc_gdn_gates.argtypes = [_d, _d, _d, _d, _dp, _dp]
+    L.orc_gdn_gates.restype = None
+    gdn = [_i] * 6 + [_dp, _l, _dp, _dp, _dp, _dp, _dp, _ip, _dp, _d, _i, _d, _dp, _dp, _d, _i]
+    L.orc_gdn_step.argtypes = gdn
+    L.orc_gdn_step_buffered.argtypes = gdn + [_dp, _dp, _dp, _ip, _i, _i]
+    L.orc_conv1d_update.argtypes = [_i] * 4 + [_dp, _dp, _dp, _dp, _ip, _i, _dp, _i]
+    L.orc_kda_step.argtypes = [_i] * 4 + [_dp, _dp, _dp, _dp, _dp, _d, _dp, _ip, _dp,
+                                          _dp, _dp, _d, _d, _i, _d]
+    L.orc_kda_decode.argtypes = [_i] * 5 + [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _d,
+                                            _dp, _ip, _dp, _dp, _dp, _d, _d, _i, _d, _dp]
+    L.orc_mamba_step.argtypes = [_i] * 4 + [_dp] * 8 + [_ip, _dp]
+    for f in ("orc_gdn_step", "orc_gdn_step_buffered", "orc_conv1d_update",
+              "orc_kda_step", "orc_kda_decode", "orc_mamba_step", "orc_num_threads"):
+        getattr(L, f).restype = _i
+    return L
+
+
 def lib():
     """Load liboracle.so, building it first only if it is not there."""
     global _LIB
     if _LIB is None:
         if not os.path.exists(_build.LIB):
             _build.build()
-        L = ctypes.CDLL(_build.LIB)
-        L.orc_softplus.argtypes = [_d]
-        L.orc_sigmoid.argtypes = [_d]
-        L.orc_silu.argtypes = [_d]
-        L.orc_round_fmt.argtypes = [_d, _i]
-        L.orc_kda_gate.argtypes = [_d, _d, _d, _d]
-        for f in ("orc_softplus", "orc_sigmoid", "orc_silu", "orc_round_fmt", "orc_kda_gate"):
-            getattr(L, f).restype = _d
-        L.orc_gdn_gates.argtypes = [_d, _d, _d, _d, _dp, _dp]
-        L.orc_gdn_gates.restype = None
-        gdn = [_i] * 6 + [_dp, _l, _dp, _dp, _dp, _dp, _dp, _ip, _dp, _d, _i, _d, _dp, _dp, _d, _i]
-        L.orc_gdn_step.argtypes = gdn
-        L.orc_gdn_step_buffered.argtypes = gdn + [_dp, _dp, _dp, _ip, _i, _i]
-        L.orc_conv1d_update.argtypes = [_i] * 4 + [_dp, _dp, _dp, _dp, _ip, _i, _dp, _i]
-        L.orc_kda_step.argtypes = [_i] * 4 + [_dp, _dp, _dp, _dp, _dp, _d, _dp, _ip, _dp,
-                                              _dp, _dp, _d, _d, _i, _d]
-        L.orc_kda_decode.argtypes = [_i] * 5 + [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _d,
-                                                _dp, _ip, _dp, _dp, _dp, _d, _d, _i, _d, _dp]
-        L.orc_mamba_step.argtypes = [_i] * 4 + [_dp] * 8 + [_ip, _dp]
-        for f in ("orc_gdn_step", "orc_gdn_step_buffered", "orc_conv1d_update",
-                  "orc_kda_step", "orc_kda_decode", "orc_mamba_step", "orc_num_threads"):
-            getattr(L, f).restype = _i
-        _LIB = L
+        _LIB = configure(ctypes.CDLL(_build.LIB))
     return _LIB
 
 

@@ -13,16 +13,16 @@ SRC = os.path.join(HERE, "ssm_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
+def build(verbose: bool = False, src: str = SRC, lib: str = LIB) -> str:
+    tmp = lib + ".tmp"
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off",
            "-fno-fast-math", "-fPIC", "-shared", "-Wall", "-Wextra",
-           "-o", tmp, SRC, "-lm"]
+           "-o", tmp, src, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -66,7 +66,7 @@ def ssmd_last_error() -> str:
 
 def _check(rc: int, name: str):
     if rc != 0:
-        raise SsmdError(rc, f"{name}: {ssmd_last_error()}")
+        raise SsmdError(rc, ssmd_last_error() or name)
 
 
 def _ptr(t):

@@ -100,8 +100,8 @@ __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tile
   float qf[NV * 4], kf[NV * 4];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    load_act4(p.qkv, qrow + (int64_t)h * K + RL::col(c, j), p.act_dt, &qf[4 * j]);
-    load_act4(p.qkv, qrow + (int64_t)(p.H + h) * K + RL::col(c, j), p.act_dt, &kf[4 * j]);
+    load_act4(p.qkv, qrow + (int64_t)h * K + RL::col(c, j), p.act_dt, p.qkv_vec, &qf[4 * j]);
+    load_act4(p.qkv, qrow + (int64_t)(p.H + h) * K + RL::col(c, j), p.act_dt, p.qkv_vec, &kf[4 * j]);
   }
   float qs = p.scale, ks = 1.f;
   if (p.use_l2) {

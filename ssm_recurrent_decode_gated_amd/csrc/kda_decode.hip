@@ -132,7 +132,7 @@ __global__ __launch_bounds__(512) void kda_decode_kernel(KdaParams p) {
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     float rg[4];
-    load_act4(p.raw_g, hoff + RL::col(c, j), p.act_dt, rg);
+    load_act4(p.raw_g, hoff + RL::col(c, j), p.act_dt, p.raw_g_vec, rg);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float db = p.dt_bias ? p.dt_bias[h * D + RL::col(c, j) + e] : 0.f;

@@ -79,11 +79,9 @@ int check_gdn(const char* fn, const void* qkv, int64_t stride, const void* a, co
   if (!qkv || !a || !b || !A_log || !dt_bias || !state || !idx || !out)
     return fail(SSMD_ERR_NULL_ARG, "%s: a required pointer is NULL", fn);
   const int64_t need = 2LL * H * K + (int64_t)HV * V;
-  if (stride < need || stride % 4)
-    return fail(SSMD_ERR_BAD_SHAPE, "%s: qkv_row_stride %lld must be >= %lld and a multiple of 4", fn,
-                (long long)stride, (long long)need);
-  if (!aligned(qkv, 4 * dtype_bytes(act)))
-    return fail(SSMD_ERR_BAD_SHAPE, "%s: mixed_qkv must be %d-byte aligned", fn, 4 * dtype_bytes(act));
+  if (stride < need)
+    return fail(SSMD_ERR_BAD_SHAPE, "%s: qkv_row_stride %lld < 2*H*K + HV*V = %lld", fn, (long long)stride,
+                (long long)need);
   if (!aligned(state, 16)) return fail(SSMD_ERR_BAD_SHAPE, "%s: state must be 16-byte aligned", fn);
   if ((int64_t)B * HV * ((V + 7) / 8) >= (1LL << 31))
     return fail(SSMD_ERR_BAD_SHAPE, "%s: B*HV too large for one launch", fn);
@@ -100,6 +98,7 @@ ssmd::GdnParams gdn_params(const void* qkv, int64_t stride, const void* a, const
   ssmd::GdnParams p{};
   p.qkv = qkv;
   p.qkv_stride = stride;
+  p.qkv_vec = stride % 4 == 0 && aligned(qkv, 4 * dtype_bytes(act));
   p.a = a;
   p.b = b;
   p.A_log = A_log;
@@ -228,9 +227,7 @@ int kda_decode_step(const void* x, const float* conv_weight, const float* conv_b
   if (T == 0) return ok();
   if (!x || !conv_weight || !conv_state || !raw_g || !raw_beta || !state || !state_indices || !out)
     return fail(SSMD_ERR_NULL_ARG, "%s: a required pointer is NULL", fn);
-  if (!aligned(raw_g, 4 * dtype_bytes(act_dtype)) || !aligned(state, 16))
-    return fail(SSMD_ERR_BAD_SHAPE, "%s: raw_g must be %d-byte and state 16-byte aligned", fn,
-                4 * dtype_bytes(act_dtype));
+  if (!aligned(state, 16)) return fail(SSMD_ERR_BAD_SHAPE, "%s: state must be 16-byte aligned", fn);
   ssmd::KdaParams p{};
   p.x = x;
   p.conv_w = conv_weight;
@@ -240,6 +237,7 @@ int kda_decode_step(const void* x, const float* conv_weight, const float* conv_b
   p.cs_chan = cs_chan_stride;
   p.cs_tap = cs_tap_stride;
   p.raw_g = raw_g;
+  p.raw_g_vec = aligned(raw_g, 4 * dtype_bytes(act_dtype));
   p.raw_beta = raw_beta;
   p.A_log = A_log;
   p.dt_bias = dt_bias;

@@ -33,9 +33,18 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);  // RNE
 }
 
-// Load 4 consecutive activation elements (element offset `off`, a multiple of
-// 4 from a suitably aligned base) as fp32. `dt` is uniform across the wave.
-__device__ __forceinline__ void load_act4(const void* base, int64_t off, int dt, float out[4]) {
+__device__ __forceinline__ float load_act1(const void* base, int64_t off, int dt);
+
+// Load 4 consecutive activation elements (element offset `off`) as fp32.
+// With `vec` (base aligned to 4 elements and `off` a multiple of 4) this is
+// one 64/128-bit load; otherwise four element loads. `dt` and `vec` are
+// uniform across the wave.
+__device__ __forceinline__ void load_act4(const void* base, int64_t off, int dt, bool vec, float out[4]) {
+  if (!vec) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = load_act1(base, off + e, dt);
+    return;
+  }
   if (dt == SSMD_F32) {
     f4 v = *reinterpret_cast<const f4*>(static_cast<const float*>(base) + off);
     out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;

@@ -10,6 +10,7 @@ namespace ssmd {
 struct GdnParams {
   const void* qkv;
   int64_t qkv_stride;
+  bool qkv_vec;  // rows are 4-element aligned: q/k fragments use vector loads
   const void* a;
   const void* b;
   const float* A_log;
@@ -42,6 +43,7 @@ struct KdaParams {
   void* conv_state;
   int64_t cs_slot, cs_chan, cs_tap;
   const void* raw_g;
+  bool raw_g_vec;  // raw_g is 4-element aligned: vector loads
   const void* raw_beta;
   const float* A_log;
   const float* dt_bias;

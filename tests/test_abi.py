@@ -67,10 +67,7 @@ def _gdn(L, **kw):
     (dict(act=7), BAD_DTYPE),
     (dict(odt=-1), BAD_DTYPE),
     (dict(nact=3), BAD_DTYPE),
-    (dict(stride=8191), BAD_SHAPE),
-    (dict(stride=8190), BAD_SHAPE),
-    (dict(qkv=0x10002), BAD_SHAPE),      # bf16 activations need 8-byte alignment
-    (dict(act=0, qkv=0x10008), BAD_SHAPE),  # fp32 activations need 16-byte alignment
+    (dict(stride=8191), BAD_SHAPE),      # below 2*H*K + HV*V
     (dict(state=0x60004), BAD_SHAPE),
 ])
 def test_gdn_host_validation(kw, code):

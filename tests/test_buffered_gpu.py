@@ -7,6 +7,8 @@ folded state on flush rows, and untouched checkpoints and ring positions on
 the others. Chained runs follow the oracle's own bf16 ring over several
 cycles to the chained tolerance.
 """
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -72,6 +74,7 @@ def test_buffered_single_call_every_phase(case):
     assert_mixed(out.reshape(B, HV, V), ro, FP32_TOL, "output")
     got_st = st_d.cpu()
     got = {k: to_np64(v) for k, v in ring_d.items()}
+    ring0 = {k: v.double().numpy() for k, v in ring.items()}
     G = HV // H
     for b in range(B):
         s, p = int(idx[b]), phases[b]
@@ -83,28 +86,50 @@ def test_buffered_single_call_every_phase(case):
         _assert_ring16(got["k_cache"][s, :, p], ref_ring["k_cache"][s, :, p], f"key record row {b}")
         np.testing.assert_allclose(got["g_cache"][s, :, p], ref_ring["g_cache"][s, :, p], rtol=1e-5)
         others = [j for j in range(L) if j != p]
-        np.testing.assert_array_equal(got["d_cache"][s, :, others], ring["d_cache"][s, :, others].double().numpy())
-        np.testing.assert_array_equal(got["k_cache"][s, :, others], ring["k_cache"][s, :, others].double().numpy())
-        np.testing.assert_array_equal(got["g_cache"][s, :, others], ring["g_cache"][s, :, others].double().numpy())
+        for k in ring0:
+            np.testing.assert_array_equal(got[k][s][:, others], ring0[k][s][:, others], err_msg=f"{k} row {b}")
     for s in set(range(w.num_slots)) - set(idx.tolist()):
         assert torch.equal(got_st[s], st[s])
-        for k in ring:
-            np.testing.assert_array_equal(got[k][s], ring[k][s].double().numpy())
+        for k in ring0:
+            np.testing.assert_array_equal(got[k][s], ring0[k][s])
     assert G >= 1
 
 
-@pytest.mark.parametrize("L", [1, 8, 16])
-def test_buffered_chain_matches_oracle(L):
+RING_FLIP_MAX = 2.0 ** -6   # bf16 ring: largest error one or two record flips can cause
+RING_FLIP_FRAC = 1e-3       # ... and the share of elements they may touch
+
+
+def _assert_chain(x, ref, act, what):
+    """fp32 rings: the chained tolerance everywhere. bf16 rings: a record
+    whose exact value sits near a rounding midpoint may be stored as either
+    neighbour (both are correct roundings), and every later output of that
+    row moves by up to one bf16 ulp of that record's term (2^-8 relative when
+    the term dominates). Such flips are rare and local, so: almost every
+    element within the chained tolerance, none beyond 2^-6."""
+    if act == "f32":
+        return assert_mixed(x, ref, CHAIN_TOL, what)
+    from tests._helpers import mixed_err
+    xv = to_np64(x) if isinstance(x, torch.Tensor) else np.asarray(x)
+    err = mixed_err(xv.reshape(ref.shape), ref)
+    assert err.max() <= RING_FLIP_MAX, f"{what}: max err {err.max():.2e} > {RING_FLIP_MAX:.1e}"
+    frac = float((err > CHAIN_TOL).mean())
+    assert frac <= RING_FLIP_FRAC, f"{what}: {frac:.2%} of elements beyond {CHAIN_TOL}"
+    assert np.median(err) <= 1e-5, f"{what}: median err {np.median(err):.2e}"
+
+
+@pytest.mark.parametrize("L,act", [(1, "bf16"), (8, "f32"), (16, "f32"), (8, "bf16"), (16, "bf16")])
+def test_buffered_chain_matches_oracle(L, act):
     """B=64, H=16, HV=32, K=V=128 (the long-horizon workload) for 3 full
     cycles from a zeroed ring at write_pos 0, the host advancing write_pos.
-    The oracle follows rows 5 and 40 with its own bf16 ring."""
+    The oracle follows rows 5 and 40 with its own ring in the same format."""
     need_gpu()
-    w = W.GDN_B64_CHAIN
+    w = replace(W.GDN_B64_CHAIN, act=act, name=W.GDN_B64_CHAIN.name + "_" + act)
+    tdt = W.DTYPES[act]
     P, idx = W.gdn_params(w), W.slot_indices(w)
     st = W.gdn_state(w)
     st_d = st.to(DEV)
-    ring_d = {"d_cache": torch.zeros(w.num_slots, w.HV, L, w.V, dtype=torch.bfloat16, device=DEV),
-              "k_cache": torch.zeros(w.num_slots, w.H, L, w.K, dtype=torch.bfloat16, device=DEV),
+    ring_d = {"d_cache": torch.zeros(w.num_slots, w.HV, L, w.V, dtype=tdt, device=DEV),
+              "k_cache": torch.zeros(w.num_slots, w.H, L, w.K, dtype=tdt, device=DEV),
               "g_cache": torch.zeros(w.num_slots, w.HV, L, device=DEV)}
     rows = [5, 40]
     ref = st[rows].double().numpy().copy()
@@ -112,6 +137,7 @@ def test_buffered_chain_matches_oracle(L):
     sub = np.arange(2, dtype=np.int32)
     out = torch.empty(w.B, 1, w.HV, w.V, device=DEV)
     Pd = {k: v.to(DEV) for k, v in P.items()}
+    fmt = O.FMT_F32 if act == "f32" else O.FMT_BF16
     for t in range(3 * L if L > 1 else 8):
         x = W.gdn_step_inputs(w, 5000 + t)
         p = t % L
@@ -121,10 +147,10 @@ def test_buffered_chain_matches_oracle(L):
                                    ring_d["k_cache"], ring_d["g_cache"], wp.to(DEV))
         ro = O.gdn_step_buffered(x["qkv"][rows], x["a"][rows], x["b"][rows], P["A_log"], P["dt_bias"], ref,
                                  sub, rr["d"], rr["k"], rr["g"], np.full(2, p, np.int32), L,
-                                 H=w.H, HV=w.HV, K=w.K, V=w.V, ring_fmt=O.FMT_BF16)
-        assert_mixed(out[rows].reshape(2, w.HV, w.V), ro, CHAIN_TOL, f"output step {t} (phase {p})")
+                                 H=w.H, HV=w.HV, K=w.K, V=w.V, ring_fmt=fmt)
+        _assert_chain(out[rows].reshape(2, w.HV, w.V), ro, act, f"output step {t} (phase {p})")
         if p == L - 1:
-            assert_mixed(st_d[rows], ref, CHAIN_TOL, f"checkpoint after step {t}")
+            _assert_chain(st_d[rows], ref, act, f"checkpoint after step {t}")
 
 
 def test_buffered_L1_equals_packed_on_gpu():
