@@ -25,10 +25,16 @@
 
 namespace ssmd {
 
-template <int K, int RG, bool NORM>
+template <int K>
+constexpr int buf_rg() {
+  return K == 16 ? 1 : (K == 32 ? 2 : (K == 256 ? 2 : 4));
+}
+
+template <int K, bool NORM, int ACT, bool VEC>
 __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tiles_per_head,
                                                            int rows_per_tile) {
   using RL = RowLayout<K>;
+  constexpr int RG = buf_rg<K>();
   constexpr int LPR = RL::LPR, NV = RL::NV, RPI = RL::RPI, ROWS = RG * RPI;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -54,55 +60,92 @@ __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tile
   const int r1 = min(V, r0 + rows_per_tile);
   const int64_t qrow = (int64_t)bi * p.qkv_stride;
   const int64_t vbase = qrow + 2 * (int64_t)p.H * K + (int64_t)hv * V;
+  const int64_t gidx = (int64_t)bi * p.HV + hv;
+  // rows of a pass are interleaved across the block's waves
+  auto row_of = [&](int pass, int i) { return pass + (i * nwaves + wave) * RPI + rr; };
 
   // LDS: kr [pos][K] ring keys, dr [pos][rows_per_tile] ring deltas of this
-  // tile, cf [pos + 1] coefficients (c_j, then c_ck), ca / cg [pos] = c_j
-  // times the record's dot with k / q.
+  // tile, gl [pos] ring log decays, cf [pos + 1] coefficients (c_j, then
+  // c_ck), ca / cg [pos] = c_j times the record's dot with k / q, rk / rq
+  // [rows_per_tile] = the ring's share of (S_{p-1} k) and (S_{p-1} q) per row.
   extern __shared__ float lds[];
   float* kr = lds;
   float* dr = kr + pos * K;
-  float* cf = dr + pos * rows_per_tile;
+  float* gl = dr + pos * rows_per_tile;
+  float* cf = gl + pos;
   float* ca = cf + pos + 1;
   float* cg = ca + pos;
+  float* rk = cg + pos;
+  float* rq = rk + rows_per_tile;
   __shared__ float o_lds[NORM ? 1024 : 1];
   __shared__ float red_lds[1];
 
-  // ---- first pass of checkpoint loads
-  int base = r0 + wave * ROWS;
-  f4 s[RG][NV];
-  float vv[RG];
-#pragma unroll
-  for (int i = 0; i < RG; ++i) {
-    const int row = base + i * RPI + rr;
-#pragma unroll
-    for (int j = 0; j < NV; ++j)
-      s[i][j] = row < r1 ? ld4<false>(S + (int64_t)row * K + RL::col(c, j)) : f4{0.f, 0.f, 0.f, 0.f};
-    vv[i] = row < r1 ? load_act1(p.qkv, vbase + row, p.act_dt) : 0.f;
-  }
-
-  // ---- stage the ring records of this cycle (j < pos)
-  const int64_t kr_g = ((int64_t)slot * p.H + h) * p.L * K;
-  for (int e = tid; e < pos * K; e += blockDim.x) kr[e] = load_act1(p.k_cache, kr_g + e, p.act_dt);
-  const int tr = r1 - r0;
-  const int64_t dr_g = ((int64_t)slot * p.HV + hv) * p.L * V;
-  for (int e = tid; e < pos * tr; e += blockDim.x) {
-    const int j = e / tr, r = e - j * tr;
-    dr[j * rows_per_tile + r] = load_act1(p.d_cache, dr_g + (int64_t)j * V + r0 + r, p.act_dt);
-  }
-  const float* gr = p.g_cache + ((int64_t)slot * p.HV + hv) * p.L;
-  if (tid <= pos) {
-    float sum = 0.f;
-    for (int i = (tid < pos ? tid + 1 : 0); i < pos; ++i) sum += gr[i];
-    cf[tid] = expf(sum);
-  }
-
-  // ---- prologue: q/k fragments, L2 norms, gates
+  // ---- small loads first (activations, then this cycle's ring records
+  // j < pos), then the checkpoint stream: waiting for the small ones never
+  // waits for the stream. The ring staging issues up to RING_U loads per
+  // thread before its first LDS store.
   float qf[NV * 4], kf[NV * 4];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    load_act4(p.qkv, qrow + (int64_t)h * K + RL::col(c, j), p.act_dt, p.qkv_vec, &qf[4 * j]);
-    load_act4(p.qkv, qrow + (int64_t)(p.H + h) * K + RL::col(c, j), p.act_dt, p.qkv_vec, &kf[4 * j]);
+    ld_act4<ACT, VEC>(p.qkv, qrow + (int64_t)h * K + RL::col(c, j), &qf[4 * j]);
+    ld_act4<ACT, VEC>(p.qkv, qrow + (int64_t)(p.H + h) * K + RL::col(c, j), &kf[4 * j]);
   }
+  const float av = ld_act<ACT>(p.a, gidx);
+  const float bv = ld_act<ACT>(p.b, gidx);
+  const float A_log = p.A_log[hv];
+  const float dt_bias = p.dt_bias[hv];
+  const int64_t kr_g = ((int64_t)slot * p.H + h) * p.L * K;
+  const int tr = r1 - r0;
+  const int64_t dr_g = ((int64_t)slot * p.HV + hv) * p.L * V;
+  const float* gr = p.g_cache + ((int64_t)slot * p.HV + hv) * p.L;
+  const int nk = pos * K, nd = pos * tr, bd = blockDim.x;
+  constexpr int RING_U = 8;
+  float kt[RING_U], dt[RING_U];
+  float gt = 0.f;
+  if (pos > 0) {  // uniform: clamped indices, no per-element branch
+#pragma unroll
+    for (int m = 0; m < RING_U; ++m) kt[m] = ld_act<ACT>(p.k_cache, kr_g + min(tid + m * bd, nk - 1));
+#pragma unroll
+    for (int m = 0; m < RING_U; ++m) {
+      const int e = min(tid + m * bd, nd - 1);
+      const int j = e / tr;
+      dt[m] = ld_act<ACT>(p.d_cache, dr_g + (int64_t)j * V + r0 + (e - j * tr));
+    }
+    gt = gr[min(tid, pos - 1)];
+  }
+  f4 s[RG][NV];
+  float vv[RG];
+  auto load_group = [&](int pass, int i) {
+    const int row = min(row_of(pass, i), r1 - 1);  // past-the-end rows re-read the last one
+    vv[i] = ld_act<ACT>(p.qkv, vbase + row);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) s[i][j] = ld4<true>(S + (int64_t)row * K + RL::col(c, j));
+  };
+  int pass = r0;
+#pragma unroll
+  for (int i = 0; i < RG; ++i) load_group(pass, i);
+
+  // ---- ring records to LDS (rare long rings finish with a plain loop)
+  if (pos > 0) {
+#pragma unroll
+    for (int m = 0; m < RING_U; ++m) {
+      const int e = tid + m * bd;
+      if (e < nk) kr[e] = kt[m];
+      if (e < nd) {
+        const int j = e / tr;
+        dr[j * rows_per_tile + (e - j * tr)] = dt[m];
+      }
+    }
+    for (int e = tid + RING_U * bd; e < nk; e += bd) kr[e] = ld_act<ACT>(p.k_cache, kr_g + e);
+    for (int e = tid + RING_U * bd; e < nd; e += bd) {
+      const int j = e / tr;
+      dr[j * rows_per_tile + (e - j * tr)] = ld_act<ACT>(p.d_cache, dr_g + (int64_t)j * V + r0 + (e - j * tr));
+    }
+    if (tid < pos) gl[tid] = gt;
+    for (int e = tid + bd; e < pos; e += bd) gl[e] = gr[e];
+  }
+
+  // ---- prologue: L2 norms, scale, gates
   float qs = p.scale, ks = 1.f;
   if (p.use_l2) {
     float sq = 0.f, sk = 0.f;
@@ -124,12 +167,17 @@ __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tile
     kq += kf[e] * qf[e];
   }
   kq = group_sum<LPR>(kq);
-  const int64_t gidx = (int64_t)bi * p.HV + hv;
-  const float av = load_act1(p.a, gidx, p.act_dt);
-  const float bv = load_act1(p.b, gidx, p.act_dt);
-  const float g = -expf(p.A_log[hv]) * softplus_f(av + p.dt_bias[hv]);
+  const float g = -expf(A_log) * softplus_f(av + dt_bias);
   const float beta = sigmoid_f(bv);
   const float decay = expf(g);
+  __syncthreads();
+
+  // ---- replay coefficients: c_j = exp(sum_{j<i<pos} g_i), c_ck = exp(sum_{i<pos} g_i)
+  if (tid <= pos) {
+    float sum = 0.f;
+    for (int i = (tid < pos ? tid + 1 : 0); i < pos; ++i) sum += gl[i];
+    cf[tid] = expf(sum);
+  }
   __syncthreads();
 
   // ---- record dots: lane group (wave, rr) takes records j = wave*RPI + rr + m*nwaves*RPI
@@ -149,12 +197,22 @@ __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tile
     }
   }
   __syncthreads();
+
+  // ---- the ring's share of S_{p-1} k and S_{p-1} q, once per row
+  for (int e = tid; e < 2 * tr; e += bd) {
+    const int r = e < tr ? e : e - tr;
+    const float* coef = e < tr ? ca : cg;
+    float acc = 0.f;
+    for (int j = 0; j < pos; ++j) acc += coef[j] * dr[j * rows_per_tile + r];
+    (e < tr ? rk : rq)[r] = acc;
+  }
+  __syncthreads();
   const float cck = cf[pos];
   const int64_t obase = gidx * V;
   const int64_t dw = dr_g + (int64_t)pos * V;  // this step's delta record
 
   // ---- stream the checkpoint rows
-  while (base < r1) {
+  while (true) {
     float delta[RG];
 #pragma unroll
     for (int i = 0; i < RG; ++i) {
@@ -168,20 +226,14 @@ __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tile
       }
       dk = group_sum<LPR>(dk);
       dq = group_sum<LPR>(dq);
-      const int row = base + i * RPI + rr;
-      float sk = cck * dk, sqv = cck * dq;
-      if (row < r1) {
-        const float* dcol = dr + (row - r0);
-        for (int j = 0; j < pos; ++j) {
-          const float d = dcol[j * rows_per_tile];
-          sk += ca[j] * d;
-          sqv += cg[j] * d;
-        }
-      }
+      const int row = row_of(pass, i);
+      const int rowc = min(row, r1 - 1);
+      const float sk = cck * dk + rk[rowc - r0];
+      const float sqv = cck * dq + rq[rowc - r0];
       delta[i] = beta * (vv[i] - decay * sk);
       const float o = decay * sqv + delta[i] * kq;
       if (row < r1 && c == 0) {
-        store_act1(p.d_cache, dw + row, p.act_dt, delta[i]);
+        st_act<ACT>(p.d_cache, dw + row, delta[i]);
         if constexpr (NORM) o_lds[row] = o;
         else store_act1(p.out, obase + row, p.out_dt, o);
       }
@@ -199,15 +251,15 @@ __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tile
         const float cj = cf[j];
 #pragma unroll
         for (int i = 0; i < RG; ++i) {
-          const int row = base + i * RPI + rr;
-          const float e = row < r1 ? cj * dr[j * rows_per_tile + row - r0] : 0.f;
+          const int rowc = min(row_of(pass, i), r1 - 1);
+          const float e = cj * dr[j * rows_per_tile + rowc - r0];
 #pragma unroll
           for (int jj = 0; jj < NV; ++jj) s[i][jj] += e * kv[jj];
         }
       }
 #pragma unroll
       for (int i = 0; i < RG; ++i) {
-        const int row = base + i * RPI + rr;
+        const int row = row_of(pass, i);
         if (row < r1) {
 #pragma unroll
           for (int j = 0; j < NV; ++j) {
@@ -216,22 +268,15 @@ __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tile
             n.y = decay * s[i][j].y + delta[i] * kf[4 * j + 1];
             n.z = decay * s[i][j].z + delta[i] * kf[4 * j + 2];
             n.w = decay * s[i][j].w + delta[i] * kf[4 * j + 3];
-            st4<false>(S + (int64_t)row * K + RL::col(c, j), n);
+            st4<true>(S + (int64_t)row * K + RL::col(c, j), n);
           }
         }
       }
     }
-    base += nwaves * ROWS;
-    if (base < r1) {
+    pass += nwaves * ROWS;
+    if (pass >= r1) break;
 #pragma unroll
-      for (int i = 0; i < RG; ++i) {
-        const int row = base + i * RPI + rr;
-#pragma unroll
-        for (int j = 0; j < NV; ++j)
-          s[i][j] = row < r1 ? ld4<false>(S + (int64_t)row * K + RL::col(c, j)) : f4{0.f, 0.f, 0.f, 0.f};
-        vv[i] = row < r1 ? load_act1(p.qkv, vbase + row, p.act_dt) : 0.f;
-      }
-    }
+    for (int i = 0; i < RG; ++i) load_group(pass, i);
   }
 
   // ---- append this step's key (once per q/k head) and g
@@ -240,7 +285,7 @@ __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tile
 #pragma unroll
     for (int j = 0; j < NV; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) store_act1(p.k_cache, kw + RL::col(c, j) + e, p.act_dt, kf[4 * j + e]);
+      for (int e = 0; e < 4; ++e) st_act<ACT>(p.k_cache, kw + RL::col(c, j) + e, kf[4 * j + e]);
   }
   if (tile == 0 && tid == 0) p.g_cache[((int64_t)slot * p.HV + hv) * p.L + pos] = g;
 
@@ -255,7 +300,7 @@ __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tile
     __syncthreads();
     const float inv = rsqrtf(red_lds[0] / (float)V + p.norm_eps);
     for (int r = tid; r < V; r += blockDim.x) {
-      const float z = load_act1(p.norm_gate, obase + r, p.act_dt);
+      const float z = ld_act<ACT>(p.norm_gate, obase + r);
       const float gz = p.norm_act == SSMD_ACT_SIGMOID ? sigmoid_f(z) : silu_f(z);
       const float w = p.norm_w ? p.norm_w[r] : 1.f;
       store_act1(p.out, obase + r, p.out_dt, o_lds[r] * inv * w * gz);
@@ -265,51 +310,69 @@ __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tile
 
 namespace {
 
-template <int K, int RG>
-hipError_t launch_bk(const GdnParams& p, int wpb, hipStream_t st) {
+template <int K, bool NORM, int ACT, bool VEC>
+hipError_t launch_bk(const GdnParams& p, const Launch& l, hipStream_t st) {
   constexpr int RPI = RowLayout<K>::RPI;
-  const int wave_rows = RG * RPI;
-  const bool norm = p.norm_gate != nullptr;
+  const int wave_rows = buf_rg<K>() * RPI;
+  int wpb = l.wpb;
   int tiles, rows_per_tile;
-  if (norm) {
+  if (NORM) {
     tiles = 1;
     rows_per_tile = p.V;
   } else {
     rows_per_tile = wpb * wave_rows;
     tiles = (p.V + rows_per_tile - 1) / rows_per_tile;
   }
-  int need = (min(p.V, rows_per_tile) + wave_rows - 1) / wave_rows;
+  const int need = (min(p.V, rows_per_tile) + wave_rows - 1) / wave_rows;
   if (wpb > need) wpb = need;
-  const int pmax = p.L - 1;
-  const size_t lds = sizeof(float) * ((size_t)pmax * K + (size_t)pmax * rows_per_tile + 3 * (size_t)pmax + 1);
+  const size_t lds = buffered_lds_bytes(K, rows_per_tile, p.L);
   const dim3 grid((unsigned)((int64_t)p.B * p.HV * tiles));
-  const dim3 block(64 * wpb);
-  if (norm)
-    gdn_buffered_kernel<K, RG, true><<<grid, block, lds, st>>>(p, tiles, rows_per_tile);
-  else
-    gdn_buffered_kernel<K, RG, false><<<grid, block, lds, st>>>(p, tiles, rows_per_tile);
+  gdn_buffered_kernel<K, NORM, ACT, VEC><<<grid, dim3(64 * wpb), lds, st>>>(p, tiles, rows_per_tile);
   return hipGetLastError();
 }
 
-template <int K>
-hipError_t launch_brg(const GdnParams& p, const Launch& l, hipStream_t st) {
-  switch (l.rg) {
-    case 1: return launch_bk<K, 1>(p, l.wpb, st);
-    case 2: return launch_bk<K, 2>(p, l.wpb, st);
-    case 4: return launch_bk<K, 4>(p, l.wpb, st);
-    default: return hipErrorInvalidValue;
+template <int K, bool NORM>
+hipError_t launch_bact(const GdnParams& p, const Launch& l, hipStream_t st) {
+  const bool vec = p.qkv_vec;
+  switch (p.act_dt) {
+    case SSMD_F32: return vec ? launch_bk<K, NORM, SSMD_F32, true>(p, l, st) : launch_bk<K, NORM, SSMD_F32, false>(p, l, st);
+    case SSMD_BF16: return vec ? launch_bk<K, NORM, SSMD_BF16, true>(p, l, st) : launch_bk<K, NORM, SSMD_BF16, false>(p, l, st);
+    default: return vec ? launch_bk<K, NORM, SSMD_F16, true>(p, l, st) : launch_bk<K, NORM, SSMD_F16, false>(p, l, st);
   }
+}
+
+template <int K>
+hipError_t launch_bnorm(const GdnParams& p, const Launch& l, hipStream_t st) {
+  return p.norm_gate ? launch_bact<K, true>(p, l, st) : launch_bact<K, false>(p, l, st);
 }
 
 }  // namespace
 
+// LDS of the ring staging for a tile of `rows` rows: kr, dr, gl, cf, ca, cg,
+// rk, rq (see the kernel); the host checks it against the budget.
+size_t buffered_lds_bytes(int K, int rows, int L) {
+  const size_t pm = (size_t)(L - 1);
+  return sizeof(float) * (pm * (size_t)K + pm * (size_t)rows + 4 * pm + 1 + 2 * (size_t)rows);
+}
+
+int buffered_rows_per_tile(int K, int V, bool norm, const Launch& l) {
+  if (norm) return V;
+  switch (K) {
+    case 16: return l.wpb * buf_rg<16>() * RowLayout<16>::RPI;
+    case 32: return l.wpb * buf_rg<32>() * RowLayout<32>::RPI;
+    case 64: return l.wpb * buf_rg<64>() * RowLayout<64>::RPI;
+    case 128: return l.wpb * buf_rg<128>() * RowLayout<128>::RPI;
+    default: return l.wpb * buf_rg<256>() * RowLayout<256>::RPI;
+  }
+}
+
 hipError_t launch_gdn_buffered(const GdnParams& p, const Launch& l, hipStream_t st) {
   switch (p.K) {
-    case 16: return launch_brg<16>(p, l, st);
-    case 32: return launch_brg<32>(p, l, st);
-    case 64: return launch_brg<64>(p, l, st);
-    case 128: return launch_brg<128>(p, l, st);
-    case 256: return launch_brg<256>(p, l, st);
+    case 16: return launch_bnorm<16>(p, l, st);
+    case 32: return launch_bnorm<32>(p, l, st);
+    case 64: return launch_bnorm<64>(p, l, st);
+    case 128: return launch_bnorm<128>(p, l, st);
+    case 256: return launch_bnorm<256>(p, l, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -14,15 +14,24 @@
 // through HBM). The state rows then stream exactly as in the GDN kernel, with
 // the decay a per-column vector (lane constants, since a lane's columns are
 // fixed). The gated RMSNorm needs the whole head, so the block owns all D
-// rows. The first pass of state loads is issued before the conv prologue.
+// rows. The gate inputs and the first pass of state loads are issued before
+// the conv prologue, so the state stream is in flight while the conv runs.
+#include <type_traits>
+
 #include "ssmd_device.h"
 #include "ssmd_internal.h"
 
 namespace ssmd {
 
-template <int D, int RG, bool NORM>
+template <int D>
+constexpr int kda_rg() {
+  return D == 16 ? 1 : (D == 32 ? 2 : (D == 256 ? 2 : 4));
+}
+
+template <int D, bool NORM, int ACT, bool VEC>
 __global__ __launch_bounds__(512) void kda_decode_kernel(KdaParams p) {
   using RL = RowLayout<D>;
+  constexpr int RG = kda_rg<D>();
   constexpr int LPR = RL::LPR, NV = RL::NV, RPI = RL::RPI, ROWS = RG * RPI;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -36,63 +45,84 @@ __global__ __launch_bounds__(512) void kda_decode_kernel(KdaParams p) {
   const int slot = p.idx[t];
   if (slot <= 0 || slot >= p.num_slots) return;  // NULL block or padding
   float* S = p.state + ((int64_t)slot * p.H + h) * (int64_t)D * D;
+  auto row_of = [&](int pass, int i) { return pass + (i * nwaves + wave) * RPI + rr; };
+  const int64_t hoff = ((int64_t)t * p.H + h) * D;
 
-  // ---- first pass of state loads
-  int base = wave * ROWS;
-  f4 s[RG][NV];
+  // ---- small loads first (this thread's conv channels: state taps and x;
+  // the gate inputs), then the first pass of state loads: waiting for the
+  // small ones never waits for the state stream.
+  using T = typename std::conditional<ACT == SSMD_F32, float, uint16_t>::type;
+  constexpr int CPT = 4;   // conv channels per thread held in registers (3*D <= CPT*blockDim)
+  constexpr int WMAX = 8;  // widest conv accepted by the host
+  const int C = 3 * p.H * D;
+  const int W = p.W;
+  const int nch = 3 * D;
+  T* cs = static_cast<T*>(p.conv_state);
+  const T* xr = static_cast<const T*>(p.x) + (int64_t)t * C;
+  const int64_t cs_base = (int64_t)slot * p.cs_slot;
+  auto chan = [&](int ci) {  // global channel of head-local channel ci (q, k, v slices)
+    const int part = ci / D;
+    return part * p.H * D + h * D + (ci - part * D);
+  };
+  T raw[CPT][WMAX];  // window = [state taps 0..W-2 (oldest first), x]
 #pragma unroll
-  for (int i = 0; i < RG; ++i) {
-    const int row = base + i * RPI + rr;
+  for (int m = 0; m < CPT; ++m) {
+    const int gc = chan(min(tid + m * (int)blockDim.x, nch - 1));
+    const int64_t cso = cs_base + (int64_t)gc * p.cs_chan;
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
-      s[i][j] = row < D ? ld4<false>(S + (int64_t)row * D + RL::col(c, j)) : f4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < WMAX - 1; ++j)
+      if (j < W - 1) raw[m][j] = cs[cso + (int64_t)j * p.cs_tap];
+    raw[m][WMAX - 1] = xr[gc];
   }
+  float rg[NV * 4];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) ld_act4<ACT, VEC>(p.raw_g, hoff + RL::col(c, j), &rg[4 * j]);
+  const float rbeta = ld_act<ACT>(p.raw_beta, (int64_t)t * p.H + h);
+  f4 s[RG][NV];
+  auto load_group = [&](int pass, int i) {
+    const int row = min(row_of(pass, i), D - 1);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) s[i][j] = ld4<true>(S + (int64_t)row * D + RL::col(c, j));
+  };
+  int pass = 0;
+#pragma unroll
+  for (int i = 0; i < RG; ++i) load_group(pass, i);
 
   // ---- conv update of this head's q, k, v channels -> y (LDS, fp32)
   __shared__ float y[3 * D];
   __shared__ float o_lds[NORM ? D : 1];
   __shared__ float red_lds[1];
-  const int C = 3 * p.H * D;
-  const int W = p.W;
-  {
-    const int64_t xrow = (int64_t)t * C;
-    uint16_t* cs16 = static_cast<uint16_t*>(p.conv_state);
-    float* cs32 = static_cast<float*>(p.conv_state);
-    const int64_t cs_base = (int64_t)slot * p.cs_slot;
-    for (int ci = tid; ci < 3 * D; ci += blockDim.x) {
-      const int part = ci / D;  // 0 = q, 1 = k, 2 = v
-      const int gc = part * p.H * D + h * D + (ci - part * D);
-      const float* wr = p.conv_w + (int64_t)gc * W;
-      const int64_t cso = cs_base + (int64_t)gc * p.cs_chan;
-      // window = [state taps 0..W-2 (oldest first), x]; raw bits kept for the roll
-      uint32_t raw[8];
-      float win[8];
-      for (int j = 0; j < W - 1; ++j) {
-        const int64_t o = cso + (int64_t)j * p.cs_tap;
-        if (p.act_dt == SSMD_F32) {
-          win[j] = cs32[o];
-          raw[j] = __float_as_uint(win[j]);
-        } else {
-          raw[j] = cs16[o];
-          win[j] = p.act_dt == SSMD_BF16 ? bf16_bits_to_f32(raw[j]) : f16_bits_to_f32(raw[j]);
-        }
-      }
-      if (p.act_dt == SSMD_F32) {
-        win[W - 1] = static_cast<const float*>(p.x)[xrow + gc];
-        raw[W - 1] = __float_as_uint(win[W - 1]);
-      } else {
-        raw[W - 1] = static_cast<const uint16_t*>(p.x)[xrow + gc];
-        win[W - 1] = p.act_dt == SSMD_BF16 ? bf16_bits_to_f32(raw[W - 1]) : f16_bits_to_f32(raw[W - 1]);
-      }
-      float acc = p.conv_b ? p.conv_b[gc] : 0.f;
-      for (int j = 0; j < W; ++j) acc += wr[j] * win[j];
-      for (int j = 0; j < W - 1; ++j) {  // roll: tap j <- window[j + 1]
-        const int64_t o = cso + (int64_t)j * p.cs_tap;
-        if (p.act_dt == SSMD_F32) cs32[o] = __uint_as_float(raw[j + 1]);
-        else cs16[o] = (uint16_t)raw[j + 1];
-      }
-      y[ci] = silu_f(acc);
-    }
+  auto to_f = [](T v) -> float {
+    if constexpr (ACT == SSMD_F32) return v;
+    else if constexpr (ACT == SSMD_BF16) return bf16_bits_to_f32(v);
+    else return f16_bits_to_f32(v);
+  };
+  auto conv_channel = [&](int ci, const T* win_state, T xv) {
+    const int gc = chan(ci);
+    const float* wr = p.conv_w + (int64_t)gc * W;
+    const int64_t cso = cs_base + (int64_t)gc * p.cs_chan;
+    float acc = p.conv_b ? p.conv_b[gc] : 0.f;
+#pragma unroll
+    for (int j = 0; j < WMAX - 1; ++j)
+      if (j < W - 1) acc += wr[j] * to_f(win_state[j]);
+    acc += wr[W - 1] * to_f(xv);
+    // roll: tap j <- window[j + 1]; the newest tap takes x
+#pragma unroll
+    for (int j = 0; j < WMAX - 2; ++j)
+      if (j < W - 2) cs[cso + (int64_t)j * p.cs_tap] = win_state[j + 1];
+    cs[cso + (int64_t)(W - 2) * p.cs_tap] = xv;
+    y[ci] = silu_f(acc);
+  };
+#pragma unroll
+  for (int m = 0; m < CPT; ++m) {
+    const int ci = tid + m * (int)blockDim.x;
+    if (ci < nch) conv_channel(ci, raw[m], raw[m][WMAX - 1]);
+  }
+  for (int ci = tid + CPT * (int)blockDim.x; ci < nch; ci += blockDim.x) {  // only with tiny blocks
+    T win[WMAX];
+    const int64_t cso = cs_base + (int64_t)chan(ci) * p.cs_chan;
+    for (int j = 0; j < W - 1; ++j) win[j] = cs[cso + (int64_t)j * p.cs_tap];
+    conv_channel(ci, win, xr[chan(ci)]);
   }
   __syncthreads();
 
@@ -127,22 +157,19 @@ __global__ __launch_bounds__(512) void kda_decode_kernel(KdaParams p) {
     kq += kf[e] * qf[e];
   }
   kq = group_sum<LPR>(kq);
-  const int64_t hoff = ((int64_t)t * p.H + h) * D;
   const float ea = p.A_log ? expf(p.A_log[h]) : 1.f;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    float rg[4];
-    load_act4(p.raw_g, hoff + RL::col(c, j), p.act_dt, p.raw_g_vec, rg);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float db = p.dt_bias ? p.dt_bias[h * D + RL::col(c, j) + e] : 0.f;
-      dec[4 * j + e] = expf(p.lower_bound * sigmoid_f(ea * (rg[e] + db)));
+      dec[4 * j + e] = expf(p.lower_bound * sigmoid_f(ea * (rg[4 * j + e] + db)));
     }
   }
-  const float beta = sigmoid_f(load_act1(p.raw_beta, (int64_t)t * p.H + h, p.act_dt));
+  const float beta = sigmoid_f(rbeta);
 
   // ---- stream the state rows
-  while (base < D) {
+  while (true) {
 #pragma unroll
     for (int i = 0; i < RG; ++i) {
       float dk = 0.f, dq = 0.f;
@@ -159,8 +186,8 @@ __global__ __launch_bounds__(512) void kda_decode_kernel(KdaParams p) {
       }
       dk = group_sum<LPR>(dk);
       dq = group_sum<LPR>(dq);
-      const int row = base + i * RPI + rr;
-      const float vrow = row < D ? y[2 * D + row] : 0.f;
+      const int row = row_of(pass, i);
+      const float vrow = y[2 * D + min(row, D - 1)];
       const float delta = beta * (vrow - dk);
       const float o = dq + delta * kq;
       if (row < D) {
@@ -171,7 +198,7 @@ __global__ __launch_bounds__(512) void kda_decode_kernel(KdaParams p) {
           n.y = s[i][j].y + delta * kf[4 * j + 1];
           n.z = s[i][j].z + delta * kf[4 * j + 2];
           n.w = s[i][j].w + delta * kf[4 * j + 3];
-          st4<false>(S + (int64_t)row * D + RL::col(c, j), n);
+          st4<true>(S + (int64_t)row * D + RL::col(c, j), n);
         }
         if (c == 0) {
           if constexpr (NORM) o_lds[row] = o;
@@ -179,16 +206,10 @@ __global__ __launch_bounds__(512) void kda_decode_kernel(KdaParams p) {
         }
       }
     }
-    base += nwaves * ROWS;
-    if (base < D) {
+    pass += nwaves * ROWS;
+    if (pass >= D) break;
 #pragma unroll
-      for (int i = 0; i < RG; ++i) {
-        const int row = base + i * RPI + rr;
-#pragma unroll
-        for (int j = 0; j < NV; ++j)
-          s[i][j] = row < D ? ld4<false>(S + (int64_t)row * D + RL::col(c, j)) : f4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
+    for (int i = 0; i < RG; ++i) load_group(pass, i);
   }
 
   if constexpr (NORM) {
@@ -202,7 +223,7 @@ __global__ __launch_bounds__(512) void kda_decode_kernel(KdaParams p) {
     __syncthreads();
     const float inv = rsqrtf(red_lds[0] / (float)D + p.norm_eps);
     for (int r = tid; r < D; r += blockDim.x) {
-      const float gz = sigmoid_f(load_act1(p.gate, hoff + r, p.act_dt));
+      const float gz = sigmoid_f(ld_act<ACT>(p.gate, hoff + r));
       const float w = p.norm_w ? p.norm_w[r] : 1.f;
       store_act1(p.out, hoff + r, p.out_dt, o_lds[r] * inv * w * gz);
     }
@@ -211,40 +232,41 @@ __global__ __launch_bounds__(512) void kda_decode_kernel(KdaParams p) {
 
 namespace {
 
-template <int D, int RG>
-hipError_t launch_kk(const KdaParams& p, int wpb, hipStream_t st) {
+template <int D, bool NORM, int ACT, bool VEC>
+hipError_t launch_kk(const KdaParams& p, const Launch& l, hipStream_t st) {
   constexpr int RPI = RowLayout<D>::RPI;
-  const int wave_rows = RG * RPI;
+  const int wave_rows = kda_rg<D>() * RPI;
   const int need = (D + wave_rows - 1) / wave_rows;
-  if (wpb > need) wpb = need;
+  const int wpb = l.wpb > need ? need : l.wpb;
   const dim3 grid((unsigned)((int64_t)p.T * p.H));
-  const dim3 block(64 * wpb);
-  if (p.gate)
-    kda_decode_kernel<D, RG, true><<<grid, block, 0, st>>>(p);
-  else
-    kda_decode_kernel<D, RG, false><<<grid, block, 0, st>>>(p);
+  kda_decode_kernel<D, NORM, ACT, VEC><<<grid, dim3(64 * wpb), 0, st>>>(p);
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_krg(const KdaParams& p, const Launch& l, hipStream_t st) {
-  switch (l.rg) {
-    case 1: return launch_kk<D, 1>(p, l.wpb, st);
-    case 2: return launch_kk<D, 2>(p, l.wpb, st);
-    case 4: return launch_kk<D, 4>(p, l.wpb, st);
-    default: return hipErrorInvalidValue;
+template <int D, bool NORM>
+hipError_t launch_kact(const KdaParams& p, const Launch& l, hipStream_t st) {
+  const bool vec = p.raw_g_vec;
+  switch (p.act_dt) {
+    case SSMD_F32: return vec ? launch_kk<D, NORM, SSMD_F32, true>(p, l, st) : launch_kk<D, NORM, SSMD_F32, false>(p, l, st);
+    case SSMD_BF16: return vec ? launch_kk<D, NORM, SSMD_BF16, true>(p, l, st) : launch_kk<D, NORM, SSMD_BF16, false>(p, l, st);
+    default: return vec ? launch_kk<D, NORM, SSMD_F16, true>(p, l, st) : launch_kk<D, NORM, SSMD_F16, false>(p, l, st);
   }
+}
+
+template <int D>
+hipError_t launch_knorm(const KdaParams& p, const Launch& l, hipStream_t st) {
+  return p.gate ? launch_kact<D, true>(p, l, st) : launch_kact<D, false>(p, l, st);
 }
 
 }  // namespace
 
 hipError_t launch_kda(const KdaParams& p, const Launch& l, hipStream_t st) {
   switch (p.D) {
-    case 16: return launch_krg<16>(p, l, st);
-    case 32: return launch_krg<32>(p, l, st);
-    case 64: return launch_krg<64>(p, l, st);
-    case 128: return launch_krg<128>(p, l, st);
-    case 256: return launch_krg<256>(p, l, st);
+    case 16: return launch_knorm<16>(p, l, st);
+    case 32: return launch_knorm<32>(p, l, st);
+    case 64: return launch_knorm<64>(p, l, st);
+    case 128: return launch_knorm<128>(p, l, st);
+    case 256: return launch_knorm<256>(p, l, st);
     default: return hipErrorInvalidValue;
   }
 }

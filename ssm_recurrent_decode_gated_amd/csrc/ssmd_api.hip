@@ -32,27 +32,21 @@ int dtype_bytes(int d) { return d == SSMD_F32 ? 4 : 2; }
 bool head_size_ok(int k) { return k == 16 || k == 32 || k == 64 || k == 128 || k == 256; }
 bool aligned(const void* p, int bytes) { return ((uintptr_t)p % (uintptr_t)bytes) == 0; }
 
-// Launch shape for the state-streaming kernels. Defaults: 4 waves per block;
-// enough row groups per wave that a 128-row head is one pass per wave.
-// SSMD_TUNE="rg,wpb,nt" overrides them (read once), for shape sweeps.
-ssmd::Launch launch_for(int K) {
+// Launch shape of the state-streaming kernels: 4 waves per block, one block
+// per work unit (measured best on MI355X among 1-8 waves per block and capped
+// grid-stride grids). SSMD_TUNE="wpb[,grid_cap]" overrides it (read once),
+// for launch-shape sweeps.
+ssmd::Launch launch_for() {
   static int tuned = -1;
-  static ssmd::Launch override_l{0, 0, 0};
+  static ssmd::Launch override_l{4, 0};
   if (tuned < 0) {
     const char* e = getenv("SSMD_TUNE");
-    int rg = 0, wpb = 0, nt = 0;
-    tuned = (e && sscanf(e, "%d,%d,%d", &rg, &wpb, &nt) == 3 && (rg == 1 || rg == 2 || rg == 4) &&
-             wpb >= 1 && wpb <= 8) ? 1 : 0;
-    if (tuned) override_l = ssmd::Launch{rg, wpb, nt};
+    int wpb = 0, cap = 0;
+    const int n = e ? sscanf(e, "%d,%d", &wpb, &cap) : 0;
+    tuned = (n >= 1 && wpb >= 1 && wpb <= 8 && cap >= 0) ? 1 : 0;
+    if (tuned) override_l = ssmd::Launch{wpb, cap};
   }
-  if (tuned == 1) return override_l;
-  switch (K) {
-    case 16: return ssmd::Launch{1, 4, 0};
-    case 32: return ssmd::Launch{2, 4, 0};
-    case 64: return ssmd::Launch{4, 4, 0};
-    case 128: return ssmd::Launch{4, 4, 0};
-    default: return ssmd::Launch{2, 4, 0};  // 256
-  }
+  return tuned == 1 ? override_l : ssmd::Launch{4, 0};
 }
 
 int launch_status(hipError_t e, const char* what) {
@@ -170,7 +164,7 @@ int gdn_decode_step(const void* mixed_qkv, int64_t qkv_row_stride, const void* a
   ssmd::GdnParams p = gdn_params(mixed_qkv, qkv_row_stride, a, b, A_log, dt_bias, state, num_slots,
                                  ssm_state_indices, out, B, H, HV, K, V, act_dtype, out_dtype, scale,
                                  use_qk_l2norm, l2norm_eps, norm_gate, norm_weight, norm_eps, norm_act);
-  return launch_status(ssmd::launch_gdn(p, launch_for(K), stream), "gdn_decode_step");
+  return launch_status(ssmd::launch_gdn(p, launch_for(), stream), "gdn_decode_step");
 }
 
 int gdn_decode_step_buffered(const void* mixed_qkv, int64_t qkv_row_stride, const void* a,
@@ -187,9 +181,9 @@ int gdn_decode_step_buffered(const void* mixed_qkv, int64_t qkv_row_stride, cons
                      ssm_state_indices, out, B, H, HV, K, V, act_dtype, out_dtype, norm_gate, norm_act);
   if (rc) return rc;
   if (L < 1 || L > 64) return fail(SSMD_ERR_BAD_SHAPE, "%s: L = %d outside [1, 64]", fn, L);
-  const ssmd::Launch l = launch_for(K);
-  const int rpt = norm_gate ? V : l.wpb * l.rg * (64 / (K >= 32 ? 8 : K / 4));
-  const size_t lds = sizeof(float) * ((size_t)(L - 1) * ((size_t)K + (size_t)rpt) + 3 * (size_t)(L - 1) + 1);
+  const ssmd::Launch l = launch_for();
+  const int rpt = ssmd::buffered_rows_per_tile(K, V, norm_gate != nullptr, l);
+  const size_t lds = ssmd::buffered_lds_bytes(K, rpt, L);
   if (lds > 60 * 1024)
     return fail(SSMD_ERR_UNSUPPORTED, "%s: ring staging needs %zu bytes of LDS (> 60 KiB); lower L", fn, lds);
   if (B == 0) return ok();
@@ -258,7 +252,7 @@ int kda_decode_step(const void* x, const float* conv_weight, const float* conv_b
   p.scale = scale;
   p.use_l2 = use_qk_l2norm ? 1 : 0;
   p.l2eps = l2norm_eps;
-  return launch_status(ssmd::launch_kda(p, launch_for(D), stream), fn);
+  return launch_status(ssmd::launch_kda(p, launch_for(), stream), fn);
 }
 
 int ssmd_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {

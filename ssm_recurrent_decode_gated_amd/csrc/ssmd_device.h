@@ -78,6 +78,47 @@ __device__ __forceinline__ void store_act1(void* base, int64_t off, int dt, floa
   }
 }
 
+// Compile-time-typed activation loads: no dtype branch in the kernel body, so
+// the compiler can keep every state load in flight across them.
+template <int ACT>
+__device__ __forceinline__ float ld_act(const void* base, int64_t off) {
+  if constexpr (ACT == SSMD_F32) return static_cast<const float*>(base)[off];
+  else if constexpr (ACT == SSMD_BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[off]);
+  else return f16_bits_to_f32(static_cast<const uint16_t*>(base)[off]);
+}
+
+// 4 consecutive elements; VEC: `base + off` is aligned to 4 elements.
+template <int ACT, bool VEC>
+__device__ __forceinline__ void ld_act4(const void* base, int64_t off, float out[4]) {
+  if constexpr (!VEC) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = ld_act<ACT>(base, off + e);
+  } else if constexpr (ACT == SSMD_F32) {
+    f4 v = *reinterpret_cast<const f4*>(static_cast<const float*>(base) + off);
+    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+  } else {
+    uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + off);
+    if constexpr (ACT == SSMD_BF16) {
+      out[0] = __uint_as_float(v.x << 16);
+      out[1] = __uint_as_float(v.x & 0xffff0000u);
+      out[2] = __uint_as_float(v.y << 16);
+      out[3] = __uint_as_float(v.y & 0xffff0000u);
+    } else {
+      out[0] = f16_bits_to_f32(v.x & 0xffffu);
+      out[1] = f16_bits_to_f32(v.x >> 16);
+      out[2] = f16_bits_to_f32(v.y & 0xffffu);
+      out[3] = f16_bits_to_f32(v.y >> 16);
+    }
+  }
+}
+
+template <int ACT>
+__device__ __forceinline__ void st_act(void* base, int64_t off, float v) {
+  if constexpr (ACT == SSMD_F32) static_cast<float*>(base)[off] = v;
+  else if constexpr (ACT == SSMD_BF16) static_cast<uint16_t*>(base)[off] = f32_to_bf16_bits(v);
+  else static_cast<uint16_t*>(base)[off] = f32_to_f16_bits(v);
+}
+
 // ------------------------------------------------------------- math
 __device__ __forceinline__ float softplus_f(float x) { return x > 20.f ? x : log1pf(expf(x)); }
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }

@@ -64,9 +64,8 @@ struct KdaParams {
 
 // Launch shape of the state-streaming kernels, chosen on the host.
 struct Launch {
-  int rg;   // row groups per wave per pass (rows per wave pass = rg * 64 / LPR)
-  int wpb;  // waves per workgroup
-  int nt;   // non-temporal state loads/stores
+  int wpb;       // waves per workgroup
+  int grid_cap;  // > 0: at most this many blocks, each walking units with a grid stride
 };
 
 // Launchers: return a hipError_t from the launch.
@@ -75,7 +74,9 @@ hipError_t launch_gdn_buffered(const GdnParams& p, const Launch& l, hipStream_t 
 hipError_t launch_kda(const KdaParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
 
-// Compiled head sizes / row-group choices (checked on the host).
-bool gdn_supported(int K, int rg);
+// Rows of one buffered-kernel tile, and the LDS its ring staging needs.
+int buffered_rows_per_tile(int K, int V, bool norm, const Launch& l);
+size_t buffered_lds_bytes(int K, int rows, int L);
+
 
 }  // namespace ssmd
