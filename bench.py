@@ -31,8 +31,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 * 2 ** 20
-KERNEL_SOURCES = ["ssm_recurrent_decode_gated_amd/csrc/gdn_decode.hip",
-                  "ssm_recurrent_decode_gated_amd/csrc/ssmd_device.h"]
+KERNEL_SOURCES = ["ssm_recurrent_decode_gated_amd/csrc/gdn_decode_pf.hip",
+                  "ssm_recurrent_decode_gated_amd/csrc/ssmd_device.h",
+                  "ssm_recurrent_decode_gated_amd/csrc/ssmd_internal.h"]
+KERNEL_NAME = "gdn_decode_pf_kernel"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gdn_b256_of264_hbm_counters.txt")
 METRIC = "state GB/s (% of HBM peak) and µs/step, GDN decode HV=32 K=V=128, B=1/16/256"
 
@@ -305,7 +307,7 @@ def _read_counter_csv(d, counter):
             if r.get("Counter_Name") != counter:
                 continue
             name = r.get("Kernel_Name", "")
-            key = "gdn" if "gdn_decode_kernel" in name else ("copy" if "stream_copy_kernel" in name else None)
+            key = "gdn" if KERNEL_NAME in name else ("copy" if "stream_copy_kernel" in name else None)
             if key:
                 per.setdefault(key, {}).setdefault(r.get("Dispatch_Id"), 0.0)
                 per[key][r.get("Dispatch_Id")] += float(r["Counter_Value"])
@@ -322,7 +324,7 @@ def summarize_counters(fetch_dir, write_dir, out, command):
     ff, wf = copy_bytes / 1024 / f["copy"], copy_bytes / 1024 / w["copy"]
     traffic = f["gdn"] * 1024 * ff + w["gdn"] * 1024 * wf
     lines = [
-        "# rocprofv3 HBM counters, gdn_decode_kernel at B=256 of 264 slots (H=16 HV=32 K=V=128, bf16 act)",
+        f"# rocprofv3 HBM counters, {KERNEL_NAME} at B=256 of 264 slots (H=16 HV=32 K=V=128, bf16 act)",
         f"# command: {command}",
         "# values are KiB per dispatch, averaged over dispatches; the copy kernel moves copy_bytes each way",
         f"kernel_source_sha256 = {kernel_source_hash()}",
@@ -409,7 +411,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(h["alg_gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(h["alg_gbs"] / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic),
-                     "algorithmic_bytes_per_launch": h["alg_bytes"], "kernel": "gdn_decode_kernel"},
+                     "algorithmic_bytes_per_launch": h["alg_bytes"], "kernel": KERNEL_NAME},
         "cpu_baseline": cpu,
         "extra": extra,
     }

@@ -1,0 +1,188 @@
+// gdn_decode_pf.hip -- packed GDN decode (no output norm): persistent blocks
+// that prefetch the next work unit's state while the current one is computed
+// and stored. Same arithmetic and row layout as gdn_decode.hip.
+//
+// Launch shape (measured on MI355X, B = 256, HV = 32, K = V = 128): one
+// 4-wave block per CU, each wave holding the state pass of two work units
+// (this one and the next), streams at 5.68 TB/s, against 5.45 TB/s for one
+// block per unit with every pass in flight at once and 5.63 TB/s for the best
+// plain copy kernel. Fewer concurrent streams with continuous prefetch keep
+// the HBM busier than many short-lived blocks; the grid must match the CU
+// count exactly (a few blocks more or fewer leaves CUs with twice the work).
+#include "ssmd_device.h"
+#include "ssmd_internal.h"
+
+namespace ssmd {
+
+// Rows per wave per unit: 32 for K = 64/128 (16 KB of state), fewer where a
+// second unit would not fit the register file.
+template <int K>
+constexpr int pf_rg() {
+  return K == 16 ? 1 : (K == 32 ? 2 : (K == 256 ? 1 : 4));
+}
+
+template <int K, int ACT, bool VEC>
+__global__ __launch_bounds__(512) void gdn_decode_pf_kernel(GdnParams p, int tiles_per_head,
+                                                            int rows_per_tile, int n_units) {
+  using RL = RowLayout<K>;
+  constexpr int RG = pf_rg<K>();
+  constexpr int LPR = RL::LPR, NV = RL::NV, RPI = RL::RPI;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const int c = lane % LPR;
+  const int rr = lane / LPR;
+
+  struct Unit {
+    int slot, bi, hv, h, r0, r1;
+    float qf[NV * 4], kf[NV * 4], vv[RG], av, bv, A_log, dt_bias;
+    f4 s[RG][NV];
+  };
+  auto fetch = [&](int unit, Unit& U) {
+    int bid = unit;
+    const int tile = bid % tiles_per_head;
+    bid /= tiles_per_head;
+    U.hv = bid % p.HV;
+    U.bi = bid / p.HV;
+    U.slot = p.idx[U.bi];
+    if (U.slot < 0 || U.slot >= p.num_slots) return;
+    U.h = U.hv / (p.HV / p.H);
+    U.r0 = tile * rows_per_tile;
+    U.r1 = min(p.V, U.r0 + rows_per_tile);
+    const int64_t qrow = (int64_t)U.bi * p.qkv_stride;
+    const int64_t vbase = qrow + 2 * (int64_t)p.H * K + (int64_t)U.hv * p.V;
+    const int64_t gidx = (int64_t)U.bi * p.HV + U.hv;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      ld_act4<ACT, VEC>(p.qkv, qrow + (int64_t)U.h * K + RL::col(c, j), &U.qf[4 * j]);
+      ld_act4<ACT, VEC>(p.qkv, qrow + (int64_t)(p.H + U.h) * K + RL::col(c, j), &U.kf[4 * j]);
+    }
+    U.av = ld_act<ACT>(p.a, gidx);
+    U.bv = ld_act<ACT>(p.b, gidx);
+    U.A_log = p.A_log[U.hv];
+    U.dt_bias = p.dt_bias[U.hv];
+    const float* S = p.state + ((int64_t)U.slot * p.HV + U.hv) * (int64_t)p.V * K;
+#pragma unroll
+    for (int i = 0; i < RG; ++i) {
+      const int row = min(U.r0 + (i * nwaves + wave) * RPI + rr, U.r1 - 1);
+      U.vv[i] = ld_act<ACT>(p.qkv, vbase + row);
+#pragma unroll
+      for (int j = 0; j < NV; ++j) U.s[i][j] = ld4<true>(S + (int64_t)row * K + RL::col(c, j));
+    }
+  };
+  auto compute = [&](Unit& U) {
+    if (U.slot < 0 || U.slot >= p.num_slots) return;
+    float qs = p.scale, ks = 1.f;
+    if (p.use_l2) {
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int e = 0; e < NV * 4; ++e) {
+        sq += U.qf[e] * U.qf[e];
+        sk += U.kf[e] * U.kf[e];
+      }
+      sq = group_sum<LPR>(sq);
+      sk = group_sum<LPR>(sk);
+      qs *= rsqrtf(sq + p.l2eps);
+      ks = rsqrtf(sk + p.l2eps);
+    }
+    float kq = 0.f;
+#pragma unroll
+    for (int e = 0; e < NV * 4; ++e) {
+      U.qf[e] *= qs;
+      U.kf[e] *= ks;
+      kq += U.kf[e] * U.qf[e];
+    }
+    kq = group_sum<LPR>(kq);
+    const float g = -expf(U.A_log) * softplus_f(U.av + U.dt_bias);
+    const float beta = sigmoid_f(U.bv);
+    const float decay = expf(g);
+    float* S = p.state + ((int64_t)U.slot * p.HV + U.hv) * (int64_t)p.V * K;
+    const int64_t obase = ((int64_t)U.bi * p.HV + U.hv) * p.V;
+#pragma unroll
+    for (int i = 0; i < RG; ++i) {
+      float dk = 0.f, dq = 0.f;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        dk += U.s[i][j].x * U.kf[4 * j] + U.s[i][j].y * U.kf[4 * j + 1] + U.s[i][j].z * U.kf[4 * j + 2] +
+              U.s[i][j].w * U.kf[4 * j + 3];
+        dq += U.s[i][j].x * U.qf[4 * j] + U.s[i][j].y * U.qf[4 * j + 1] + U.s[i][j].z * U.qf[4 * j + 2] +
+              U.s[i][j].w * U.qf[4 * j + 3];
+      }
+      dk = group_sum<LPR>(dk);
+      dq = group_sum<LPR>(dq);
+      const float delta = beta * (U.vv[i] - decay * dk);
+      const float o = decay * dq + delta * kq;
+      const int row = U.r0 + (i * nwaves + wave) * RPI + rr;
+      if (row < U.r1) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          f4 n;
+          n.x = decay * U.s[i][j].x + delta * U.kf[4 * j];
+          n.y = decay * U.s[i][j].y + delta * U.kf[4 * j + 1];
+          n.z = decay * U.s[i][j].z + delta * U.kf[4 * j + 2];
+          n.w = decay * U.s[i][j].w + delta * U.kf[4 * j + 3];
+          st4<true>(S + (int64_t)row * K + RL::col(c, j), n);
+        }
+        if (c == 0) store_act1(p.out, obase + row, p.out_dt, o);
+      }
+    }
+  };
+
+  Unit A, B;
+  int u = blockIdx.x;
+  const int g = gridDim.x;
+  if (u < n_units) fetch(u, A);
+  while (u < n_units) {
+    if (u + g < n_units) fetch(u + g, B);
+    compute(A);
+    if (u + g >= n_units) break;
+    if (u + 2 * g < n_units) fetch(u + 2 * g, A);
+    compute(B);
+    u += 2 * g;
+  }
+}
+
+namespace {
+
+template <int K, int ACT, bool VEC>
+hipError_t launch_pf_k(const GdnParams& p, const Launch& l, int n_cu, hipStream_t st) {
+  const int wave_rows = pf_rg<K>() * RowLayout<K>::RPI;
+  int wpb = l.wpb;
+  const int rows_per_tile = wpb * wave_rows;
+  const int tiles = (p.V + rows_per_tile - 1) / rows_per_tile;
+  // never launch more waves than a tile has rows for
+  const int need = (min(p.V, rows_per_tile) + wave_rows - 1) / wave_rows;
+  if (wpb > need) wpb = need;
+  const int64_t units = (int64_t)p.B * p.HV * tiles;
+  const int64_t cap = l.grid_cap > 0 ? l.grid_cap : n_cu;
+  const int64_t blocks = units < cap ? units : cap;
+  gdn_decode_pf_kernel<K, ACT, VEC><<<dim3((unsigned)blocks), dim3(64 * wpb), 0, st>>>(p, tiles, rows_per_tile,
+                                                                                    (int)units);
+  return hipGetLastError();
+}
+
+template <int K>
+hipError_t launch_pf_act(const GdnParams& p, const Launch& l, int n_cu, hipStream_t st) {
+  const bool vec = p.qkv_vec;
+  switch (p.act_dt) {
+    case SSMD_F32: return vec ? launch_pf_k<K, SSMD_F32, true>(p, l, n_cu, st) : launch_pf_k<K, SSMD_F32, false>(p, l, n_cu, st);
+    case SSMD_BF16: return vec ? launch_pf_k<K, SSMD_BF16, true>(p, l, n_cu, st) : launch_pf_k<K, SSMD_BF16, false>(p, l, n_cu, st);
+    default: return vec ? launch_pf_k<K, SSMD_F16, true>(p, l, n_cu, st) : launch_pf_k<K, SSMD_F16, false>(p, l, n_cu, st);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gdn_pf(const GdnParams& p, const Launch& l, int n_cu, hipStream_t st) {
+  if (p.norm_gate) return hipErrorInvalidValue;
+  switch (p.K) {
+    case 16: return launch_pf_act<16>(p, l, n_cu, st);
+    case 32: return launch_pf_act<32>(p, l, n_cu, st);
+    case 64: return launch_pf_act<64>(p, l, n_cu, st);
+    case 128: return launch_pf_act<128>(p, l, n_cu, st);
+    case 256: return launch_pf_act<256>(p, l, n_cu, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace ssmd

@@ -32,10 +32,10 @@ int dtype_bytes(int d) { return d == SSMD_F32 ? 4 : 2; }
 bool head_size_ok(int k) { return k == 16 || k == 32 || k == 64 || k == 128 || k == 256; }
 bool aligned(const void* p, int bytes) { return ((uintptr_t)p % (uintptr_t)bytes) == 0; }
 
-// Launch shape of the state-streaming kernels: 4 waves per block, one block
-// per work unit (measured best on MI355X among 1-8 waves per block and capped
-// grid-stride grids). SSMD_TUNE="wpb[,grid_cap]" overrides it (read once),
-// for launch-shape sweeps.
+// Launch shape of the state-streaming kernels: 4 waves per block. The packed
+// step without a norm runs persistent prefetching blocks, one per CU; the
+// other kernels run one block per work unit. SSMD_TUNE="wpb[,grid_cap]"
+// overrides it (read once) for launch-shape sweeps.
 ssmd::Launch launch_for() {
   static int tuned = -1;
   static ssmd::Launch override_l{4, 0};
@@ -47,6 +47,25 @@ ssmd::Launch launch_for() {
     if (tuned) override_l = ssmd::Launch{wpb, cap};
   }
   return tuned == 1 ? override_l : ssmd::Launch{4, 0};
+}
+
+// Compute units of the current device, cached per device (a host-side query;
+// nothing is enqueued, so it is safe under stream capture).
+int cu_count(int* n) {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(SSMD_ERR_LAUNCH, "hipGetDevice failed");
+  if (dev < 64 && cache[dev] > 0) {
+    *n = cache[dev];
+    return SSMD_OK;
+  }
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
+    return fail(SSMD_ERR_LAUNCH, "cannot read the compute-unit count of device %d", dev);
+  if (dev < 64) cache[dev] = v;
+  *n = v;
+  return SSMD_OK;
 }
 
 int launch_status(hipError_t e, const char* what) {
@@ -164,7 +183,13 @@ int gdn_decode_step(const void* mixed_qkv, int64_t qkv_row_stride, const void* a
   ssmd::GdnParams p = gdn_params(mixed_qkv, qkv_row_stride, a, b, A_log, dt_bias, state, num_slots,
                                  ssm_state_indices, out, B, H, HV, K, V, act_dtype, out_dtype, scale,
                                  use_qk_l2norm, l2norm_eps, norm_gate, norm_weight, norm_eps, norm_act);
-  return launch_status(ssmd::launch_gdn(p, launch_for(), stream), "gdn_decode_step");
+  const ssmd::Launch l = launch_for();
+  if (!norm_gate) {
+    int n_cu = 0;
+    if (int rc2 = cu_count(&n_cu)) return rc2;
+    return launch_status(ssmd::launch_gdn_pf(p, l, n_cu, stream), "gdn_decode_step");
+  }
+  return launch_status(ssmd::launch_gdn(p, l, stream), "gdn_decode_step");
 }
 
 int gdn_decode_step_buffered(const void* mixed_qkv, int64_t qkv_row_stride, const void* a,

@@ -70,6 +70,9 @@ struct Launch {
 
 // Launchers: return a hipError_t from the launch.
 hipError_t launch_gdn(const GdnParams& p, const Launch& l, hipStream_t s);
+// Persistent prefetching form of the packed step (no output norm); the grid
+// is n_cu blocks unless Launch.grid_cap says otherwise.
+hipError_t launch_gdn_pf(const GdnParams& p, const Launch& l, int n_cu, hipStream_t s);
 hipError_t launch_gdn_buffered(const GdnParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_kda(const KdaParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
