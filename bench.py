@@ -235,6 +235,35 @@ def kda(dev, reps=30):
             "pct_hbm_peak": round(100 * sb / us / 1e3 / HBM_PEAK_GBS, 2), "pools": M}
 
 
+def mamba(dev, reps=30):
+    """Mamba-1 decode (graph replay of one call per pool): the MBU write-up's
+    table shapes, plus a bandwidth-sized batch. Byte counts: the write-up's
+    model B*D*(20N+24), and the state traffic B*D*N*8."""
+    import torch
+    import ssm_recurrent_decode_gated_amd as S
+    import workloads as W
+    res = {}
+    for (B, Dm, N) in ((1, 1536, 16), (8, 1536, 16), (1, 1536, 64), (256, 4096, 16)):
+        w = W.MambaWorkload(f"mamba_b{B}_d{Dm}_n{N}", B=B, Dm=Dm, N=N, num_slots=B)
+        d = W.mamba_inputs(w)
+        pool_bytes = B * Dm * N * 4
+        M = _pools_for(pool_bytes)
+        dd = {k: v.to(dev) for k, v in d.items()}
+        pools = [dd["h"]] + [dd["h"].clone() for _ in range(M - 1)]
+        out = torch.empty(B, Dm, device=dev)
+
+        def call(i):
+            S.mamba_decode_step(dd["x"], dd["dt"], dd["A"], dd["Bm"], dd["Cm"], dd["Dv"], dd["z"], pools[i],
+                                dd["idx"], out)
+        us = graph_time_us([lambda i=i: call(i) for i in range(M)], reps, torch.cuda.current_stream())
+        res[f"B{B}_D{Dm}_N{N}"] = {"us_per_step": round(us, 3),
+                                   "page_model_GBps": round(B * Dm * (20 * N + 24) / us / 1e3, 1),
+                                   "state_GBps": round(B * Dm * N * 8 / us / 1e3, 1), "pools": M}
+        del pools, dd
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(su, target_s=10.0):
     """The fp64 oracle, as it stands, on the host cores: the full B=256 step
     repeated (state evolving) until about target_s seconds have passed."""
@@ -387,6 +416,7 @@ def main():
         extra["graph_sweep"] = sweep(dev)
         extra["buffered_b64"] = buffered(dev)
         extra["kda_t64_h96"] = kda(dev)
+        extra["mamba1"] = mamba(dev)
         extra["pct_of_copy_ceiling"] = round(100 * h["state_gbs"] / extra["copy_ceiling"]["GBps"], 2)
     w = h["w"]
     traffic = counters_traffic()

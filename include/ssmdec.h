@@ -192,6 +192,31 @@ int kda_decode_step(const void* x,
                     float scale, int32_t use_qk_l2norm, float l2norm_eps,
                     hipStream_t stream);
 
+/*
+ * mamba_decode_step -- one Mamba-1 selective-scan decode step (the diagonal
+ * relative of the delta rule), "Triton decode kernel + MBU analysis",
+ * "Kernel design". For every row b whose slot s = state_indices[b] is in
+ * [0, num_slots), and every channel d < Dm, with h = state[s, d, :] (N wide):
+ *   dA = exp(dt[b,d] * A[d,:]);  dB = dt[b,d] * Bm[b,:]
+ *   h <- dA * h + dB * x[b,d]                    (state updated in place)
+ *   y  = sum_n Cm[b,n] h[n] + Dvec[d] x[b,d]     (Dvec NULL: no skip term)
+ *   y *= silu(z[b,d])                            (z NULL: no gate)
+ *   out[b,d] = y (out_dtype, RNE)
+ * dt is taken as given (already positive). The page's kernel allocates a
+ * fresh state each call; here the state is a slot pool updated in place, as
+ * in the other calls.
+ *   x, dt, z [B, Dm] act_dtype;  Bm, Cm [B, N] act_dtype;  A [Dm, N] fp32
+ *   (16-byte aligned);  Dvec [Dm] fp32;  state [num_slots, Dm, N] fp32;
+ *   out [B, Dm] out_dtype;  N in {16, 32, 64, 128, 256}; B >= 0.
+ */
+int mamba_decode_step(const void* x, const void* dt, const float* A,
+                      const void* Bm, const void* Cm, const float* Dvec,
+                      const void* z, float* state, int32_t num_slots,
+                      const int32_t* state_indices, void* out,
+                      int32_t B, int32_t Dm, int32_t N,
+                      int32_t act_dtype, int32_t out_dtype,
+                      hipStream_t stream);
+
 /* Message for the last non-zero status returned on this thread ("" if none). */
 const char* ssmd_last_error(void);
 

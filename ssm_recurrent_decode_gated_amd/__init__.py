@@ -16,9 +16,10 @@ from ._binding import (  # noqa: F401
     gdn_decode_step_buffered,
     kda_decode_step,
     load_library,
+    mamba_decode_step,
     ssmd_last_error,
     ssmd_stream_copy,
 )
 
-__all__ = ["gdn_decode_step", "gdn_decode_step_buffered", "kda_decode_step", "ssmd_last_error",
-           "ssmd_stream_copy", "SsmdError", "load_library"]
+__all__ = ["gdn_decode_step", "gdn_decode_step_buffered", "kda_decode_step", "mamba_decode_step",
+           "ssmd_last_error", "ssmd_stream_copy", "SsmdError", "load_library"]

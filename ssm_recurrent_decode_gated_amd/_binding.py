@@ -20,8 +20,8 @@ SSMD_F32, SSMD_BF16, SSMD_F16 = 0, 1, 2
 SSMD_ACT_SILU, SSMD_ACT_SIGMOID = 0, 1
 DTYPE_CODE = {torch.float32: SSMD_F32, torch.bfloat16: SSMD_BF16, torch.float16: SSMD_F16}
 ACT_CODE = {"silu": SSMD_ACT_SILU, "sigmoid": SSMD_ACT_SIGMOID}
-EXPORTS = ("gdn_decode_step", "gdn_decode_step_buffered", "kda_decode_step", "ssmd_last_error",
-           "ssmd_stream_copy")
+EXPORTS = ("gdn_decode_step", "gdn_decode_step_buffered", "kda_decode_step", "mamba_decode_step",
+           "ssmd_last_error", "ssmd_stream_copy")
 
 
 class SsmdError(RuntimeError):
@@ -51,8 +51,11 @@ def load_library() -> ctypes.CDLL:
         L.kda_decode_step.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _f, _p, _i32,
                                       _p, _p, _p, _p, _f, _i32, _i32, _i32, _i32, _i32, _i32, _f,
                                       _i32, _f, _p]
+        L.mamba_decode_step.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _p, _i32, _i32, _i32,
+                                        _i32, _i32, _p]
         L.ssmd_stream_copy.argtypes = [_p, _p, _i64, _p]
-        for f in ("gdn_decode_step", "gdn_decode_step_buffered", "kda_decode_step", "ssmd_stream_copy"):
+        for f in ("gdn_decode_step", "gdn_decode_step_buffered", "kda_decode_step", "mamba_decode_step",
+                  "ssmd_stream_copy"):
             getattr(L, f).restype = ctypes.c_int
         L.ssmd_last_error.argtypes = []
         L.ssmd_last_error.restype = ctypes.c_char_p
@@ -226,6 +229,34 @@ def kda_decode_step(x, conv_weight, conv_bias, conv_state, raw_g, raw_beta, A_lo
         _ptr(output_gate), _ptr(norm_weight), norm_eps, T, H, D, W, DTYPE_CODE[act],
         DTYPE_CODE[out.dtype], scale, int(bool(use_qk_l2norm)), l2norm_eps, _stream(state, stream))
     _check(rc, "kda_decode_step")
+    return out
+
+
+def mamba_decode_step(x, dt, A, Bm, Cm, Dvec, z, state, state_indices, out, *, stream=None):
+    """One Mamba-1 selective-scan decode step (state and out updated in
+    place); see mamba_decode_step in include/ssmdec.h."""
+    _dev(state, "state", torch.float32)
+    if state.dim() != 3:
+        raise ValueError("state must be [num_slots, D, N]")
+    num_slots, Dm, N = state.shape
+    _dev(x, "x", _ACTS)
+    B = x.shape[0]
+    act = x.dtype
+    _dev(x, "x", act, (B, Dm))
+    _dev(dt, "dt", act, (B, Dm))
+    _dev(A, "A", torch.float32, (Dm, N))
+    _dev(Bm, "Bm", act, (B, N))
+    _dev(Cm, "Cm", act, (B, N))
+    if Dvec is not None:
+        _dev(Dvec, "Dvec", torch.float32, (Dm,))
+    if z is not None:
+        _dev(z, "z", act, (B, Dm))
+    _dev(state_indices, "state_indices", torch.int32, (B,))
+    _dev(out, "out", _ACTS, (B, Dm))
+    rc = load_library().mamba_decode_step(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dvec), _ptr(z), _ptr(state), num_slots,
+        _ptr(state_indices), _ptr(out), B, Dm, N, DTYPE_CODE[act], DTYPE_CODE[out.dtype], _stream(state, stream))
+    _check(rc, "mamba_decode_step")
     return out
 
 

@@ -280,6 +280,43 @@ int kda_decode_step(const void* x, const float* conv_weight, const float* conv_b
   return launch_status(ssmd::launch_kda(p, launch_for(), stream), fn);
 }
 
+int mamba_decode_step(const void* x, const void* dt, const float* A, const void* Bm, const void* Cm,
+                      const float* Dvec, const void* z, float* state, int32_t num_slots,
+                      const int32_t* state_indices, void* out, int32_t B, int32_t Dm, int32_t N,
+                      int32_t act_dtype, int32_t out_dtype, hipStream_t stream) {
+  const char* fn = "mamba_decode_step";
+  if (B < 0) return fail(SSMD_ERR_BAD_SHAPE, "%s: B = %d < 0", fn, B);
+  if (Dm < 1) return fail(SSMD_ERR_BAD_SHAPE, "%s: D = %d < 1", fn, Dm);
+  if (!head_size_ok(N)) return fail(SSMD_ERR_UNSUPPORTED, "%s: N = %d not in {16,32,64,128,256}", fn, N);
+  if (num_slots < 1) return fail(SSMD_ERR_BAD_SHAPE, "%s: num_slots = %d < 1", fn, num_slots);
+  if (!valid_dtype(act_dtype) || !valid_dtype(out_dtype))
+    return fail(SSMD_ERR_BAD_DTYPE, "%s: bad act/out dtype (%d, %d)", fn, act_dtype, out_dtype);
+  if ((int64_t)B * ((Dm + 63) / 64) >= (1LL << 31)) return fail(SSMD_ERR_BAD_SHAPE, "%s: B*D too large", fn);
+  if (B == 0) return ok();
+  if (!x || !dt || !A || !Bm || !Cm || !state || !state_indices || !out)
+    return fail(SSMD_ERR_NULL_ARG, "%s: a required pointer is NULL", fn);
+  if (!aligned(A, 16) || !aligned(state, 16))
+    return fail(SSMD_ERR_BAD_SHAPE, "%s: A and state must be 16-byte aligned", fn);
+  ssmd::MambaParams p{};
+  p.x = x;
+  p.dt = dt;
+  p.A = A;
+  p.Bm = Bm;
+  p.Cm = Cm;
+  p.Dvec = Dvec;
+  p.z = z;
+  p.state = state;
+  p.num_slots = num_slots;
+  p.idx = state_indices;
+  p.out = out;
+  p.B = B;
+  p.Dm = Dm;
+  p.N = N;
+  p.act_dt = act_dtype;
+  p.out_dt = out_dtype;
+  return launch_status(ssmd::launch_mamba(p, launch_for(), stream), fn);
+}
+
 int ssmd_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
   if (!src || !dst) return fail(SSMD_ERR_NULL_ARG, "ssmd_stream_copy: NULL pointer");
   if (bytes < 0 || bytes % 16) return fail(SSMD_ERR_BAD_SHAPE, "ssmd_stream_copy: bytes must be a multiple of 16");

@@ -62,6 +62,22 @@ struct KdaParams {
   float l2eps;
 };
 
+struct MambaParams {
+  const void* x;
+  const void* dt;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dvec;
+  const void* z;
+  float* state;
+  int32_t num_slots;
+  const int32_t* idx;
+  void* out;
+  int32_t B, Dm, N;
+  int32_t act_dt, out_dt;
+};
+
 // Launch shape of the state-streaming kernels, chosen on the host.
 struct Launch {
   int wpb;       // waves per workgroup
@@ -75,6 +91,7 @@ hipError_t launch_gdn(const GdnParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_gdn_pf(const GdnParams& p, const Launch& l, int n_cu, hipStream_t s);
 hipError_t launch_gdn_buffered(const GdnParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_kda(const KdaParams& p, const Launch& l, hipStream_t s);
+hipError_t launch_mamba(const MambaParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
 
 // Rows of one buffered-kernel tile, and the LDS its ring staging needs.

@@ -136,3 +136,20 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(Bd, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="not built"):
         Bd.load_library()
+
+
+def test_mamba_host_validation():
+    L = S.load_library()
+
+    def call(B=8, Dm=1536, N=16, x=0x10000, A=0x20000, state=0x30000, act=0, slots=8):
+        return L.mamba_decode_step(x, 0x11000, A, 0x12000, 0x13000, None, None, state, slots, 0x14000, 0x15000,
+                                   B, Dm, N, act, 0, None)
+    assert call(N=12) == UNSUPPORTED
+    assert call(Dm=0) == BAD_SHAPE
+    assert call(B=-1) == BAD_SHAPE
+    assert call(slots=0) == BAD_SHAPE
+    assert call(act=9) == BAD_DTYPE
+    assert call(x=None) == NULL_ARG
+    assert call(A=0x20004) == BAD_SHAPE
+    assert call(state=0x30008) == BAD_SHAPE
+    assert call(B=0, x=None) == OK
