@@ -142,6 +142,37 @@ def headline(dev, steps, warmup):
             "alg_bytes": ab, "state_bytes": sb, "setup": su}
 
 
+def state16(dev, steps=200, warmup=10):
+    """The B=256-of-264 step on a bf16 state pool (gdn_decode_step_state16):
+    half the state bytes of the fp32 step."""
+    import torch
+    import ssm_recurrent_decode_gated_amd as S
+    import workloads as W
+    w = W.GDN_B256
+    pool_bytes = w.num_slots * w.HV * w.V * w.K * 2
+    M = _pools_for(pool_bytes)
+    su = GDNSetup(w, 1, dev)
+    first = su.pools[0].to(torch.bfloat16)
+    su.pools = None
+    torch.cuda.empty_cache()
+    pools = [first] + [first.clone() for _ in range(M - 1)]
+
+    def call(i):
+        S.gdn_decode_step_state16(su.qkv, su.a, su.b, su.A_log, su.dt_bias, pools[i % M], su.idx_d, su.out)
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    it = iter(range(10 ** 9))
+    ms = _events_ms(lambda: call(next(it)), steps, torch.cuda.current_stream())
+    us = ms * 1e3 / steps
+    sb = w.B * w.HV * w.V * w.K * 2 * 2
+    del pools, su
+    torch.cuda.empty_cache()
+    return {"workload": w.name + "_bf16_state", "us_per_step": round(us, 3), "state_GBps": round(sb / us / 1e3, 1),
+            "pct_hbm_peak": round(100 * sb / us / 1e3 / HBM_PEAK_GBS, 2), "pools": M,
+            "speedup_vs_fp32_state": None}
+
+
 def sweep(dev, batches=(1, 16, 64, 256), reps=50):
     import workloads as W
     import torch
@@ -417,6 +448,8 @@ def main():
         extra["buffered_b64"] = buffered(dev)
         extra["kda_t64_h96"] = kda(dev)
         extra["mamba1"] = mamba(dev)
+        extra["state16_b256"] = state16(dev)
+        extra["state16_b256"]["speedup_vs_fp32_state"] = round(h["us"] / extra["state16_b256"]["us_per_step"], 3)
         extra["pct_of_copy_ceiling"] = round(100 * h["state_gbs"] / extra["copy_ceiling"]["GBps"], 2)
     w = h["w"]
     traffic = counters_traffic()

@@ -104,6 +104,32 @@ int gdn_decode_step(const void* mixed_qkv, int64_t qkv_row_stride,
                     hipStream_t stream);
 
 /*
+ * gdn_decode_step_state16 -- gdn_decode_step on a state pool stored in 16-bit
+ * floats. "Optimization Log: Qwen3.5-27B Dense on B200" ("Kernel 4: Fused
+ * DeltaNet Recurrent") sizes the per-head state as a 16-bit [128, 128] tile;
+ * storing it so halves the dominant traffic of the step.
+ *
+ * Computes exactly what gdn_decode_step computes, in fp32, from the state
+ * read as 16-bit values; the updated rows are rounded (RNE) to state_dtype
+ * once, when they are stored, and this step's output is formed from the
+ * unrounded update. state is [num_slots, HV, V, K] of state_dtype
+ * (SSMD_BF16 or SSMD_F16), 16-byte aligned. All other arguments, layouts and
+ * conventions are those of gdn_decode_step.
+ */
+int gdn_decode_step_state16(const void* mixed_qkv, int64_t qkv_row_stride,
+                            const void* a, const void* b,
+                            const float* A_log, const float* dt_bias,
+                            void* state, int32_t state_dtype, int32_t num_slots,
+                            const int32_t* ssm_state_indices,
+                            void* out,
+                            int32_t B, int32_t H, int32_t HV, int32_t K, int32_t V,
+                            int32_t act_dtype, int32_t out_dtype,
+                            float scale, int32_t use_qk_l2norm, float l2norm_eps,
+                            const void* norm_gate, const float* norm_weight,
+                            float norm_eps, int32_t norm_act,
+                            hipStream_t stream);
+
+/*
  * gdn_decode_step_buffered -- the GDN step with the state written back only
  * once every L steps ([REPLAY] module docstring, `_bench_cfg`,
  * `_state_bytes_per_step`, `_amortize`).

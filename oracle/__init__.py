@@ -39,7 +39,7 @@ def configure(L: ctypes.CDLL) -> ctypes.CDLL:
     L.orc_gdn_gates.argtypes = [_d, _d, _d, _d, _dp, _dp]
     L.orc_gdn_gates.restype = None
     gdn = [_i] * 6 + [_dp, _l, _dp, _dp, _dp, _dp, _dp, _ip, _dp, _d, _i, _d, _dp, _dp, _d, _i]
-    L.orc_gdn_step.argtypes = gdn
+    L.orc_gdn_step.argtypes = gdn + [_i]
     L.orc_gdn_step_buffered.argtypes = gdn + [_dp, _dp, _dp, _ip, _i, _i]
     L.orc_conv1d_update.argtypes = [_i] * 4 + [_dp, _dp, _dp, _dp, _ip, _i, _dp, _i]
     L.orc_kda_step.argtypes = [_i] * 4 + [_dp, _dp, _dp, _dp, _dp, _d, _dp, _ip, _dp,
@@ -135,9 +135,10 @@ def num_threads() -> int:
 # ----------------------------------------------------------------- GDN
 def gdn_step(qkv, a, b, A_log, dt_bias, state, idx, *, H, HV, K, V, scale=None,
              use_l2=True, l2eps=1e-6, norm_gate=None, norm_weight=None,
-             norm_eps=1e-5, norm_act=ACT_SILU):
+             norm_eps=1e-5, norm_act=ACT_SILU, state_fmt=FMT_NONE):
     """One packed GDN step. `state` is a float64 [num_slots, HV, V, K] array
-    updated in place. Returns out float64 [B, HV, V] (NaN for padded rows)."""
+    updated in place (rounded to state_fmt when stored). Returns out float64
+    [B, HV, V] (NaN for padded rows)."""
     qkv, a, b = f64(qkv), f64(a), f64(b)
     A_log, dt_bias, idx = f64(A_log), f64(dt_bias), i32(idx)
     assert state.dtype == np.float64 and state.flags["C_CONTIGUOUS"]
@@ -150,7 +151,7 @@ def gdn_step(qkv, a, b, A_log, dt_bias, state, idx, *, H, HV, K, V, scale=None,
     scale = K ** -0.5 if scale is None else scale
     _chk(lib().orc_gdn_step(B, H, HV, K, V, num_slots, _p(qkv), qkv.shape[1], _p(a), _p(b),
                             _p(A_log), _p(dt_bias), _p(state), _p(idx), _p(out), scale,
-                            int(use_l2), l2eps, _p(ng), _p(nw), norm_eps, norm_act))
+                            int(use_l2), l2eps, _p(ng), _p(nw), norm_eps, norm_act, int(state_fmt)))
     return out
 
 

@@ -202,13 +202,17 @@ static void gated_rmsnorm(double *o, int V, const double *gate,
  * indexed by ssm_state_indices; out [B, 1, HV, V]).
  * Value head hv reads q/k head hv / (HV/H) (contiguous GQA groups).
  * Row b is padded, and touches nothing, when idx[b] < 0 or >= num_slots.
- * state is fp64 and updated in place; out receives unrounded fp64. */
+ * state is fp64 and updated in place; out receives unrounded fp64.
+ * state_fmt: the format the pool stores the state in (ORC_FMT_NONE keeps fp64;
+ * ORC_FMT_BF16 / F16 model the 16-bit per-head state of [LOG] "Kernel 4": the
+ * updated state is rounded once when stored, after this step's output has
+ * been formed from the unrounded update). */
 int orc_gdn_step(int B, int H, int HV, int K, int V, int num_slots,
                  const double *qkv, long qkv_stride, const double *a,
                  const double *b, const double *A_log, const double *dt_bias,
                  double *state, const int32_t *idx, double *out, double scale,
                  int use_l2, double l2eps, const double *norm_gate,
-                 const double *norm_w, double norm_eps, int norm_act)
+                 const double *norm_w, double norm_eps, int norm_act, int state_fmt)
 {
     if (B < 0 || H < 1 || HV < 1 || HV % H || K < 1 || V < 1 || num_slots < 1)
         return ORC_BAD;
@@ -233,6 +237,9 @@ int orc_gdn_step(int B, int H, int HV, int K, int V, int num_slots,
             double *S = state + ((size_t)s * HV + hv) * (size_t)V * K;
             const double *v = row + 2 * (size_t)H * K + (size_t)hv * V;
             delta_rule_head(S, V, K, decay, k, q, v, beta, o, delta, u);
+            if (state_fmt != ORC_FMT_NONE)
+                for (size_t e = 0; e < (size_t)V * K; ++e)
+                    S[e] = orc_round_fmt(S[e], state_fmt);
             if (norm_gate)
                 gated_rmsnorm(o, V, norm_gate + ((size_t)bi * HV + hv) * V,
                               norm_w, norm_eps, norm_act);

@@ -20,8 +20,8 @@ SSMD_F32, SSMD_BF16, SSMD_F16 = 0, 1, 2
 SSMD_ACT_SILU, SSMD_ACT_SIGMOID = 0, 1
 DTYPE_CODE = {torch.float32: SSMD_F32, torch.bfloat16: SSMD_BF16, torch.float16: SSMD_F16}
 ACT_CODE = {"silu": SSMD_ACT_SILU, "sigmoid": SSMD_ACT_SIGMOID}
-EXPORTS = ("gdn_decode_step", "gdn_decode_step_buffered", "kda_decode_step", "mamba_decode_step",
-           "ssmd_last_error", "ssmd_stream_copy")
+EXPORTS = ("gdn_decode_step", "gdn_decode_step_state16", "gdn_decode_step_buffered", "kda_decode_step",
+           "mamba_decode_step", "ssmd_last_error", "ssmd_stream_copy")
 
 
 class SsmdError(RuntimeError):
@@ -48,14 +48,15 @@ def load_library() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.gdn_decode_step.argtypes = _GDN_ARGS + [_p]
         L.gdn_decode_step_buffered.argtypes = _GDN_ARGS + [_p, _p, _p, _p, _i32, _p]
+        L.gdn_decode_step_state16.argtypes = _GDN_ARGS[:7] + [_i32] + _GDN_ARGS[7:] + [_p]
         L.kda_decode_step.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _f, _p, _i32,
                                       _p, _p, _p, _p, _f, _i32, _i32, _i32, _i32, _i32, _i32, _f,
                                       _i32, _f, _p]
         L.mamba_decode_step.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _p, _i32, _i32, _i32,
                                         _i32, _i32, _p]
         L.ssmd_stream_copy.argtypes = [_p, _p, _i64, _p]
-        for f in ("gdn_decode_step", "gdn_decode_step_buffered", "kda_decode_step", "mamba_decode_step",
-                  "ssmd_stream_copy"):
+        for f in ("gdn_decode_step", "gdn_decode_step_state16", "gdn_decode_step_buffered", "kda_decode_step",
+                  "mamba_decode_step", "ssmd_stream_copy"):
             getattr(L, f).restype = ctypes.c_int
         L.ssmd_last_error.argtypes = []
         L.ssmd_last_error.restype = ctypes.c_char_p
@@ -100,8 +101,8 @@ _ACTS = (torch.float32, torch.bfloat16, torch.float16)
 
 
 def _gdn_common(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices, out, H, norm_gate,
-                norm_weight):
-    _dev(state, "state", torch.float32)
+                norm_weight, state_dtypes=(torch.float32,)):
+    _dev(state, "state", state_dtypes)
     if state.dim() != 4:
         raise ValueError("state must be [num_slots, HV, V, K]")
     num_slots, HV, V, K = state.shape
@@ -147,6 +148,25 @@ def gdn_decode_step(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices, o
                            _ptr(norm_gate), _ptr(norm_weight), norm_eps, ACT_CODE[norm_act],
                            _stream(state, stream))
     _check(rc, "gdn_decode_step")
+    return out
+
+
+def gdn_decode_step_state16(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices, out, *, H=None,
+                            scale=None, use_qk_l2norm=True, l2norm_eps=1e-6, norm_gate=None,
+                            norm_weight=None, norm_eps=1e-5, norm_act="silu", stream=None):
+    """The packed GDN step on a bf16 or f16 state pool (rounded once per step
+    on store); see gdn_decode_step_state16 in include/ssmdec.h."""
+    B, H, HV, K, V, num_slots, act, odt = _gdn_common(
+        mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices, out, H, norm_gate, norm_weight,
+        state_dtypes=(torch.bfloat16, torch.float16))
+    scale = K ** -0.5 if scale is None else scale
+    L = load_library()
+    rc = L.gdn_decode_step_state16(_ptr(mixed_qkv), mixed_qkv.stride(0), _ptr(a), _ptr(b), _ptr(A_log),
+                                   _ptr(dt_bias), _ptr(state), DTYPE_CODE[state.dtype], num_slots,
+                                   _ptr(ssm_state_indices), _ptr(out), B, H, HV, K, V, act, odt, scale,
+                                   int(bool(use_qk_l2norm)), l2norm_eps, _ptr(norm_gate), _ptr(norm_weight),
+                                   norm_eps, ACT_CODE[norm_act], _stream(state, stream))
+    _check(rc, "gdn_decode_step_state16")
     return out
 
 

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tile
   const int G = p.HV / p.H;
   const int h = hv / G;
   const int V = p.V;
-  float* S = p.state + ((int64_t)slot * p.HV + hv) * (int64_t)V * K;
+  float* S = static_cast<float*>(p.state) + ((int64_t)slot * p.HV + hv) * (int64_t)V * K;
   const int r0 = tile * rows_per_tile;
   const int r1 = min(V, r0 + rows_per_tile);
   const int64_t qrow = (int64_t)bi * p.qkv_stride;

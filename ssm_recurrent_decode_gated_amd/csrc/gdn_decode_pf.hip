@@ -61,7 +61,7 @@ __global__ __launch_bounds__(512) void gdn_decode_pf_kernel(GdnParams p, int til
     U.bv = ld_act<ACT>(p.b, gidx);
     U.A_log = p.A_log[U.hv];
     U.dt_bias = p.dt_bias[U.hv];
-    const float* S = p.state + ((int64_t)U.slot * p.HV + U.hv) * (int64_t)p.V * K;
+    const float* S = static_cast<float*>(p.state) + ((int64_t)U.slot * p.HV + U.hv) * (int64_t)p.V * K;
 #pragma unroll
     for (int i = 0; i < RG; ++i) {
       const int row = min(U.r0 + (i * nwaves + wave) * RPI + rr, U.r1 - 1);
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(512) void gdn_decode_pf_kernel(GdnParams p, int til
     const float g = -expf(U.A_log) * softplus_f(U.av + U.dt_bias);
     const float beta = sigmoid_f(U.bv);
     const float decay = expf(g);
-    float* S = p.state + ((int64_t)U.slot * p.HV + U.hv) * (int64_t)p.V * K;
+    float* S = static_cast<float*>(p.state) + ((int64_t)U.slot * p.HV + U.hv) * (int64_t)p.V * K;
     const int64_t obase = ((int64_t)U.bi * p.HV + U.hv) * p.V;
 #pragma unroll
     for (int i = 0; i < RG; ++i) {

@@ -75,7 +75,7 @@ int launch_status(hipError_t e, const char* what) {
 
 // Checks shared by the two GDN entry points. Returns SSMD_OK or an error.
 int check_gdn(const char* fn, const void* qkv, int64_t stride, const void* a, const void* b,
-              const float* A_log, const float* dt_bias, const float* state, int32_t num_slots,
+              const float* A_log, const float* dt_bias, const void* state, int32_t num_slots,
               const int32_t* idx, const void* out, int32_t B, int32_t H, int32_t HV, int32_t K,
               int32_t V, int32_t act, int32_t odt, const void* norm_gate, int32_t norm_act) {
   if (B < 0) return fail(SSMD_ERR_BAD_SHAPE, "%s: B = %d < 0", fn, B);
@@ -103,7 +103,7 @@ int check_gdn(const char* fn, const void* qkv, int64_t stride, const void* a, co
 }
 
 ssmd::GdnParams gdn_params(const void* qkv, int64_t stride, const void* a, const void* b,
-                           const float* A_log, const float* dt_bias, float* state, int32_t num_slots,
+                           const float* A_log, const float* dt_bias, void* state, int32_t num_slots,
                            const int32_t* idx, void* out, int32_t B, int32_t H, int32_t HV, int32_t K,
                            int32_t V, int32_t act, int32_t odt, float scale, int32_t use_l2,
                            float l2eps, const void* norm_gate, const float* norm_w, float norm_eps,
@@ -117,6 +117,7 @@ ssmd::GdnParams gdn_params(const void* qkv, int64_t stride, const void* a, const
   p.A_log = A_log;
   p.dt_bias = dt_bias;
   p.state = state;
+  p.state_dt = SSMD_F32;
   p.num_slots = num_slots;
   p.idx = idx;
   p.out = out;
@@ -190,6 +191,29 @@ int gdn_decode_step(const void* mixed_qkv, int64_t qkv_row_stride, const void* a
     return launch_status(ssmd::launch_gdn_pf(p, l, n_cu, stream), "gdn_decode_step");
   }
   return launch_status(ssmd::launch_gdn(p, l, stream), "gdn_decode_step");
+}
+
+int gdn_decode_step_state16(const void* mixed_qkv, int64_t qkv_row_stride, const void* a, const void* b,
+                            const float* A_log, const float* dt_bias, void* state, int32_t state_dtype,
+                            int32_t num_slots, const int32_t* ssm_state_indices, void* out, int32_t B,
+                            int32_t H, int32_t HV, int32_t K, int32_t V, int32_t act_dtype,
+                            int32_t out_dtype, float scale, int32_t use_qk_l2norm, float l2norm_eps,
+                            const void* norm_gate, const float* norm_weight, float norm_eps,
+                            int32_t norm_act, hipStream_t stream) {
+  const char* fn = "gdn_decode_step_state16";
+  int rc = check_gdn(fn, mixed_qkv, qkv_row_stride, a, b, A_log, dt_bias, state, num_slots,
+                     ssm_state_indices, out, B, H, HV, K, V, act_dtype, out_dtype, norm_gate, norm_act);
+  if (rc) return rc;
+  if (state_dtype != SSMD_BF16 && state_dtype != SSMD_F16)
+    return fail(SSMD_ERR_BAD_DTYPE, "%s: state_dtype must be SSMD_BF16 or SSMD_F16 (got %d)", fn, state_dtype);
+  if (B == 0) return ok();
+  ssmd::GdnParams p = gdn_params(mixed_qkv, qkv_row_stride, a, b, A_log, dt_bias, state, num_slots,
+                                 ssm_state_indices, out, B, H, HV, K, V, act_dtype, out_dtype, scale,
+                                 use_qk_l2norm, l2norm_eps, norm_gate, norm_weight, norm_eps, norm_act);
+  p.state_dt = state_dtype;
+  int n_cu = 0;
+  if (int rc2 = cu_count(&n_cu)) return rc2;
+  return launch_status(ssmd::launch_gdn_s16(p, launch_for(), n_cu, stream), fn);
 }
 
 int gdn_decode_step_buffered(const void* mixed_qkv, int64_t qkv_row_stride, const void* a,

@@ -17,12 +17,11 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
   return __uint_as_float(h << 16);
 }
 
-// fp32 -> bf16 round-to-nearest-even; NaN stays NaN (quiet).
+// fp32 -> bf16, round-to-nearest-even (the default rounding mode), NaN stays
+// NaN: gfx950 converts natively (v_cvt_pk_bf16_f32, two values per
+// instruction), with no per-element branch.
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
@@ -169,6 +168,68 @@ struct RowLayout {
   static constexpr int RPI = 64 / LPR;             // rows per wave-wide access
   __device__ static __forceinline__ int col(int c, int j) { return 4 * (c + LPR * j); }
 };
+
+// Row layout for a state of 16-bit elements: a lane's 128-bit access holds
+// EV = 8 consecutive elements, so lane c of a row owns columns
+// 8(c + LPR j) .. 8(c + LPR j) + 7; one wave-wide access covers RPI rows x 128
+// contiguous bytes, as in the fp32 layout.
+template <int K>
+struct RowLayout16 {
+  static_assert(K == 16 || K == 32 || K == 64 || K == 128 || K == 256, "head size");
+  static constexpr int EV = 8;
+  static constexpr int LPR = K / EV >= 8 ? 8 : K / EV;  // lanes per row
+  static constexpr int NV = K / (EV * LPR);            // 128-bit accesses per lane per row
+  static constexpr int RPI = 64 / LPR;                  // rows per wave-wide access
+  __device__ static __forceinline__ int col(int c, int j) { return EV * (c + LPR * j); }
+};
+
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ u4 ld16x8(const void* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u4*>(p));
+  else return *reinterpret_cast<const u4*>(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ void st16x8(void* p, u4 v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u4*>(p));
+  else *reinterpret_cast<u4*>(p) = v;
+}
+
+// 8 packed 16-bit values <-> fp32 (ST = SSMD_BF16 or SSMD_F16; RNE on packing)
+template <int ST>
+__device__ __forceinline__ void unpack8(u4 v, float out[8]) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t x = v[w];
+    if constexpr (ST == SSMD_BF16) {
+      out[2 * w] = __uint_as_float(x << 16);
+      out[2 * w + 1] = __uint_as_float(x & 0xffff0000u);
+    } else {
+      out[2 * w] = f16_bits_to_f32(x & 0xffffu);
+      out[2 * w + 1] = f16_bits_to_f32(x >> 16);
+    }
+  }
+}
+
+template <int ST>
+__device__ __forceinline__ u4 pack8(const float in[8]) {
+  u4 v;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t lo, hi;
+    if constexpr (ST == SSMD_BF16) {
+      lo = f32_to_bf16_bits(in[2 * w]);
+      hi = f32_to_bf16_bits(in[2 * w + 1]);
+    } else {
+      lo = f32_to_f16_bits(in[2 * w]);
+      hi = f32_to_f16_bits(in[2 * w + 1]);
+    }
+    v[w] = lo | (hi << 16);
+  }
+  return v;
+}
 
 template <bool NT>
 __device__ __forceinline__ f4 ld4(const float* p) {

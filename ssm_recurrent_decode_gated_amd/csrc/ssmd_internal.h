@@ -15,7 +15,8 @@ struct GdnParams {
   const void* b;
   const float* A_log;
   const float* dt_bias;
-  float* state;
+  void* state;       // fp32 pool, or 16-bit for the state16 entry point
+  int32_t state_dt;  // SSMD_F32, SSMD_BF16 or SSMD_F16
   int32_t num_slots;
   const int32_t* idx;
   void* out;
@@ -89,6 +90,8 @@ hipError_t launch_gdn(const GdnParams& p, const Launch& l, hipStream_t s);
 // Persistent prefetching form of the packed step (no output norm); the grid
 // is n_cu blocks unless Launch.grid_cap says otherwise.
 hipError_t launch_gdn_pf(const GdnParams& p, const Launch& l, int n_cu, hipStream_t s);
+// The packed step on a 16-bit state pool (persistent prefetching blocks).
+hipError_t launch_gdn_s16(const GdnParams& p, const Launch& l, int n_cu, hipStream_t s);
 hipError_t launch_gdn_buffered(const GdnParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_kda(const KdaParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_mamba(const MambaParams& p, const Launch& l, hipStream_t s);

@@ -42,6 +42,7 @@ MUTANTS = [
     ("no flush", "if (p == L - 1)\n                memcpy(ck, S", "if (p == L)\n                memcpy(ck, S"),
     ("ring stores unrounded delta", "dring[(size_t)p * V + r] = orc_round_fmt(delta[r], ring_fmt);",
      "dring[(size_t)p * V + r] = delta[r];"),
+    ("16-bit state not rounded", "S[e] = orc_round_fmt(S[e], state_fmt);", "S[e] = S[e];"),
     ("mamba drops input", "h[n] = dA * h[n] + dB * xv;", "h[n] = dA * h[n] + dB;"),
     ("mamba no D skip", "acc += Dv[d] * xv;", "acc += Dv[d];"),
     ("bf16 rounding truncates", "double r = nearbyint(x / ulp) * ulp;", "double r = trunc(x / ulp) * ulp;"),
@@ -56,6 +57,8 @@ def _pin_functions():
         params = inspect.signature(fn).parameters
         if "L" in params:
             fns += [(f"{name}[L={L}]", lambda fn=fn, L=L: fn(L)) for L in (1, 3, 8)]
+        elif "fmt" in params:
+            fns += [(f"{name}[fmt={f}]", lambda fn=fn, f=f: fn(f)) for f in (O.FMT_BF16, O.FMT_F16)]
         elif not params:
             fns.append((name, fn))
     return fns

@@ -268,6 +268,26 @@ def test_pin_gated_norm_constant_output():
         np.testing.assert_allclose(out[0, 0], w * f(z) / math.sqrt(1 + eps), rtol=1e-14)
 
 
+@pytest.mark.parametrize("fmt", [O.FMT_BF16, O.FMT_F16])
+def test_pin_16bit_state_rounds_on_store_only(fmt):
+    """A 16-bit state pool ([LOG] "Kernel 4" sizes the state as 16-bit) stores
+    round(S_new) while the step's output comes from the unrounded S_new: the
+    output equals the fp64-state run exactly and the stored state is its
+    elementwise rounding."""
+    rng = np.random.default_rng(60 + fmt)
+    B, H, HV, K, V = 3, 2, 4, 16, 8
+    qkv, a, b, A_log, dt_bias, state = _rand_gdn(rng, B, H, HV, K, V, slots=4)
+    state = np.vectorize(lambda x: O.round_fmt(x, fmt))(state)  # a pool that holds 16-bit values
+    idx = np.array([3, 1, 0], np.int32)
+    s64, s16 = state.copy(), state.copy()
+    o64 = O.gdn_step(qkv, a, b, A_log, dt_bias, s64, idx, H=H, HV=HV, K=K, V=V)
+    o16 = O.gdn_step(qkv, a, b, A_log, dt_bias, s16, idx, H=H, HV=HV, K=K, V=V, state_fmt=fmt)
+    np.testing.assert_array_equal(o16, o64)
+    np.testing.assert_array_equal(s16, np.vectorize(lambda x: O.round_fmt(x, fmt))(s64))
+    assert not np.array_equal(s16[idx], s64[idx])
+    np.testing.assert_array_equal(s16[2], state[2])
+
+
 # ------------------------------------------------------------ buffered step
 def _buffered_setup(rng, B=3, H=2, HV=4, K=8, V=6, L=4):
     qkv, a, b, A_log, dt_bias, state = _rand_gdn(rng, B, H, HV, K, V, slots=B)
