@@ -47,7 +47,8 @@ def configure(L: ctypes.CDLL) -> ctypes.CDLL:
     L.orc_kda_decode.argtypes = [_i] * 5 + [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _d,
                                             _dp, _ip, _dp, _dp, _dp, _d, _d, _i, _d, _dp]
     L.orc_mamba_step.argtypes = [_i] * 4 + [_dp] * 8 + [_ip, _dp]
-    for f in ("orc_gdn_step", "orc_gdn_step_buffered", "orc_conv1d_update",
+    L.orc_gdn_step_conv.argtypes = [_i] * 7 + [_dp] * 9 + [_ip, _dp, _d, _i, _d, _dp, _dp, _d, _i, _dp]
+    for f in ("orc_gdn_step", "orc_gdn_step_buffered", "orc_conv1d_update", "orc_gdn_step_conv",
               "orc_kda_step", "orc_kda_decode", "orc_mamba_step", "orc_num_threads"):
         getattr(L, f).restype = _i
     return L
@@ -178,6 +179,32 @@ def gdn_step_buffered(qkv, a, b, A_log, dt_bias, state, idx, d_cache, k_cache, g
         B, H, HV, K, V, num_slots, _p(qkv), qkv.shape[1], _p(a), _p(b), _p(A_log),
         _p(dt_bias), _p(state), _p(idx), _p(out), scale, int(use_l2), l2eps, _p(ng), _p(nw),
         norm_eps, norm_act, _p(d_cache), _p(k_cache), _p(g_cache), _p(wp), L, ring_fmt))
+    return out
+
+
+def gdn_step_conv(x, conv_w, conv_bias, conv_state, a, b, A_log, dt_bias, state, idx, *, H, HV, K, V,
+                  scale=None, use_l2=True, l2eps=1e-6, norm_gate=None, norm_weight=None,
+                  norm_eps=1e-5, norm_act=ACT_SILU):
+    """GDN step with the causal conv1d update (+SiLU) fused in front. x is the
+    pre-conv [B, 2HK + HV V]; conv_state float64 logical [num_slots, C, W-1]
+    and state float64 [num_slots, HV, V, K] are updated in place. Returns out
+    [B, HV, V]."""
+    x, conv_w, a, b = f64(x), f64(conv_w), f64(a), f64(b)
+    A_log, dt_bias, idx = f64(A_log), f64(dt_bias), i32(idx)
+    cb = None if conv_bias is None else f64(conv_bias)
+    B = idx.shape[0]
+    W = conv_w.shape[1]
+    C = 2 * H * K + HV * V
+    assert x.shape == (B, C) and conv_state.shape[1:] == (C, W - 1)
+    out = np.full((B, HV, V), np.nan)
+    ysc = np.zeros((B, C))
+    ng = None if norm_gate is None else f64(norm_gate)
+    nw = None if norm_weight is None else f64(norm_weight)
+    scale = K ** -0.5 if scale is None else scale
+    _chk(lib().orc_gdn_step_conv(B, H, HV, K, V, W, state.shape[0], _p(x), _p(conv_w), _p(cb),
+                                 _p(conv_state), _p(a), _p(b), _p(A_log), _p(dt_bias), _p(state),
+                                 _p(idx), _p(out), scale, int(use_l2), l2eps, _p(ng), _p(nw), norm_eps,
+                                 norm_act, _p(ysc)))
     return out
 
 

@@ -459,6 +459,32 @@ int orc_kda_decode(int T, int H, int D, int W, int num_slots, const double *x,
                         norm_eps, scale, use_l2, l2eps);
 }
 
+/* GDN with its causal conv1d update fused in front (the KDA fused op's
+ * pattern, [KDA] module docstring and `triton_chain`, applied to the GDN step
+ * of [REPLAY]; [LOG] "Integration" lists the DeltaNet forward as projection +
+ * conv1d + recurrent + gated norm): the pre-conv activations x [B][2HK+HV*V]
+ * go through orc_conv1d_update (SiLU, conv state per slot, padded rows
+ * skipped by the GDN rule), and the fp64 conv output is the step's mixed_qkv.
+ * y_scratch is [B][2HK+HV*V]. */
+int orc_gdn_step_conv(int B, int H, int HV, int K, int V, int W, int num_slots,
+                      const double *x, const double *conv_w,
+                      const double *conv_b, double *conv_state,
+                      const double *a, const double *b, const double *A_log,
+                      const double *dt_bias, double *state, const int32_t *idx,
+                      double *out, double scale, int use_l2, double l2eps,
+                      const double *norm_gate, const double *norm_w,
+                      double norm_eps, int norm_act, double *y_scratch)
+{
+    const int C = 2 * H * K + HV * V;
+    int rc = orc_conv1d_update(B, C, W, num_slots, x, conv_w, conv_b, conv_state,
+                               idx, 0, y_scratch, 1);
+    if (rc)
+        return rc;
+    return orc_gdn_step(B, H, HV, K, V, num_slots, y_scratch, C, a, b, A_log,
+                        dt_bias, state, idx, out, scale, use_l2, l2eps,
+                        norm_gate, norm_w, norm_eps, norm_act, ORC_FMT_NONE);
+}
+
 /* ------------------------------------------------------------------ */
 /* Mamba-1 selective-scan decode step                                  */
 /* ------------------------------------------------------------------ */

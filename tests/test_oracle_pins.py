@@ -472,6 +472,35 @@ def test_pin_kda_decode_is_conv_then_step():
     assert np.isnan(o1[1]).all()
 
 
+def test_pin_gdn_conv_is_conv_then_step():
+    """The fused GDN conv step equals the conv update (SiLU) followed by the GDN
+    step on the fp64 conv output; padded rows (GDN rule: < 0 or >= num_slots)
+    touch neither the conv state nor the recurrent state."""
+    rng = np.random.default_rng(50)
+    B, H, HV, K, V, W = 3, 2, 4, 8, 6, 4
+    C = 2 * H * K + HV * V
+    x = rng.standard_normal((B, C))
+    cw = rng.standard_normal((C, W)) * 0.5
+    cb = rng.standard_normal(C) * 0.1
+    a, b = rng.standard_normal((B, HV)), rng.standard_normal((B, HV))
+    A_log, dt_bias = rng.standard_normal(HV) * 0.3, rng.standard_normal(HV) * 0.1
+    cs = rng.standard_normal((4, C, W - 1))
+    st = rng.standard_normal((4, HV, V, K))
+    idx = np.array([2, -1, 0], np.int32)
+    cs1, st1, cs2, st2 = cs.copy(), st.copy(), cs.copy(), st.copy()
+    o1 = O.gdn_step_conv(x, cw, cb, cs1, a, b, A_log, dt_bias, st1, idx, H=H, HV=HV, K=K, V=V)
+    y = O.conv1d_update(x, cw, cb, cs2, idx, skip_slot0=False)
+    o2 = O.gdn_step(np.nan_to_num(y), a, b, A_log, dt_bias, st2, idx, H=H, HV=HV, K=K, V=V)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(cs1, cs2)
+    np.testing.assert_array_equal(st1, st2)
+    for s_ in (1, 3):
+        np.testing.assert_array_equal(cs1[s_], cs[s_])
+        np.testing.assert_array_equal(st1[s_], st[s_])
+    assert not np.array_equal(cs1[0], cs[0])  # slot 0 is a real slot for GDN
+    assert np.isnan(o1[1]).all()
+
+
 # ------------------------------------------------------------ Mamba-1
 def test_pin_mamba_scalar_recurrence():
     """N = 1 with constant inputs: h_T = a^T h0 + dB x (1 - a^T) / (1 - a) with
