@@ -266,6 +266,37 @@ def kda(dev, reps=30):
             "pct_hbm_peak": round(100 * sb / us / 1e3 / HBM_PEAK_GBS, 2), "pools": M}
 
 
+def gdn_conv(dev, reps=30, Wd=4):
+    """The B=256-of-264 GDN step with its causal conv1d update fused in front
+    (gdn_decode_step_conv, conv width 4, bf16 conv state in the [slots, C,
+    W-1] layout), graph replay of one call per pool. Algorithmic bytes: the
+    packed step's plus the conv state read and written and the conv weights
+    read once."""
+    import torch
+    import ssm_recurrent_decode_gated_amd as S
+    import workloads as W
+    w = W.GDN_B256
+    pool_bytes = w.num_slots * w.HV * w.V * w.K * 4
+    M = _pools_for(pool_bytes)
+    su = GDNSetup(w, M, dev)
+    cv = W.gdn_conv(w, Wd)
+    cw, cb = cv["conv_weight"].to(dev), cv["conv_bias"].to(dev)
+    cs = [cv["conv_state"].to(dev) for _ in range(M)]
+
+    def call(i):
+        S.gdn_decode_step_conv(su.qkv, cw, cb, cs[i], su.a, su.b, su.A_log, su.dt_bias, su.pools[i], su.idx_d,
+                               su.out)
+    us = graph_time_us([lambda i=i: call(i) for i in range(M)], reps, torch.cuda.current_stream())
+    C = 2 * w.H * w.K + w.HV * w.V
+    sb = gdn_state_bytes(w.B, w.HV, w.V, w.K)
+    ab = gdn_alg_bytes(w.B, w.H, w.HV, w.K, w.V) + 2 * w.B * C * (Wd - 1) * 2 + C * (Wd + 1) * 4
+    del su, cs
+    torch.cuda.empty_cache()
+    return {"workload": w.name + f"_conv{Wd}", "us_per_step": round(us, 3), "state_GBps": round(sb / us / 1e3, 1),
+            "alg_GBps": round(ab / us / 1e3, 1), "pct_hbm_peak_alg": round(100 * ab / us / 1e3 / HBM_PEAK_GBS, 2),
+            "pools": M}
+
+
 def mamba(dev, reps=30):
     """Mamba-1 decode (graph replay of one call per pool): the MBU write-up's
     table shapes, plus a bandwidth-sized batch. Byte counts: the write-up's
@@ -409,7 +440,7 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="headline only (no sweep/buffered/KDA/copy)")
+    ap.add_argument("--no-extras", action="store_true", help="headline only (no sweep/buffered/KDA/conv/Mamba/copy)")
     ap.add_argument("--profile-pass", action="store_true")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--out", default=COUNTERS_FILE)
@@ -447,6 +478,7 @@ def main():
         extra["graph_sweep"] = sweep(dev)
         extra["buffered_b64"] = buffered(dev)
         extra["kda_t64_h96"] = kda(dev)
+        extra["gdn_conv_b256"] = gdn_conv(dev)
         extra["mamba1"] = mamba(dev)
         extra["state16_b256"] = state16(dev)
         extra["state16_b256"]["speedup_vs_fp32_state"] = round(h["us"] / extra["state16_b256"]["us_per_step"], 3)

@@ -167,6 +167,46 @@ int gdn_decode_step_buffered(const void* mixed_qkv, int64_t qkv_row_stride,
                              hipStream_t stream);
 
 /*
+ * gdn_decode_step_conv -- gdn_decode_step with the causal conv1d update + SiLU
+ * of its q, k and v channels fused in front, in one launch (the fused op of
+ * [KDA] module docstring and `triton_chain` applied to the GDN step; [LOG]
+ * "Kernel 5: Fused Causal Conv1d Update" and "Integration" place the conv
+ * between the input projection and the recurrence).
+ *
+ * For every row b whose slot s = ssm_state_indices[b] is in [0, num_slots)
+ * and every channel c < C = 2*H*K + HV*V:
+ *   window = [conv_state[s, c, 0..W-2], x[b, c]]  (oldest first)
+ *   y[c]   = silu(sum_j conv_weight[c, j] window[j] + conv_bias[c])
+ *   conv_state[s, c, :] <- window[1..W-1]         (bit-exact shift)
+ * then gdn_decode_step on mixed_qkv[b] = y (kept in fp32, never rounded to
+ * act_dtype). Padded rows touch neither state nor conv_state nor out.
+ *   x            [B, row stride x_row_stride >= C] act_dtype, pre-conv,
+ *                q heads | k heads | v heads as mixed_qkv of gdn_decode_step
+ *   conv_weight  [C, W] fp32; conv_bias [C] fp32 or NULL
+ *   conv_state   logical [num_slots, C, W-1] act_dtype at element strides
+ *                (cs_slot_stride, cs_chan_stride, cs_tap_stride), as in
+ *                kda_decode_step (SD and DS layouts alike)
+ *   2 <= W <= 8; HV / H <= 16 and (HV / H) * V <= 4096 (one block holds a
+ *   q/k head's whole group of value heads). All other arguments, layouts and
+ *   conventions are those of gdn_decode_step.
+ */
+int gdn_decode_step_conv(const void* x, int64_t x_row_stride,
+                         const float* conv_weight, const float* conv_bias,
+                         void* conv_state, int64_t cs_slot_stride,
+                         int64_t cs_chan_stride, int64_t cs_tap_stride, int32_t W,
+                         const void* a, const void* b,
+                         const float* A_log, const float* dt_bias,
+                         float* state, int32_t num_slots,
+                         const int32_t* ssm_state_indices,
+                         void* out,
+                         int32_t B, int32_t H, int32_t HV, int32_t K, int32_t V,
+                         int32_t act_dtype, int32_t out_dtype,
+                         float scale, int32_t use_qk_l2norm, float l2norm_eps,
+                         const void* norm_gate, const float* norm_weight,
+                         float norm_eps, int32_t norm_act,
+                         hipStream_t stream);
+
+/*
  * kda_decode_step -- the fused KDA decode op: causal conv1d update + SiLU,
  * per-key-channel gated delta rule, sigmoid-gated RMSNorm, in one launch
  * ([KDA] module docstring, `triton_chain` and `fused`, `_gated_rmsnorm`;

@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     SsmdError,
     gdn_decode_step,
     gdn_decode_step_buffered,
+    gdn_decode_step_conv,
     gdn_decode_step_state16,
     kda_decode_step,
     load_library,
@@ -22,5 +23,6 @@ from ._binding import (  # noqa: F401
     ssmd_stream_copy,
 )
 
-__all__ = ["gdn_decode_step", "gdn_decode_step_state16", "gdn_decode_step_buffered", "kda_decode_step", "mamba_decode_step",
-           "ssmd_last_error", "ssmd_stream_copy", "SsmdError", "load_library"]
+__all__ = ["gdn_decode_step", "gdn_decode_step_state16", "gdn_decode_step_buffered", "gdn_decode_step_conv",
+           "kda_decode_step", "mamba_decode_step", "ssmd_last_error", "ssmd_stream_copy", "SsmdError",
+           "load_library"]

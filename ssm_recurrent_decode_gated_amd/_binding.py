@@ -20,8 +20,8 @@ SSMD_F32, SSMD_BF16, SSMD_F16 = 0, 1, 2
 SSMD_ACT_SILU, SSMD_ACT_SIGMOID = 0, 1
 DTYPE_CODE = {torch.float32: SSMD_F32, torch.bfloat16: SSMD_BF16, torch.float16: SSMD_F16}
 ACT_CODE = {"silu": SSMD_ACT_SILU, "sigmoid": SSMD_ACT_SIGMOID}
-EXPORTS = ("gdn_decode_step", "gdn_decode_step_state16", "gdn_decode_step_buffered", "kda_decode_step",
-           "mamba_decode_step", "ssmd_last_error", "ssmd_stream_copy")
+EXPORTS = ("gdn_decode_step", "gdn_decode_step_state16", "gdn_decode_step_buffered", "gdn_decode_step_conv",
+           "kda_decode_step", "mamba_decode_step", "ssmd_last_error", "ssmd_stream_copy")
 
 
 class SsmdError(RuntimeError):
@@ -49,14 +49,16 @@ def load_library() -> ctypes.CDLL:
         L.gdn_decode_step.argtypes = _GDN_ARGS + [_p]
         L.gdn_decode_step_buffered.argtypes = _GDN_ARGS + [_p, _p, _p, _p, _i32, _p]
         L.gdn_decode_step_state16.argtypes = _GDN_ARGS[:7] + [_i32] + _GDN_ARGS[7:] + [_p]
+        L.gdn_decode_step_conv.argtypes = [_p, _i64, _p, _p, _p, _i64, _i64, _i64, _i32] + _GDN_ARGS[2:] + [_p]
         L.kda_decode_step.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _f, _p, _i32,
                                       _p, _p, _p, _p, _f, _i32, _i32, _i32, _i32, _i32, _i32, _f,
                                       _i32, _f, _p]
         L.mamba_decode_step.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _p, _i32, _i32, _i32,
                                         _i32, _i32, _p]
         L.ssmd_stream_copy.argtypes = [_p, _p, _i64, _p]
-        for f in ("gdn_decode_step", "gdn_decode_step_state16", "gdn_decode_step_buffered", "kda_decode_step",
-                  "mamba_decode_step", "ssmd_stream_copy"):
+        for f in EXPORTS:
+            if f == "ssmd_last_error":
+                continue
             getattr(L, f).restype = ctypes.c_int
         L.ssmd_last_error.argtypes = []
         L.ssmd_last_error.restype = ctypes.c_char_p
@@ -194,6 +196,35 @@ def gdn_decode_step_buffered(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_i
         ACT_CODE[norm_act], _ptr(d_cache), _ptr(k_cache), _ptr(g_cache), _ptr(write_pos), L_,
         _stream(state, stream))
     _check(rc, "gdn_decode_step_buffered")
+    return out
+
+
+def gdn_decode_step_conv(x, conv_weight, conv_bias, conv_state, a, b, A_log, dt_bias, state,
+                         ssm_state_indices, out, *, H=None, scale=None, use_qk_l2norm=True,
+                         l2norm_eps=1e-6, norm_gate=None, norm_weight=None, norm_eps=1e-5,
+                         norm_act="silu", stream=None):
+    """The GDN step with its causal conv1d update + SiLU fused in front; see
+    gdn_decode_step_conv in include/ssmdec.h. x is the pre-conv row (unit
+    column stride, any row stride); conv_state is the logical
+    [num_slots, C, W-1] view of either physical layout."""
+    B, H, HV, K, V, num_slots, act, odt = _gdn_common(x, a, b, A_log, dt_bias, state,
+                                                      ssm_state_indices, out, H, norm_gate, norm_weight)
+    C = 2 * H * K + HV * V
+    _dev(conv_weight, "conv_weight", torch.float32)
+    if conv_weight.dim() != 2 or conv_weight.shape[0] != C:
+        raise ValueError(f"conv_weight must be [{C}, W]")
+    W = conv_weight.shape[1]
+    if conv_bias is not None:
+        _dev(conv_bias, "conv_bias", torch.float32, (C,))
+    _dev(conv_state, "conv_state", x.dtype, (num_slots, C, W - 1), contiguous=False)
+    scale = K ** -0.5 if scale is None else scale
+    rc = load_library().gdn_decode_step_conv(
+        _ptr(x), x.stride(0), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state), conv_state.stride(0),
+        conv_state.stride(1), conv_state.stride(2), W, _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+        _ptr(state), num_slots, _ptr(ssm_state_indices), _ptr(out), B, H, HV, K, V, act, odt, scale,
+        int(bool(use_qk_l2norm)), l2norm_eps, _ptr(norm_gate), _ptr(norm_weight), norm_eps,
+        ACT_CODE[norm_act], _stream(state, stream))
+    _check(rc, "gdn_decode_step_conv")
     return out
 
 

@@ -249,6 +249,42 @@ int gdn_decode_step_buffered(const void* mixed_qkv, int64_t qkv_row_stride, cons
   return launch_status(ssmd::launch_gdn_buffered(p, l, stream), fn);
 }
 
+int gdn_decode_step_conv(const void* x, int64_t x_row_stride, const float* conv_weight,
+                         const float* conv_bias, void* conv_state, int64_t cs_slot_stride,
+                         int64_t cs_chan_stride, int64_t cs_tap_stride, int32_t W, const void* a,
+                         const void* b, const float* A_log, const float* dt_bias, float* state,
+                         int32_t num_slots, const int32_t* ssm_state_indices, void* out, int32_t B,
+                         int32_t H, int32_t HV, int32_t K, int32_t V, int32_t act_dtype,
+                         int32_t out_dtype, float scale, int32_t use_qk_l2norm, float l2norm_eps,
+                         const void* norm_gate, const float* norm_weight, float norm_eps,
+                         int32_t norm_act, hipStream_t stream) {
+  const char* fn = "gdn_decode_step_conv";
+  int rc = check_gdn(fn, x, x_row_stride, a, b, A_log, dt_bias, state, num_slots, ssm_state_indices,
+                     out, B, H, HV, K, V, act_dtype, out_dtype, norm_gate, norm_act);
+  if (rc) return rc;
+  if (W < 2 || W > 8) return fail(SSMD_ERR_BAD_SHAPE, "%s: conv width W = %d outside [2, 8]", fn, W);
+  if (HV / H > 16 || (int64_t)(HV / H) * V > 4096)
+    return fail(SSMD_ERR_UNSUPPORTED, "%s: HV/H = %d > 16 or (HV/H)*V = %lld > 4096", fn, HV / H,
+                (long long)(HV / H) * V);
+  if (cs_slot_stride < 1 || cs_chan_stride < 1 || cs_tap_stride < 1)
+    return fail(SSMD_ERR_BAD_SHAPE, "%s: conv-state strides must be positive", fn);
+  if ((int64_t)B * H >= (1LL << 31)) return fail(SSMD_ERR_BAD_SHAPE, "%s: B*H too large", fn);
+  if (B == 0) return ok();
+  if (!conv_weight || !conv_state) return fail(SSMD_ERR_NULL_ARG, "%s: conv_weight or conv_state is NULL", fn);
+  ssmd::GdnConvParams cp{};
+  cp.g = gdn_params(x, x_row_stride, a, b, A_log, dt_bias, state, num_slots, ssm_state_indices, out, B,
+                    H, HV, K, V, act_dtype, out_dtype, scale, use_qk_l2norm, l2norm_eps, norm_gate,
+                    norm_weight, norm_eps, norm_act);
+  cp.conv_w = conv_weight;
+  cp.conv_b = conv_bias;
+  cp.conv_state = conv_state;
+  cp.cs_slot = cs_slot_stride;
+  cp.cs_chan = cs_chan_stride;
+  cp.cs_tap = cs_tap_stride;
+  cp.W = W;
+  return launch_status(ssmd::launch_gdn_conv(cp, launch_for(), stream), fn);
+}
+
 int kda_decode_step(const void* x, const float* conv_weight, const float* conv_bias, void* conv_state,
                     int64_t cs_slot_stride, int64_t cs_chan_stride, int64_t cs_tap_stride,
                     const void* raw_g, const void* raw_beta, const float* A_log, const float* dt_bias,

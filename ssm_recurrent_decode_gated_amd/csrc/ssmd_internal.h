@@ -37,6 +37,18 @@ struct GdnParams {
   int32_t L;
 };
 
+// GDN step with the causal conv1d update in front: g.qkv is the pre-conv row
+// x (stride g.qkv_stride); the conv state holds the last W - 1 inputs of each
+// channel in the activation dtype.
+struct GdnConvParams {
+  GdnParams g;
+  const float* conv_w;  // [C][W], C = 2 H K + HV V
+  const float* conv_b;  // [C] or NULL
+  void* conv_state;
+  int64_t cs_slot, cs_chan, cs_tap;
+  int32_t W;
+};
+
 struct KdaParams {
   const void* x;
   const float* conv_w;
@@ -94,6 +106,7 @@ hipError_t launch_gdn_pf(const GdnParams& p, const Launch& l, int n_cu, hipStrea
 hipError_t launch_gdn_s16(const GdnParams& p, const Launch& l, int n_cu, hipStream_t s);
 hipError_t launch_gdn_buffered(const GdnParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_kda(const KdaParams& p, const Launch& l, hipStream_t s);
+hipError_t launch_gdn_conv(const GdnConvParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_mamba(const MambaParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
 

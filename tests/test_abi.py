@@ -153,3 +153,23 @@ def test_mamba_host_validation():
     assert call(A=0x20004) == BAD_SHAPE
     assert call(state=0x30008) == BAD_SHAPE
     assert call(B=0, x=None) == OK
+
+
+def test_gdn_conv_host_validation():
+    L = S.load_library()
+
+    def call(W=4, cw=0x90000, cst=0xA0000, cs=(8192 * 3, 3, 1), H=16, HV=32, V=128, B=4, x=0x10000):
+        stride = 2 * H * 128 + HV * V
+        return L.gdn_decode_step_conv(x, stride, cw, None, cst, cs[0], cs[1], cs[2], W, 0x20000, 0x30000,
+                                      0x40000, 0x50000, 0x60000, 16, 0x70000, 0x80000, B, H, HV, 128, V, 1, 1,
+                                      0.088, 1, 1e-6, None, None, 1e-5, 0, None)
+    assert call(W=1) == BAD_SHAPE
+    assert call(W=9) == BAD_SHAPE
+    assert call(cw=None) == NULL_ARG
+    assert call(cst=None) == NULL_ARG
+    assert call(x=None) == NULL_ARG
+    assert call(cs=(1, 0, 1)) == BAD_SHAPE
+    assert call(H=1, HV=32) == UNSUPPORTED        # a q/k group of 32 value heads
+    assert call(H=4, HV=64, V=512) == UNSUPPORTED  # (HV/H) V = 8192 outputs in one group
+    assert call(HV=24) == BAD_SHAPE
+    assert call(B=0, x=None, cw=None, cst=None) == OK

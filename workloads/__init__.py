@@ -130,6 +130,23 @@ def gdn_ring(w: GDNWorkload, L: int, seed=0) -> dict:
     }
 
 
+def gdn_conv(w: GDNWorkload, W: int = 4, seed=0, layout="DS", bias=True) -> dict:
+    """Conv parameters and state of the conv-fused GDN step, over the
+    C = 2HK + HV V channels of mixed_qkv: conv_weight [C, W] ~ N(0, 1/W),
+    conv_bias [C] ~ N(0, 0.1^2) fp32, and conv_state, a logical
+    [num_slots, C, W-1] view (activation dtype, ~N(0, 1)) over the physical
+    layout `layout` ("DS" = [slots, C, W-1], "SD" = [slots, W-1, C])."""
+    g = generator(seed, w.name, "conv", W)
+    C = 2 * w.H * w.K + w.HV * w.V
+    cs = normal((w.num_slots, C, W - 1), 1.0, w.act, g)
+    d = {
+        "conv_weight": normal((C, W), W ** -0.5, "f32", g),
+        "conv_bias": normal((C,), 0.1, "f32", g) if bias else None,
+        "conv_state": cs.transpose(1, 2).contiguous().transpose(1, 2) if layout == "SD" else cs.contiguous(),
+    }
+    return d
+
+
 # ----------------------------------------------------------------- KDA
 @dataclass(frozen=True)
 class KDAWorkload:
