@@ -47,9 +47,10 @@ def configure(L: ctypes.CDLL) -> ctypes.CDLL:
     L.orc_kda_decode.argtypes = [_i] * 5 + [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _d,
                                             _dp, _ip, _dp, _dp, _dp, _d, _d, _i, _d, _dp]
     L.orc_mamba_step.argtypes = [_i] * 4 + [_dp] * 8 + [_ip, _dp]
+    L.orc_mamba_scan.argtypes = [_i] * 5 + [_dp] * 8 + [_ip, _ip, _i, _dp]
     L.orc_gdn_step_conv.argtypes = [_i] * 7 + [_dp] * 9 + [_ip, _dp, _d, _i, _d, _dp, _dp, _d, _i, _dp]
     for f in ("orc_gdn_step", "orc_gdn_step_buffered", "orc_conv1d_update", "orc_gdn_step_conv",
-              "orc_kda_step", "orc_kda_decode", "orc_mamba_step", "orc_num_threads"):
+              "orc_kda_step", "orc_kda_decode", "orc_mamba_step", "orc_mamba_scan", "orc_num_threads"):
         getattr(L, f).restype = _i
     return L
 
@@ -268,6 +269,23 @@ def kda_decode(x, conv_w, conv_bias, conv_state, raw_g, raw_beta, state, idx, *,
 
 
 # ----------------------------------------------------------------- Mamba
+def mamba_scan(x, dt, A, Bm, Cm, Dv, z, hpool, idx, lengths=None, zero_init=False):
+    """Mamba-1 over T tokens per row (prefill); x, dt, z [B, T, D], Bm, Cm
+    [B, T, N]; hpool float64 [num_slots, D, N] in place (read unless
+    zero_init, written with the final state). Returns y [B, T, D] (NaN where
+    not written)."""
+    x, dt, A, Bm, Cm, idx = f64(x), f64(dt), f64(A), f64(Bm), f64(Cm), i32(idx)
+    Dv = None if Dv is None else f64(Dv)
+    z = None if z is None else f64(z)
+    ln = None if lengths is None else i32(lengths)
+    B, T, Dm = x.shape
+    N = A.shape[1]
+    y = np.full((B, T, Dm), np.nan)
+    _chk(lib().orc_mamba_scan(B, T, Dm, N, hpool.shape[0], _p(x), _p(dt), _p(A), _p(Bm), _p(Cm), _p(Dv),
+                              _p(z), _p(hpool), _p(idx), _p(ln), int(bool(zero_init)), _p(y)))
+    return y
+
+
 def mamba_step(x, dt, A, Bm, Cm, Dv, z, hpool, idx):
     """Mamba-1 selective-scan decode step; hpool float64 [num_slots, D, N] in
     place. Returns y [B, D]."""

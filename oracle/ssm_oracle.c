@@ -528,6 +528,61 @@ int orc_mamba_step(int B, int Dm, int N, int num_slots, const double *x,
     return ORC_OK;
 }
 
+/* Mamba-1 over T tokens (prefill): the step above applied to tokens
+ * 0..len-1 of each row in order, the state carried between them ([MBU]
+ * "Prefill path": the multi-token scan over the same recurrence). Per row b
+ * with slot s = idx[b] in [0, num_slots) and len = lengths ? lengths[b] : T:
+ *   h = zero_init ? 0 : hpool[s]
+ *   for t < len: h <- exp(dt[b,t,d] A[d,:]) h + dt[b,t,d] B[b,t,:] x[b,t,d]
+ *                y[b,t,d] = sum_n C[b,t,n] h[n] (+ D[d] x) (* silu(z[b,t,d]))
+ *   hpool[s] = h
+ * x, dt, z, y are [B][T][Dm]; Bm, Cm are [B][T][N]; y rows t >= len and
+ * padded rows are not written. */
+int orc_mamba_scan(int B, int T, int Dm, int N, int num_slots, const double *x,
+                   const double *dt, const double *A, const double *Bm,
+                   const double *Cm, const double *Dv, const double *z,
+                   double *hpool, const int32_t *idx, const int32_t *lengths,
+                   int zero_init, double *y)
+{
+    if (B < 0 || T < 0 || Dm < 1 || N < 1 || num_slots < 1)
+        return ORC_BAD;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int bi = 0; bi < B; ++bi) {
+        for (int d = 0; d < Dm; ++d) {
+            const int s = idx[bi];
+            if (s < 0 || s >= num_slots)
+                continue;
+            int len = lengths ? lengths[bi] : T;
+            if (len < 0)
+                len = 0;
+            if (len > T)
+                len = T;
+            double *h = hpool + ((size_t)s * Dm + d) * (size_t)N;
+            if (zero_init)
+                for (int n = 0; n < N; ++n)
+                    h[n] = 0.0;
+            for (int t = 0; t < len; ++t) {
+                const size_t bt = (size_t)bi * T + t;
+                const double xv = x[bt * Dm + d];
+                const double dtv = dt[bt * Dm + d];
+                double acc = 0.0;
+                for (int n = 0; n < N; ++n) {
+                    const double dA = exp(dtv * A[(size_t)d * N + n]);
+                    const double dB = dtv * Bm[bt * N + n];
+                    h[n] = dA * h[n] + dB * xv;
+                    acc += Cm[bt * N + n] * h[n];
+                }
+                if (Dv)
+                    acc += Dv[d] * xv;
+                if (z)
+                    acc *= orc_silu(z[bt * Dm + d]);
+                y[bt * Dm + d] = acc;
+            }
+        }
+    }
+    return ORC_OK;
+}
+
 /* number of OpenMP threads the parallel loops above use */
 int orc_num_threads(void)
 {

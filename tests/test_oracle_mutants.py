@@ -45,6 +45,11 @@ MUTANTS = [
     ("16-bit state not rounded", "S[e] = orc_round_fmt(S[e], state_fmt);", "S[e] = S[e];"),
     ("mamba drops input", "h[n] = dA * h[n] + dB * xv;", "h[n] = dA * h[n] + dB;"),
     ("mamba no D skip", "acc += Dv[d] * xv;", "acc += Dv[d];"),
+    ("scan ignores stored state", "if (zero_init)\n                for (int n = 0; n < N; ++n)",
+     "if (1)\n                for (int n = 0; n < N; ++n)"),
+    ("scan drops last token", "for (int t = 0; t < len; ++t) {", "for (int t = 0; t < len - 1; ++t) {"),
+    ("scan reads token-major B", "const double dB = dtv * Bm[bt * N + n];",
+     "const double dB = dtv * Bm[((size_t)t * B + bi) * N + n];"),
     ("bf16 rounding truncates", "double r = nearbyint(x / ulp) * ulp;", "double r = trunc(x / ulp) * ulp;"),
 ]
 

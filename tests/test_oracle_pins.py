@@ -533,3 +533,70 @@ def test_pin_mamba_channels_independent_and_padding():
         assert y[0, d] == pytest.approx(float(Cm[0] @ hn), rel=1e-13)
     assert np.isnan(y[1]).all()
     np.testing.assert_array_equal(h[:2], h0[:2])
+
+
+def test_pin_mamba_scan_scalar_closed_form():
+    """The multi-token scan with N = 1 and constant inputs over T tokens:
+    every y_t and the final state follow the geometric closed form, from a
+    stored initial state and from zero."""
+    dt, A, Bv, Cv, Dv, x, z, h0, T = 0.05, -3.0, 0.7, 1.3, 0.4, 0.9, 0.6, 2.0, 25
+    a = math.exp(dt * A)
+    silu = z / (1 + math.exp(-z))
+    for zero_init, start in ((False, h0), (True, 0.0)):
+        h = np.array([[[h0]]])
+        y = O.mamba_scan(np.full((1, T, 1), x), np.full((1, T, 1), dt), [[A]], np.full((1, T, 1), Bv),
+                         np.full((1, T, 1), Cv), [Dv], np.full((1, T, 1), z), h, [0], zero_init=zero_init)
+        for t in range(1, T + 1):
+            ht = a ** t * start + dt * Bv * x * (1 - a ** t) / (1 - a)
+            assert y[0, t - 1, 0] == pytest.approx((Cv * ht + Dv * x) * silu, rel=1e-13)
+        assert h[0, 0, 0] == pytest.approx(a ** T * start + dt * Bv * x * (1 - a ** T) / (1 - a), rel=1e-13)
+
+
+def test_pin_mamba_scan_splits_and_lengths():
+    """Scanning T1 tokens then T2 more from the stored state equals scanning
+    T1 + T2 at once; a row of length L < T is the scan of its first L tokens
+    and leaves y past L unwritten; padded rows touch nothing; T = 1 is the
+    decode step."""
+    rng = np.random.default_rng(41)
+    B, T, Dm, N = 3, 9, 5, 4
+    x, z = rng.standard_normal((B, T, Dm)), rng.standard_normal((B, T, Dm))
+    dt = rng.uniform(0.01, 0.2, (B, T, Dm))
+    A = -rng.uniform(0.5, 4.0, (Dm, N))
+    Bm, Cm = rng.standard_normal((B, T, N)), rng.standard_normal((B, T, N))
+    Dv = rng.standard_normal(Dm)
+    h0 = rng.standard_normal((4, Dm, N))
+    idx = [3, 0, 1]
+    hw = h0.copy()
+    yw = O.mamba_scan(x, dt, A, Bm, Cm, Dv, z, hw, idx)
+    hs = h0.copy()
+    y1 = O.mamba_scan(x[:, :4], dt[:, :4], A, Bm[:, :4], Cm[:, :4], Dv, z[:, :4], hs, idx)
+    y2 = O.mamba_scan(x[:, 4:], dt[:, 4:], A, Bm[:, 4:], Cm[:, 4:], Dv, z[:, 4:], hs, idx)
+    np.testing.assert_allclose(np.concatenate([y1, y2], axis=1), yw, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(hs, hw, rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(hw[2], h0[2])  # slot 2 is not named
+    hl = h0.copy()
+    yl = O.mamba_scan(x, dt, A, Bm, Cm, Dv, z, hl, idx, lengths=[9, 4, 0])
+    np.testing.assert_allclose(yl[0], yw[0], rtol=1e-12)
+    np.testing.assert_allclose(yl[1, :4], y1[1], rtol=1e-12)
+    assert np.isnan(yl[1, 4:]).all() and np.isnan(yl[2]).all()
+    np.testing.assert_allclose(hl[0], _state_by_steps(x, dt, A, Bm, Cm, Dv, z, h0, b=1, slot=0, L=4),
+                               rtol=1e-12)
+    np.testing.assert_array_equal(hl[1], h0[1])  # length 0: state unchanged
+    hp = h0.copy()
+    yp = O.mamba_scan(x, dt, A, Bm, Cm, Dv, z, hp, [-1, 4, 2])
+    assert np.isnan(yp[:2]).all()
+    np.testing.assert_array_equal(hp[[0, 1, 3]], h0[[0, 1, 3]])
+    h1, hstep = h0.copy(), h0.copy()
+    ys = O.mamba_scan(x[:, :1], dt[:, :1], A, Bm[:, :1], Cm[:, :1], Dv, z[:, :1], h1, idx)
+    yst = O.mamba_step(x[:, 0], dt[:, 0], A, Bm[:, 0], Cm[:, 0], Dv, z[:, 0], hstep, idx)
+    np.testing.assert_allclose(ys[:, 0], yst, rtol=1e-14)
+    np.testing.assert_allclose(h1, hstep, rtol=1e-14)
+
+
+def _state_by_steps(x, dt, A, Bm, Cm, Dv, z, h0, *, b, slot, L):
+    """State of row b (stored at slot) after its first L tokens, by L single
+    decode steps."""
+    h = h0.copy()
+    for t in range(L):
+        O.mamba_step(x[b:b + 1, t], dt[b:b + 1, t], A, Bm[b:b + 1, t], Cm[b:b + 1, t], Dv, z[b:b + 1, t], h, [slot])
+    return h[slot]
