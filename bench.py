@@ -434,6 +434,25 @@ def summarize_counters(fetch_dir, write_dir, out, command):
 
 
 # ------------------------------------------------------------ main
+def summarize_trace(trace_dir, out, command, title):
+    """Markdown table of rocprofv3's kernel statistics (run_kernel_stats.csv)."""
+    import csv
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    rows = list(csv.DictReader(open(files[0])))
+    cols = ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"]
+    lines = [f"# {title}", "", "Command (run from /tmp on the MI355X, `<repo>` = repository root):", "",
+             f"    {command}", "", "`run_kernel_stats.csv`:", "", "| " + " | ".join(cols) + " |",
+             "|" + "---|" * len(cols)]
+    for r in rows:
+        vals = [f"`{r['Name']}`"] + [r.get(c, "") for c in cols[1:]]
+        lines.append("| " + " | ".join(vals) + " |")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -443,12 +462,17 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="headline only (no sweep/buffered/KDA/conv/Mamba/copy)")
     ap.add_argument("--profile-pass", action="store_true")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
+    ap.add_argument("--title", default="")
     ap.add_argument("--out", default=COUNTERS_FILE)
     ap.add_argument("--command", default="")
     args = ap.parse_args()
 
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, args.out, args.command)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.out, args.command, args.title)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the decode step has no cross-GPU exchange and this build "
@@ -467,20 +491,20 @@ def main():
     torch.cuda.synchronize()
     h = headline(dev, args.steps, args.warmup)
     torch.cuda.synchronize()
+    print(f"[bench] headline done: {h['us']:.1f} us/step", file=sys.stderr, flush=True)
     extra = {"eager_us_per_step": round(h["us"], 3)}
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(h["setup"])
+        print("[bench] cpu_baseline done", file=sys.stderr, flush=True)
     del h["setup"]
     torch.cuda.empty_cache()
     if not args.no_extras:
-        extra["copy_ceiling"] = copy_ceiling(dev)
-        extra["graph_sweep"] = sweep(dev)
-        extra["buffered_b64"] = buffered(dev)
-        extra["kda_t64_h96"] = kda(dev)
-        extra["gdn_conv_b256"] = gdn_conv(dev)
-        extra["mamba1"] = mamba(dev)
-        extra["state16_b256"] = state16(dev)
+        for key, leg in (("copy_ceiling", copy_ceiling), ("graph_sweep", sweep), ("buffered_b64", buffered),
+                         ("kda_t64_h96", kda), ("gdn_conv_b256", gdn_conv), ("mamba1", mamba),
+                         ("state16_b256", state16)):
+            extra[key] = leg(dev)
+            print(f"[bench] {key} done", file=sys.stderr, flush=True)
         extra["state16_b256"]["speedup_vs_fp32_state"] = round(h["us"] / extra["state16_b256"]["us_per_step"], 3)
         extra["pct_of_copy_ceiling"] = round(100 * h["state_gbs"] / extra["copy_ceiling"]["GBps"], 2)
     w = h["w"]

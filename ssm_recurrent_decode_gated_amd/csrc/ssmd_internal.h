@@ -108,7 +108,7 @@ hipError_t launch_gdn_buffered(const GdnParams& p, const Launch& l, hipStream_t 
 hipError_t launch_kda(const KdaParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_gdn_conv(const GdnConvParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_mamba(const MambaParams& p, const Launch& l, hipStream_t s);
-hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, int n_cu, hipStream_t s);
 
 // Rows of one buffered-kernel tile, and the LDS its ring staging needs.
 int buffered_rows_per_tile(int K, int V, bool norm, const Launch& l);
