@@ -13,7 +13,8 @@
  * Conventions for every call:
  *   - Every pointer argument is a DEVICE pointer (memory of the current HIP
  *     device), except where stated. The caller allocates and owns all
- *     buffers; the library never allocates, frees or keeps a workspace.
+ *     buffers (mamba_scan's optional workspace included); the library never
+ *     allocates, frees or keeps memory between calls.
  *   - Work is enqueued asynchronously on `stream` (0 = the null stream). No
  *     call synchronises, reads device memory on the host or allocates, so
  *     every call can be captured into a HIP graph.
@@ -282,6 +283,43 @@ int mamba_decode_step(const void* x, const void* dt, const float* A,
                       int32_t B, int32_t Dm, int32_t N,
                       int32_t act_dtype, int32_t out_dtype,
                       hipStream_t stream);
+
+/*
+ * mamba_scan -- Mamba-1 over T tokens per row (prefill): the recurrence of
+ * mamba_decode_step applied to tokens 0..len-1 of each row in order, the
+ * state carried from token to token ([MBU] "Prefill path", a multi-token scan
+ * of the "Kernel design" recurrence). For every row b whose slot
+ * s = state_indices[b] is in [0, num_slots), with len = lengths[b] clamped to
+ * [0, T] (lengths NULL: len = T) and every channel d:
+ *   h = zero_init ? 0 : state[s, d, :]
+ *   for t < len:  h <- exp(dt[b,t,d] A[d,:]) h + dt[b,t,d] Bm[b,t,:] x[b,t,d]
+ *                 out[b,t,d] = (Cm[b,t,:] . h + Dvec[d] x[b,t,d]) * silu(z[b,t,d])
+ *                 (Dvec NULL: no skip term; z NULL: no gate)
+ *   state[s, d, :] = h
+ * out rows t >= len are not written; padded rows touch nothing.
+ *   x, dt, z [B, T, Dm] act_dtype;  Bm, Cm [B, T, N] act_dtype;
+ *   A [Dm, N] fp32 (16-byte aligned);  Dvec [Dm] fp32;
+ *   state [num_slots, Dm, N] fp32 (16-byte aligned), in place;
+ *   lengths [B] int32 or NULL;  out [B, T, Dm] out_dtype;
+ *   N in {16, 32, 64, 128, 256};  0 <= B <= 65535;  T >= 0.
+ * workspace (device, 16-byte aligned, caller-owned, contents don't-care on
+ * entry and exit) lets the scan split T into chunks that run in parallel
+ * (scan each chunk from zero, carry the chunk boundaries in order, rescan
+ * each chunk from its true start): mamba_scan_workspace_bytes() gives the
+ * size that reaches full parallelism on the current device. With less (or
+ * NULL / 0) the call uses as many chunks as fit, down to one sequential pass;
+ * the result is the same up to rounding.
+ */
+int64_t mamba_scan_workspace_bytes(int32_t B, int32_t T, int32_t Dm, int32_t N);
+int mamba_scan(const void* x, const void* dt, const float* A,
+               const void* Bm, const void* Cm, const float* Dvec,
+               const void* z, float* state, int32_t num_slots,
+               const int32_t* state_indices, const int32_t* lengths,
+               int32_t zero_init, void* out,
+               void* workspace, int64_t workspace_bytes,
+               int32_t B, int32_t T, int32_t Dm, int32_t N,
+               int32_t act_dtype, int32_t out_dtype,
+               hipStream_t stream);
 
 /* Message for the last non-zero status returned on this thread ("" if none). */
 const char* ssmd_last_error(void);

@@ -19,10 +19,12 @@ from ._binding import (  # noqa: F401
     kda_decode_step,
     load_library,
     mamba_decode_step,
+    mamba_scan,
+    mamba_scan_workspace_bytes,
     ssmd_last_error,
     ssmd_stream_copy,
 )
 
 __all__ = ["gdn_decode_step", "gdn_decode_step_state16", "gdn_decode_step_buffered", "gdn_decode_step_conv",
-           "kda_decode_step", "mamba_decode_step", "ssmd_last_error", "ssmd_stream_copy", "SsmdError",
-           "load_library"]
+           "kda_decode_step", "mamba_decode_step", "mamba_scan", "mamba_scan_workspace_bytes", "ssmd_last_error",
+           "ssmd_stream_copy", "SsmdError", "load_library"]

@@ -21,7 +21,8 @@ SSMD_ACT_SILU, SSMD_ACT_SIGMOID = 0, 1
 DTYPE_CODE = {torch.float32: SSMD_F32, torch.bfloat16: SSMD_BF16, torch.float16: SSMD_F16}
 ACT_CODE = {"silu": SSMD_ACT_SILU, "sigmoid": SSMD_ACT_SIGMOID}
 EXPORTS = ("gdn_decode_step", "gdn_decode_step_state16", "gdn_decode_step_buffered", "gdn_decode_step_conv",
-           "kda_decode_step", "mamba_decode_step", "ssmd_last_error", "ssmd_stream_copy")
+           "kda_decode_step", "mamba_decode_step", "mamba_scan", "mamba_scan_workspace_bytes", "ssmd_last_error",
+           "ssmd_stream_copy")
 
 
 class SsmdError(RuntimeError):
@@ -55,11 +56,15 @@ def load_library() -> ctypes.CDLL:
                                       _i32, _f, _p]
         L.mamba_decode_step.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _p, _i32, _i32, _i32,
                                         _i32, _i32, _p]
+        L.mamba_scan.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _p, _i32, _p, _p, _i64, _i32, _i32,
+                                 _i32, _i32, _i32, _i32, _p]
+        L.mamba_scan_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
         L.ssmd_stream_copy.argtypes = [_p, _p, _i64, _p]
         for f in EXPORTS:
             if f == "ssmd_last_error":
                 continue
             getattr(L, f).restype = ctypes.c_int
+        L.mamba_scan_workspace_bytes.restype = ctypes.c_int64
         L.ssmd_last_error.argtypes = []
         L.ssmd_last_error.restype = ctypes.c_char_p
         _LIB = L
@@ -308,6 +313,54 @@ def mamba_decode_step(x, dt, A, Bm, Cm, Dvec, z, state, state_indices, out, *, s
         _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dvec), _ptr(z), _ptr(state), num_slots,
         _ptr(state_indices), _ptr(out), B, Dm, N, DTYPE_CODE[act], DTYPE_CODE[out.dtype], _stream(state, stream))
     _check(rc, "mamba_decode_step")
+    return out
+
+
+def mamba_scan_workspace_bytes(B, T, Dm, N) -> int:
+    """Workspace bytes that let mamba_scan run fully chunk-parallel on the
+    current device (0: one pass is already enough)."""
+    n = load_library().mamba_scan_workspace_bytes(B, T, Dm, N)
+    if n < 0:
+        raise SsmdError(n, ssmd_last_error())
+    return n
+
+
+def mamba_scan(x, dt, A, Bm, Cm, Dvec, z, state, state_indices, out, *, lengths=None, zero_init=False,
+               workspace=None, stream=None):
+    """Mamba-1 over T tokens per row (prefill); see mamba_scan in
+    include/ssmdec.h. workspace: an optional device tensor (any dtype) of
+    scratch; mamba_scan_workspace_bytes() gives the size for full
+    parallelism."""
+    _dev(state, "state", torch.float32)
+    if state.dim() != 3:
+        raise ValueError("state must be [num_slots, D, N]")
+    num_slots, Dm, N = state.shape
+    _dev(x, "x", _ACTS)
+    if x.dim() != 3 or x.shape[2] != Dm:
+        raise ValueError("x must be [B, T, D]")
+    B, T = x.shape[0], x.shape[1]
+    act = x.dtype
+    _dev(dt, "dt", act, (B, T, Dm))
+    _dev(A, "A", torch.float32, (Dm, N))
+    _dev(Bm, "Bm", act, (B, T, N))
+    _dev(Cm, "Cm", act, (B, T, N))
+    if Dvec is not None:
+        _dev(Dvec, "Dvec", torch.float32, (Dm,))
+    if z is not None:
+        _dev(z, "z", act, (B, T, Dm))
+    _dev(state_indices, "state_indices", torch.int32, (B,))
+    if lengths is not None:
+        _dev(lengths, "lengths", torch.int32, (B,))
+    _dev(out, "out", _ACTS, (B, T, Dm))
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    rc = load_library().mamba_scan(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dvec), _ptr(z), _ptr(state), num_slots,
+        _ptr(state_indices), _ptr(lengths), int(bool(zero_init)), _ptr(out), _ptr(workspace), ws_bytes, B, T, Dm,
+        N, DTYPE_CODE[act], DTYPE_CODE[out.dtype], _stream(state, stream))
+    _check(rc, "mamba_scan")
     return out
 
 

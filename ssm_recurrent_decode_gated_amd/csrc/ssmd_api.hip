@@ -373,6 +373,70 @@ int mamba_decode_step(const void* x, const void* dt, const float* A, const void*
   return launch_status(ssmd::launch_mamba(p, launch_for(), stream), fn);
 }
 
+int64_t mamba_scan_workspace_bytes(int32_t B, int32_t T, int32_t Dm, int32_t N) {
+  const char* fn = "mamba_scan_workspace_bytes";
+  if (B < 0 || T < 0 || Dm < 1) return fail(SSMD_ERR_BAD_SHAPE, "%s: need B >= 0, T >= 0, D >= 1", fn);
+  if (!head_size_ok(N)) return fail(SSMD_ERR_UNSUPPORTED, "%s: N = %d not in {16,32,64,128,256}", fn, N);
+  int n_cu = 0;
+  if (int rc = cu_count(&n_cu)) return rc;
+  int Lc = 0, nck = 0;
+  ssmd::mamba_scan_chunking(B, T, Dm, N, n_cu, INT64_MAX, &Lc, &nck);
+  ok();
+  return nck > 1 ? 2LL * B * nck * Dm * N * 4 : 0;
+}
+
+int mamba_scan(const void* x, const void* dt, const float* A, const void* Bm, const void* Cm,
+               const float* Dvec, const void* z, float* state, int32_t num_slots,
+               const int32_t* state_indices, const int32_t* lengths, int32_t zero_init, void* out,
+               void* workspace, int64_t workspace_bytes, int32_t B, int32_t T, int32_t Dm, int32_t N,
+               int32_t act_dtype, int32_t out_dtype, hipStream_t stream) {
+  const char* fn = "mamba_scan";
+  if (B < 0 || B > 65535) return fail(SSMD_ERR_BAD_SHAPE, "%s: B = %d outside [0, 65535]", fn, B);
+  if (T < 0) return fail(SSMD_ERR_BAD_SHAPE, "%s: T = %d < 0", fn, T);
+  if (Dm < 1) return fail(SSMD_ERR_BAD_SHAPE, "%s: D = %d < 1", fn, Dm);
+  if (!head_size_ok(N)) return fail(SSMD_ERR_UNSUPPORTED, "%s: N = %d not in {16,32,64,128,256}", fn, N);
+  if (num_slots < 1) return fail(SSMD_ERR_BAD_SHAPE, "%s: num_slots = %d < 1", fn, num_slots);
+  if (!valid_dtype(act_dtype) || !valid_dtype(out_dtype))
+    return fail(SSMD_ERR_BAD_DTYPE, "%s: bad act/out dtype (%d, %d)", fn, act_dtype, out_dtype);
+  if (workspace_bytes < 0) return fail(SSMD_ERR_BAD_SHAPE, "%s: workspace_bytes < 0", fn);
+  if ((int64_t)T * Dm >= (1LL << 40)) return fail(SSMD_ERR_BAD_SHAPE, "%s: T*D too large", fn);
+  if (B == 0) return ok();
+  if (!A || !state || !state_indices) return fail(SSMD_ERR_NULL_ARG, "%s: A, state or state_indices is NULL", fn);
+  if (T > 0 && (!x || !dt || !Bm || !Cm || !out))
+    return fail(SSMD_ERR_NULL_ARG, "%s: x, dt, Bm, Cm or out is NULL", fn);
+  if (!aligned(A, 16) || !aligned(state, 16))
+    return fail(SSMD_ERR_BAD_SHAPE, "%s: A and state must be 16-byte aligned", fn);
+  if (workspace_bytes > 0 && (!workspace || !aligned(workspace, 16)))
+    return fail(SSMD_ERR_BAD_SHAPE, "%s: workspace must be a 16-byte aligned pointer when workspace_bytes > 0", fn);
+  int n_cu = 0;
+  if (int rc = cu_count(&n_cu)) return rc;
+  ssmd::MambaScanParams p{};
+  ssmd::mamba_scan_chunking(B, T, Dm, N, n_cu, workspace ? workspace_bytes : 0, &p.Lc, &p.nck);
+  if (p.nck > 65535) return fail(SSMD_ERR_BAD_SHAPE, "%s: too many chunks (%d)", fn, p.nck);
+  p.x = x;
+  p.dt = dt;
+  p.A = A;
+  p.Bm = Bm;
+  p.Cm = Cm;
+  p.Dvec = Dvec;
+  p.z = z;
+  p.state = state;
+  p.num_slots = num_slots;
+  p.idx = state_indices;
+  p.lengths = lengths;
+  p.zero_init = zero_init ? 1 : 0;
+  p.out = out;
+  p.ws_P = static_cast<float*>(workspace);
+  p.ws_h = p.nck > 1 ? p.ws_P + (int64_t)B * p.nck * Dm * N : nullptr;
+  p.B = B;
+  p.T = T;
+  p.Dm = Dm;
+  p.N = N;
+  p.act_dt = act_dtype;
+  p.out_dt = out_dtype;
+  return launch_status(ssmd::launch_mamba_scan(p, stream), fn);
+}
+
 int ssmd_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
   if (!src || !dst) return fail(SSMD_ERR_NULL_ARG, "ssmd_stream_copy: NULL pointer");
   if (bytes < 0 || bytes % 16) return fail(SSMD_ERR_BAD_SHAPE, "ssmd_stream_copy: bytes must be a multiple of 16");

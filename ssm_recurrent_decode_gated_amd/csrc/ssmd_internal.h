@@ -91,6 +91,28 @@ struct MambaParams {
   int32_t act_dt, out_dt;
 };
 
+// Mamba-1 scan over T tokens; ws_P / ws_h: [B][nck][Dm][N] fp32 each (nck > 1).
+struct MambaScanParams {
+  const void* x;
+  const void* dt;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dvec;
+  const void* z;
+  float* state;
+  int32_t num_slots;
+  const int32_t* idx;
+  const int32_t* lengths;
+  int32_t zero_init;
+  void* out;
+  float* ws_P;
+  float* ws_h;
+  int32_t B, T, Dm, N;
+  int32_t Lc, nck;  // chunk length (a multiple of 8) and chunk count
+  int32_t act_dt, out_dt;
+};
+
 // Launch shape of the state-streaming kernels, chosen on the host.
 struct Launch {
   int wpb;       // waves per workgroup
@@ -108,6 +130,10 @@ hipError_t launch_gdn_buffered(const GdnParams& p, const Launch& l, hipStream_t 
 hipError_t launch_kda(const KdaParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_gdn_conv(const GdnConvParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_mamba(const MambaParams& p, const Launch& l, hipStream_t s);
+hipError_t launch_mamba_scan(const MambaScanParams& p, hipStream_t s);
+// Chunking of a Mamba scan on a device of n_cu compute units with ws_bytes of
+// workspace: chunk length *Lc and count *nck (1 when ws_bytes is too small).
+void mamba_scan_chunking(int B, int T, int Dm, int N, int n_cu, int64_t ws_bytes, int* Lc, int* nck);
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, int n_cu, hipStream_t s);
 
 // Rows of one buffered-kernel tile, and the LDS its ring staging needs.

@@ -20,7 +20,7 @@ OK, NULL_ARG, BAD_SHAPE, BAD_DTYPE, UNSUPPORTED = 0, -1, -2, -3, -4
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(\w+)\(", text, re.M)))
+    return sorted(set(re.findall(r"^(?:int|int64_t|const char\*)\s+(\w+)\(", text, re.M)))
 
 
 def test_header_declares_the_entry_points():
@@ -173,3 +173,26 @@ def test_gdn_conv_host_validation():
     assert call(H=4, HV=64, V=512) == UNSUPPORTED  # (HV/H) V = 8192 outputs in one group
     assert call(HV=24) == BAD_SHAPE
     assert call(B=0, x=None, cw=None, cst=None) == OK
+
+
+def test_mamba_scan_host_validation():
+    L = S.load_library()
+
+    def call(B=2, T=64, Dm=256, N=16, x=0x10000, A=0x20000, state=0x30000, act=1, slots=2, ws=None, wsb=0):
+        return L.mamba_scan(x, 0x11000, A, 0x12000, 0x13000, None, None, state, slots, 0x14000, None, 0, 0x15000,
+                            ws, wsb, B, T, Dm, N, act, 1, None)
+    assert call(N=12) == UNSUPPORTED
+    assert call(Dm=0) == BAD_SHAPE
+    assert call(B=-1) == BAD_SHAPE
+    assert call(B=70000) == BAD_SHAPE
+    assert call(T=-1) == BAD_SHAPE
+    assert call(slots=0) == BAD_SHAPE
+    assert call(act=9) == BAD_DTYPE
+    assert call(x=None) == NULL_ARG
+    assert call(state=None) == NULL_ARG
+    assert call(A=0x20004) == BAD_SHAPE
+    assert call(wsb=-1) == BAD_SHAPE
+    assert call(ws=0x40008, wsb=4096) == BAD_SHAPE  # misaligned workspace
+    assert call(B=0, x=None, state=None) == OK
+    assert L.mamba_scan_workspace_bytes(1, 64, 256, 12) == UNSUPPORTED
+    assert L.mamba_scan_workspace_bytes(-1, 64, 256, 16) == BAD_SHAPE

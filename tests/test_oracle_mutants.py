@@ -43,8 +43,11 @@ MUTANTS = [
     ("ring stores unrounded delta", "dring[(size_t)p * V + r] = orc_round_fmt(delta[r], ring_fmt);",
      "dring[(size_t)p * V + r] = delta[r];"),
     ("16-bit state not rounded", "S[e] = orc_round_fmt(S[e], state_fmt);", "S[e] = S[e];"),
-    ("mamba drops input", "h[n] = dA * h[n] + dB * xv;", "h[n] = dA * h[n] + dB;"),
-    ("mamba no D skip", "acc += Dv[d] * xv;", "acc += Dv[d];"),
+    ("mamba drops input", "Bm[(size_t)bi * N + n];\n                h[n] = dA * h[n] + dB * xv;",
+     "Bm[(size_t)bi * N + n];\n                h[n] = dA * h[n] + dB;"),
+    ("mamba no D skip", "acc += Dv[d] * xv;\n            if (z)", "acc += Dv[d];\n            if (z)"),
+    ("scan drops input", "Bm[bt * N + n];\n                    h[n] = dA * h[n] + dB * xv;",
+     "Bm[bt * N + n];\n                    h[n] = dA * h[n] + dB;"),
     ("scan ignores stored state", "if (zero_init)\n                for (int n = 0; n < N; ++n)",
      "if (1)\n                for (int n = 0; n < N; ++n)"),
     ("scan drops last token", "for (int t = 0; t < len; ++t) {", "for (int t = 0; t < len - 1; ++t) {"),

@@ -214,3 +214,34 @@ def mamba_inputs(w: MambaWorkload, seed=0, act="f32") -> dict:
         "h": normal((w.num_slots, w.Dm, w.N), 1.0, "f32", g),
         "idx": torch.arange(w.B, dtype=torch.int32),
     }
+
+
+@dataclass(frozen=True)
+class MambaScanWorkload:
+    name: str
+    B: int
+    T: int
+    Dm: int
+    N: int
+    num_slots: int
+
+
+# the page's model width (d_inner 1536, N 16) over a 2048-token prompt
+MAMBA_PREFILL = MambaScanWorkload("mamba_prefill_b1_t2048_d1536_n16", B=1, T=2048, Dm=1536, N=16, num_slots=1)
+
+
+def mamba_scan_inputs(w: MambaScanWorkload, seed=0, act="bf16") -> dict:
+    """Prefill inputs: the decode recipe with a token axis (x, dt, z [B, T, D],
+    B, C [B, T, N]); slots are a seeded permutation of the pool's first B."""
+    g = generator(seed, w.name, "mamba_scan")
+    return {
+        "x": normal((w.B, w.T, w.Dm), 1.0, act, g),
+        "dt": uniform((w.B, w.T, w.Dm), 0.001, 0.1, g).to(DTYPES[act]),
+        "A": -uniform((w.Dm, w.N), 0.5, 16.0, g),
+        "Bm": normal((w.B, w.T, w.N), 1.0, act, g),
+        "Cm": normal((w.B, w.T, w.N), 1.0, act, g),
+        "Dv": normal((w.Dm,), 1.0, "f32", g),
+        "z": normal((w.B, w.T, w.Dm), 1.0, act, g),
+        "h": normal((w.num_slots, w.Dm, w.N), 1.0, "f32", g),
+        "idx": torch.randperm(w.num_slots, generator=g)[: w.B].to(torch.int32).contiguous(),
+    }
