@@ -326,6 +326,42 @@ def mamba(dev, reps=30):
     return res
 
 
+def mamba_prefill(dev, reps=20):
+    """Mamba-1 multi-token scan (mamba_scan), bf16 activations: one 2048-token
+    prompt at the page's model width (chunk-parallel with the workspace the
+    library asks for, and one sequential pass without), and 8 prompts at
+    once. Input sets are rotated so the replayed graph touches more than the
+    Infinity Cache holds. Bytes: x, dt, z read and y written (2 B each per
+    token and channel), B and C (2 B per token and state element), the state
+    read and written once."""
+    import torch
+    import ssm_recurrent_decode_gated_amd as S
+    import workloads as W
+    res = {}
+    for (B, T, Dm, N, chunked) in ((1, 2048, 1536, 16, True), (1, 2048, 1536, 16, False), (8, 2048, 1536, 16, True)):
+        w = W.MambaScanWorkload(f"mamba_prefill_b{B}_t{T}_d{Dm}_n{N}", B=B, T=T, Dm=Dm, N=N, num_slots=B)
+        d = W.mamba_scan_inputs(w)
+        alg = B * T * Dm * 8 + B * T * N * 4 + 2 * B * Dm * N * 4
+        M = _pools_for(alg)
+        sets = [{k: v.to(dev) for k, v in d.items()} for _ in range(M)]
+        out = torch.empty(B, T, Dm, dtype=torch.bfloat16, device=dev)
+        nws = S.mamba_scan_workspace_bytes(B, T, Dm, N) if chunked else 0
+        ws = torch.empty(max(nws // 4, 1), device=dev) if nws else None
+
+        def call(i):
+            s = sets[i]
+            S.mamba_scan(s["x"], s["dt"], s["A"], s["Bm"], s["Cm"], s["Dv"], s["z"], s["h"], s["idx"], out,
+                         workspace=ws)
+        us = graph_time_us([lambda i=i: call(i) for i in range(M)], reps, torch.cuda.current_stream())
+        key = f"B{B}_T{T}_D{Dm}_N{N}_" + ("chunked" if chunked else "single_pass")
+        res[key] = {"us_per_call": round(us, 2), "tokens_per_s": round(B * T / us * 1e6),
+                    "alg_GBps": round(alg / us / 1e3, 1), "workspace_bytes": nws, "sets": M,
+                    "exp_per_s_T": round(B * T * Dm * N / us / 1e6, 2)}
+        del sets, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(su, target_s=10.0):
     """The fp64 oracle, as it stands, on the host cores: the full B=256 step
     repeated (state evolving) until about target_s seconds have passed."""
@@ -501,7 +537,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_extras:
         for key, leg in (("copy_ceiling", copy_ceiling), ("graph_sweep", sweep), ("buffered_b64", buffered),
-                         ("kda_t64_h96", kda), ("gdn_conv_b256", gdn_conv), ("mamba1", mamba),
+                         ("kda_t64_h96", kda), ("gdn_conv_b256", gdn_conv), ("mamba1", mamba), ("mamba1_prefill", mamba_prefill),
                          ("state16_b256", state16)):
             extra[key] = leg(dev)
             print(f"[bench] {key} done", file=sys.stderr, flush=True)
