@@ -47,10 +47,12 @@ def configure(L: ctypes.CDLL) -> ctypes.CDLL:
     L.orc_kda_decode.argtypes = [_i] * 5 + [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _d,
                                             _dp, _ip, _dp, _dp, _dp, _d, _d, _i, _d, _dp]
     L.orc_mamba_step.argtypes = [_i] * 4 + [_dp] * 8 + [_ip, _dp]
+    L.orc_gdn_multi.argtypes = [_i] * 7 + [_dp, ctypes.c_long] + [_dp] * 5 + [_ip, _ip, _dp, _d, _i, _d, _dp, _dp,
+                                                                        _d, _i]
     L.orc_mamba_scan.argtypes = [_i] * 5 + [_dp] * 8 + [_ip, _ip, _i, _dp]
     L.orc_gdn_step_conv.argtypes = [_i] * 7 + [_dp] * 9 + [_ip, _dp, _d, _i, _d, _dp, _dp, _d, _i, _dp]
     for f in ("orc_gdn_step", "orc_gdn_step_buffered", "orc_conv1d_update", "orc_gdn_step_conv",
-              "orc_kda_step", "orc_kda_decode", "orc_mamba_step", "orc_mamba_scan", "orc_num_threads"):
+              "orc_kda_step", "orc_kda_decode", "orc_mamba_step", "orc_mamba_scan", "orc_gdn_multi", "orc_num_threads"):
         getattr(L, f).restype = _i
     return L
 
@@ -180,6 +182,26 @@ def gdn_step_buffered(qkv, a, b, A_log, dt_bias, state, idx, d_cache, k_cache, g
         B, H, HV, K, V, num_slots, _p(qkv), qkv.shape[1], _p(a), _p(b), _p(A_log),
         _p(dt_bias), _p(state), _p(idx), _p(out), scale, int(use_l2), l2eps, _p(ng), _p(nw),
         norm_eps, norm_act, _p(d_cache), _p(k_cache), _p(g_cache), _p(wp), L, ring_fmt))
+    return out
+
+
+def gdn_multi(qkv, a, b, A_log, dt_bias, state, idx, *, H, HV, K, V, lengths=None, scale=None, use_l2=True,
+              l2eps=1e-6, norm_gate=None, norm_weight=None, norm_eps=1e-5, norm_act=ACT_SILU):
+    """GDN over T tokens per row: qkv [B, T, C], a, b [B, T, HV], norm_gate
+    [B, T, HV, V]; state float64 [num_slots, HV, V, K] in place. Returns out
+    [B, T, HV, V] (NaN where not written)."""
+    qkv, a, b = f64(qkv), f64(a), f64(b)
+    A_log, dt_bias, idx = f64(A_log), f64(dt_bias), i32(idx)
+    B, T, C = qkv.shape
+    assert C == 2 * H * K + HV * V and a.shape == (B, T, HV) and b.shape == (B, T, HV)
+    ln = None if lengths is None else i32(lengths)
+    ng = None if norm_gate is None else f64(norm_gate)
+    nw = None if norm_weight is None else f64(norm_weight)
+    out = np.full((B, T, HV, V), np.nan)
+    scale = K ** -0.5 if scale is None else scale
+    _chk(lib().orc_gdn_multi(B, T, H, HV, K, V, state.shape[0], _p(qkv), C, _p(a), _p(b), _p(A_log),
+                             _p(dt_bias), _p(state), _p(idx), _p(ln), _p(out), scale, int(use_l2), l2eps, _p(ng),
+                             _p(nw), norm_eps, norm_act))
     return out
 
 

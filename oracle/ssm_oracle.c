@@ -250,6 +250,57 @@ int orc_gdn_step(int B, int H, int HV, int K, int V, int num_slots,
     return ORC_OK;
 }
 
+/* GDN over T tokens per sequence: the packed step above applied to tokens
+ * 0..len-1 of each row in order, the state carried from token to token (the
+ * recurrent form of [LOG] "Kernel 4" run over a token axis; [MBU] "Prefill
+ * path" for the multi-token use). Row b, token t reads mixed_qkv row
+ * b*T + t (stride qkv_stride), a/b [B][T][HV], norm_gate [B][T][HV][V], and
+ * writes out [B][T][HV][V]; tokens t >= len (lengths[b], clamped to [0, T];
+ * NULL: T) and padded rows write nothing. */
+int orc_gdn_multi(int B, int T, int H, int HV, int K, int V, int num_slots,
+                  const double *qkv, long qkv_stride, const double *a,
+                  const double *b, const double *A_log, const double *dt_bias,
+                  double *state, const int32_t *idx, const int32_t *lengths,
+                  double *out, double scale, int use_l2, double l2eps,
+                  const double *norm_gate, const double *norm_w, double norm_eps,
+                  int norm_act)
+{
+    if (B < 0 || T < 0)
+        return ORC_BAD;
+    int32_t *idx_t = malloc(sizeof(int32_t) * (size_t)(B > 0 ? B : 1));
+    double *a_t = malloc(sizeof(double) * ((size_t)B * HV + 1));
+    double *b_t = malloc(sizeof(double) * ((size_t)B * HV + 1));
+    double *ng_t = norm_gate ? malloc(sizeof(double) * ((size_t)B * HV * V + 1)) : NULL;
+    double *o_t = malloc(sizeof(double) * ((size_t)B * HV * V + 1));
+    int rc = ORC_OK;
+    for (int t = 0; t < T && rc == ORC_OK; ++t) {
+        for (int bi = 0; bi < B; ++bi) {
+            int len = lengths ? lengths[bi] : T;
+            len = len < 0 ? 0 : (len > T ? T : len);
+            idx_t[bi] = t < len ? idx[bi] : -1;
+            const size_t bt = (size_t)bi * T + t;
+            memcpy(a_t + (size_t)bi * HV, a + bt * HV, sizeof(double) * HV);
+            memcpy(b_t + (size_t)bi * HV, b + bt * HV, sizeof(double) * HV);
+            if (ng_t)
+                memcpy(ng_t + (size_t)bi * HV * V, norm_gate + bt * HV * V, sizeof(double) * HV * V);
+        }
+        rc = orc_gdn_step(B, H, HV, K, V, num_slots, qkv + (size_t)t * qkv_stride,
+                          qkv_stride * T, a_t, b_t, A_log, dt_bias, state, idx_t, o_t,
+                          scale, use_l2, l2eps, ng_t, norm_w, norm_eps, norm_act,
+                          ORC_FMT_NONE);
+        for (int bi = 0; bi < B; ++bi)
+            if (idx_t[bi] >= 0 && idx_t[bi] < num_slots)
+                memcpy(out + ((size_t)bi * T + t) * HV * V, o_t + (size_t)bi * HV * V,
+                       sizeof(double) * HV * V);
+    }
+    free(idx_t);
+    free(a_t);
+    free(b_t);
+    free(ng_t);
+    free(o_t);
+    return rc;
+}
+
 /* ------------------------------------------------------------------ */
 /* buffered (L-step write-back) GDN decode step                        */
 /* ------------------------------------------------------------------ */

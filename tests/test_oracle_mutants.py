@@ -53,6 +53,9 @@ MUTANTS = [
     ("scan drops last token", "for (int t = 0; t < len; ++t) {", "for (int t = 0; t < len - 1; ++t) {"),
     ("scan reads token-major B", "const double dB = dtv * Bm[bt * N + n];",
      "const double dB = dtv * Bm[((size_t)t * B + bi) * N + n];"),
+    ("multi reads token-major gates", "memcpy(a_t + (size_t)bi * HV, a + bt * HV, sizeof(double) * HV);",
+     "memcpy(a_t + (size_t)bi * HV, a + ((size_t)t * B + bi) * HV, sizeof(double) * HV);"),
+    ("multi ignores lengths", "idx_t[bi] = t < len ? idx[bi] : -1;", "idx_t[bi] = idx[bi];"),
     ("bf16 rounding truncates", "double r = nearbyint(x / ulp) * ulp;", "double r = trunc(x / ulp) * ulp;"),
 ]
 

@@ -600,3 +600,55 @@ def _state_by_steps(x, dt, A, Bm, Cm, Dv, z, h0, *, b, slot, L):
     for t in range(L):
         O.mamba_step(x[b:b + 1, t], dt[b:b + 1, t], A, Bm[b:b + 1, t], Cm[b:b + 1, t], Dv, z[b:b + 1, t], h, [slot])
     return h[slot]
+
+
+def _gdn_multi_inputs(seed, B, T, H, HV, K, V, slots):
+    rng = np.random.default_rng(seed)
+    C = 2 * H * K + HV * V
+    return dict(qkv=rng.standard_normal((B, T, C)), a=0.5 * rng.standard_normal((B, T, HV)),
+                b=rng.standard_normal((B, T, HV)), A_log=0.3 * rng.standard_normal(HV),
+                dt_bias=0.1 * rng.standard_normal(HV), gate=rng.standard_normal((B, T, HV, V)),
+                w=1 + 0.1 * rng.standard_normal(V), state=rng.standard_normal((slots, HV, V, K)))
+
+
+def test_pin_gdn_multi_is_token_by_token_steps():
+    """T tokens in one call equal T single steps on each token's slice (GQA,
+    gated norm, permuted slots), bit for bit."""
+    B, T, H, HV, K, V = 3, 5, 2, 4, 8, 6
+    d = _gdn_multi_inputs(50, B, T, H, HV, K, V, 4)
+    idx = [2, 0, 3]
+    st_m, st_s = d["state"].copy(), d["state"].copy()
+    om = O.gdn_multi(d["qkv"], d["a"], d["b"], d["A_log"], d["dt_bias"], st_m, idx, H=H, HV=HV, K=K, V=V,
+                     norm_gate=d["gate"], norm_weight=d["w"])
+    for t in range(T):
+        os_ = O.gdn_step(d["qkv"][:, t], d["a"][:, t], d["b"][:, t], d["A_log"], d["dt_bias"], st_s, idx,
+                         H=H, HV=HV, K=K, V=V, norm_gate=d["gate"][:, t], norm_weight=d["w"])
+        np.testing.assert_array_equal(om[:, t], os_)
+    np.testing.assert_array_equal(st_m, st_s)
+
+
+def test_pin_gdn_multi_lengths_padding_split():
+    """A row of length L < T is the first L tokens and writes nothing after;
+    a padded row touches nothing; T1 tokens then T2 more equal T1 + T2."""
+    B, T, H, HV, K, V = 4, 6, 1, 2, 4, 3
+    d = _gdn_multi_inputs(51, B, T, H, HV, K, V, 5)
+    idx = [4, -1, 1, 2]
+    lengths = [6, 6, 2, 0]
+    st = d["state"].copy()
+    o = O.gdn_multi(d["qkv"], d["a"], d["b"], d["A_log"], d["dt_bias"], st, idx, H=H, HV=HV, K=K, V=V,
+                    lengths=lengths)
+    assert np.isnan(o[1]).all() and np.isnan(o[2, 2:]).all() and np.isnan(o[3]).all()
+    for s_ in (0, 2, 3):
+        np.testing.assert_array_equal(st[s_], d["state"][s_])
+    st2 = d["state"].copy()
+    o2 = O.gdn_multi(d["qkv"][:, :2], d["a"][:, :2], d["b"][:, :2], d["A_log"], d["dt_bias"], st2, idx,
+                     H=H, HV=HV, K=K, V=V)
+    np.testing.assert_array_equal(o[2, :2], o2[2])
+    np.testing.assert_array_equal(st[1], st2[1])  # row 2 (slot 1) stopped after 2 tokens
+    st3 = d["state"].copy()
+    o3a = O.gdn_multi(d["qkv"][:, :4], d["a"][:, :4], d["b"][:, :4], d["A_log"], d["dt_bias"], st3, idx,
+                      H=H, HV=HV, K=K, V=V)
+    o3b = O.gdn_multi(d["qkv"][:, 4:], d["a"][:, 4:], d["b"][:, 4:], d["A_log"], d["dt_bias"], st3, idx,
+                      H=H, HV=HV, K=K, V=V)
+    np.testing.assert_array_equal(np.concatenate([o3a, o3b], axis=1)[0], o[0])
+    np.testing.assert_array_equal(st3[4], st[4])
