@@ -168,6 +168,39 @@ int gdn_decode_step_buffered(const void* mixed_qkv, int64_t qkv_row_stride,
                              hipStream_t stream);
 
 /*
+ * gdn_fused_recurrent -- the GDN step over T tokens per sequence: for every
+ * row b with slot s = ssm_state_indices[b] in [0, num_slots) and
+ * len = lengths[b] clamped to [0, T] (lengths NULL: len = T), tokens
+ * t = 0..len-1 are each one gdn_decode_step, in order, on the same state
+ * ([LOG] "Kernel 4: Fused DeltaNet Recurrent", Math, run over a token axis;
+ * the multi-token use of [MBU] "Prefill path"). The state is read and
+ * written once per call, not once per token; the result is that of len
+ * consecutive gdn_decode_step calls up to rounding. Tokens t >= len and
+ * padded rows write no output; a row with len = 0 leaves its state as it is.
+ *   mixed_qkv  [B*T rows, row stride qkv_row_stride >= 2*H*K + HV*V]
+ *              act_dtype; token t of row b is row b*T + t
+ *   a, b       [B, T, HV] act_dtype
+ *   out        [B, T, HV, V] out_dtype
+ *   norm_gate  [B, T, HV, V] act_dtype or NULL; with it V must not exceed
+ *              what one 8-wave block holds: 256 for K = 64 and 128, 128
+ *              for K = 16, 32 and 256
+ *   T >= 0. All other arguments, layouts and conventions are those of
+ *   gdn_decode_step.
+ */
+int gdn_fused_recurrent(const void* mixed_qkv, int64_t qkv_row_stride,
+                        const void* a, const void* b,
+                        const float* A_log, const float* dt_bias,
+                        float* state, int32_t num_slots,
+                        const int32_t* ssm_state_indices, const int32_t* lengths,
+                        void* out,
+                        int32_t B, int32_t T, int32_t H, int32_t HV, int32_t K, int32_t V,
+                        int32_t act_dtype, int32_t out_dtype,
+                        float scale, int32_t use_qk_l2norm, float l2norm_eps,
+                        const void* norm_gate, const float* norm_weight,
+                        float norm_eps, int32_t norm_act,
+                        hipStream_t stream);
+
+/*
  * gdn_decode_step_conv -- gdn_decode_step with the causal conv1d update + SiLU
  * of its q, k and v channels fused in front, in one launch (the fused op of
  * [KDA] module docstring and `triton_chain` applied to the GDN step; [LOG]

@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     gdn_decode_step,
     gdn_decode_step_buffered,
     gdn_decode_step_conv,
+    gdn_fused_recurrent,
     gdn_decode_step_state16,
     kda_decode_step,
     load_library,
@@ -26,5 +27,6 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = ["gdn_decode_step", "gdn_decode_step_state16", "gdn_decode_step_buffered", "gdn_decode_step_conv",
+           "gdn_fused_recurrent",
            "kda_decode_step", "mamba_decode_step", "mamba_scan", "mamba_scan_workspace_bytes", "ssmd_last_error",
            "ssmd_stream_copy", "SsmdError", "load_library"]

@@ -21,6 +21,7 @@ SSMD_ACT_SILU, SSMD_ACT_SIGMOID = 0, 1
 DTYPE_CODE = {torch.float32: SSMD_F32, torch.bfloat16: SSMD_BF16, torch.float16: SSMD_F16}
 ACT_CODE = {"silu": SSMD_ACT_SILU, "sigmoid": SSMD_ACT_SIGMOID}
 EXPORTS = ("gdn_decode_step", "gdn_decode_step_state16", "gdn_decode_step_buffered", "gdn_decode_step_conv",
+           "gdn_fused_recurrent",
            "kda_decode_step", "mamba_decode_step", "mamba_scan", "mamba_scan_workspace_bytes", "ssmd_last_error",
            "ssmd_stream_copy")
 
@@ -50,6 +51,7 @@ def load_library() -> ctypes.CDLL:
         L.gdn_decode_step.argtypes = _GDN_ARGS + [_p]
         L.gdn_decode_step_buffered.argtypes = _GDN_ARGS + [_p, _p, _p, _p, _i32, _p]
         L.gdn_decode_step_state16.argtypes = _GDN_ARGS[:7] + [_i32] + _GDN_ARGS[7:] + [_p]
+        L.gdn_fused_recurrent.argtypes = _GDN_ARGS[:9] + [_p] + _GDN_ARGS[9:11] + [_i32] + _GDN_ARGS[11:] + [_p]
         L.gdn_decode_step_conv.argtypes = [_p, _i64, _p, _p, _p, _i64, _i64, _i64, _i32] + _GDN_ARGS[2:] + [_p]
         L.kda_decode_step.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _f, _p, _i32,
                                       _p, _p, _p, _p, _f, _i32, _i32, _i32, _i32, _i32, _i32, _f,
@@ -201,6 +203,54 @@ def gdn_decode_step_buffered(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_i
         ACT_CODE[norm_act], _ptr(d_cache), _ptr(k_cache), _ptr(g_cache), _ptr(write_pos), L_,
         _stream(state, stream))
     _check(rc, "gdn_decode_step_buffered")
+    return out
+
+
+def gdn_fused_recurrent(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices, out, *, lengths=None, H=None,
+                        scale=None, use_qk_l2norm=True, l2norm_eps=1e-6, norm_gate=None, norm_weight=None,
+                        norm_eps=1e-5, norm_act="silu", stream=None):
+    """The GDN step over T tokens per row, state read and written once; see
+    gdn_fused_recurrent in include/ssmdec.h. mixed_qkv [B, T, C] with unit
+    column stride and its B*T rows evenly spaced (any row stride >= C);
+    a, b [B, T, HV]; out and norm_gate [B, T, HV, V]."""
+    _dev(state, "state", torch.float32)
+    if state.dim() != 4:
+        raise ValueError("state must be [num_slots, HV, V, K]")
+    num_slots, HV, V, K = state.shape
+    _dev(mixed_qkv, "mixed_qkv", _ACTS, contiguous=False)
+    if mixed_qkv.dim() != 3 or mixed_qkv.stride(2) != 1:
+        raise ValueError("mixed_qkv must be [B, T, C] with unit column stride")
+    B, T, C = mixed_qkv.shape
+    row_stride = mixed_qkv.stride(1) if T > 1 else mixed_qkv.stride(0)
+    if B > 1 and T > 1 and mixed_qkv.stride(0) != T * row_stride:
+        raise ValueError("mixed_qkv rows must be evenly spaced over the flattened B*T tokens")
+    if H is None:
+        qk = C - HV * V
+        if qk <= 0 or qk % (2 * K):
+            raise ValueError("cannot infer H from mixed_qkv width; pass H=")
+        H = qk // (2 * K)
+    if C != 2 * H * K + HV * V:
+        raise ValueError(f"mixed_qkv width {C} != 2*H*K + HV*V")
+    act = mixed_qkv.dtype
+    _dev(a, "a", act, (B, T, HV))
+    _dev(b, "b", act, (B, T, HV))
+    _dev(A_log, "A_log", torch.float32, (HV,))
+    _dev(dt_bias, "dt_bias", torch.float32, (HV,))
+    _dev(ssm_state_indices, "ssm_state_indices", torch.int32, (B,))
+    if lengths is not None:
+        _dev(lengths, "lengths", torch.int32, (B,))
+    _dev(out, "out", _ACTS, (B, T, HV, V))
+    if norm_gate is not None:
+        _dev(norm_gate, "norm_gate", act, (B, T, HV, V))
+    if norm_weight is not None:
+        _dev(norm_weight, "norm_weight", torch.float32, (V,))
+    scale = K ** -0.5 if scale is None else scale
+    rc = load_library().gdn_fused_recurrent(
+        _ptr(mixed_qkv), row_stride, _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(state), num_slots,
+        _ptr(ssm_state_indices), _ptr(lengths), _ptr(out), B, T, H, HV, K, V, DTYPE_CODE[act],
+        DTYPE_CODE[out.dtype], scale, int(bool(use_qk_l2norm)), l2norm_eps, _ptr(norm_gate), _ptr(norm_weight),
+        norm_eps, ACT_CODE[norm_act], _stream(state, stream))
+    _check(rc, "gdn_fused_recurrent")
     return out
 
 

@@ -281,6 +281,36 @@ int gdn_decode_step_conv(const void* x, int64_t x_row_stride, const float* conv_
   return launch_status(ssmd::launch_gdn_conv(cp, launch_for(), stream), fn);
 }
 
+int gdn_fused_recurrent(const void* mixed_qkv, int64_t qkv_row_stride, const void* a, const void* b,
+                        const float* A_log, const float* dt_bias, float* state, int32_t num_slots,
+                        const int32_t* ssm_state_indices, const int32_t* lengths, void* out, int32_t B,
+                        int32_t T, int32_t H, int32_t HV, int32_t K, int32_t V, int32_t act_dtype,
+                        int32_t out_dtype, float scale, int32_t use_qk_l2norm, float l2norm_eps,
+                        const void* norm_gate, const float* norm_weight, float norm_eps, int32_t norm_act,
+                        hipStream_t stream) {
+  const char* fn = "gdn_fused_recurrent";
+  if (T < 0) return fail(SSMD_ERR_BAD_SHAPE, "%s: T = %d < 0", fn, T);
+  if (B < 0) return fail(SSMD_ERR_BAD_SHAPE, "%s: B = %d < 0", fn, B);
+  const int64_t rows = (int64_t)B * T;
+  if (rows >= (1LL << 31)) return fail(SSMD_ERR_BAD_SHAPE, "%s: B*T too large", fn);
+  int rc = check_gdn(fn, mixed_qkv, qkv_row_stride, a, b, A_log, dt_bias, state, num_slots, ssm_state_indices,
+                     out, (int32_t)rows, H, HV, K, V, act_dtype, out_dtype, norm_gate, norm_act);
+  if (rc) return rc;
+  if (norm_gate && V > ssmd::gdn_multi_max_norm_rows(K))
+    return fail(SSMD_ERR_UNSUPPORTED, "%s: with the gated norm V = %d exceeds %d for K = %d", fn, V,
+                ssmd::gdn_multi_max_norm_rows(K), K);
+  if (rows == 0) return ok();
+  int n_cu = 0;
+  if (int rc2 = cu_count(&n_cu)) return rc2;
+  ssmd::GdnMultiParams mp{};
+  mp.g = gdn_params(mixed_qkv, qkv_row_stride, a, b, A_log, dt_bias, state, num_slots, ssm_state_indices, out, B,
+                    H, HV, K, V, act_dtype, out_dtype, scale, use_qk_l2norm, l2norm_eps, norm_gate, norm_weight,
+                    norm_eps, norm_act);
+  mp.T = T;
+  mp.lengths = lengths;
+  return launch_status(ssmd::launch_gdn_multi(mp, launch_for(), n_cu, stream), fn);
+}
+
 int kda_decode_step(const void* x, const float* conv_weight, const float* conv_bias, void* conv_state,
                     int64_t cs_slot_stride, int64_t cs_chan_stride, int64_t cs_tap_stride,
                     const void* raw_g, const void* raw_beta, const float* A_log, const float* dt_bias,

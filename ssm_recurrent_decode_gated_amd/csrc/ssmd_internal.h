@@ -37,6 +37,15 @@ struct GdnParams {
   int32_t L;
 };
 
+// GDN over T tokens per sequence: g.qkv / g.a / g.b / g.norm_gate / g.out
+// hold B*T token rows (token t of row b is row b*T + t).
+struct GdnMultiParams {
+  GdnParams g;
+  int32_t T;
+  const int32_t* lengths;  // [B] or NULL (all T)
+  int32_t tiles, rows_per_tile;  // set by the launcher
+};
+
 // GDN step with the causal conv1d update in front: g.qkv is the pre-conv row
 // x (stride g.qkv_stride); the conv state holds the last W - 1 inputs of each
 // channel in the activation dtype.
@@ -129,6 +138,9 @@ hipError_t launch_gdn_s16(const GdnParams& p, const Launch& l, int n_cu, hipStre
 hipError_t launch_gdn_buffered(const GdnParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_kda(const KdaParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_gdn_conv(const GdnConvParams& p, const Launch& l, hipStream_t s);
+hipError_t launch_gdn_multi(const GdnMultiParams& p, const Launch& l, int n_cu, hipStream_t s);
+// Largest V the multi-token kernel takes with the gated RMSNorm (one block per head).
+int gdn_multi_max_norm_rows(int K);
 hipError_t launch_mamba(const MambaParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_mamba_scan(const MambaScanParams& p, hipStream_t s);
 // Chunking of a Mamba scan on a device of n_cu compute units with ws_bytes of

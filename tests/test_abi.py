@@ -196,3 +196,19 @@ def test_mamba_scan_host_validation():
     assert call(B=0, x=None, state=None) == OK
     assert L.mamba_scan_workspace_bytes(1, 64, 256, 12) == UNSUPPORTED
     assert L.mamba_scan_workspace_bytes(-1, 64, 256, 16) == BAD_SHAPE
+
+
+def test_gdn_fused_recurrent_host_validation():
+    L = S.load_library()
+
+    def call(T=4, V=128, K=128, ng=None, B=8, qkv=0x10000, lengths=None):
+        return L.gdn_fused_recurrent(qkv, 2 * 16 * K + 32 * V, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000, 16, 0x70000, lengths,
+                                     0x80000, B, T, 16, 32, K, V, 1, 1, 0.088, 1, 1e-6, ng, None, 1e-5, 0, None)
+    assert call(T=-1) == BAD_SHAPE
+    assert call(B=-1) == BAD_SHAPE
+    assert call(K=48) == UNSUPPORTED
+    assert call(qkv=None) == NULL_ARG
+    assert call(ng=0x90000, V=512) == UNSUPPORTED   # the norm needs the head in one block
+    assert call(ng=0x90000, K=256, V=192) == UNSUPPORTED
+    assert call(T=0, qkv=None) == OK
+    assert call(B=0, qkv=None) == OK

@@ -1,0 +1,165 @@
+"""GPU parity of gdn_fused_recurrent (the GDN step over T tokens per row,
+state held in registers) against the fp64 oracle's token-by-token steps:
+outputs and final states to the fp32 tolerance (chained tolerance over long
+token runs), 16-bit outputs to one ulp, ragged lengths and padding touching
+nothing, and T = 1 equal to the packed step."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import ssm_recurrent_decode_gated_amd as S
+import workloads as W
+from tests._helpers import CHAIN_TOL, FP32_TOL, assert_16bit, assert_mixed, need_gpu
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TD = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def _inputs(w, T, seed=0, norm=False):
+    """T tokens per row: the GDN step recipe with a token axis."""
+    xs = [W.gdn_step_inputs(w, step=t, seed=seed, norm=norm) for t in range(T)]
+    d = {k: torch.stack([x[k] for x in xs], dim=1).contiguous() for k in ("qkv", "a", "b")}
+    if norm:
+        d["norm_gate"] = torch.stack([x["norm_gate"] for x in xs], dim=1).contiguous()
+        d["norm_weight"] = xs[0]["norm_weight"]
+    return d
+
+
+def _run(w, T, d, P, st, idx, *, out_dtype="bf16", lengths=None, norm=False, norm_act="silu", sentinel=7.0):
+    st_d = st.to(DEV)
+    out = torch.full((w.B, T, w.HV, w.V), sentinel, dtype=TD[out_dtype], device=DEV)
+    kw = {}
+    if norm:
+        kw = dict(norm_gate=d["norm_gate"].to(DEV), norm_weight=d["norm_weight"].to(DEV), norm_act=norm_act)
+    S.gdn_fused_recurrent(d["qkv"].to(DEV), d["a"].to(DEV), d["b"].to(DEV), P["A_log"].to(DEV),
+                          P["dt_bias"].to(DEV), st_d, idx.to(DEV), out,
+                          lengths=None if lengths is None else lengths.to(DEV), **kw)
+    ref = st.double().numpy().copy()
+    okw = {}
+    if norm:
+        okw = dict(norm_gate=d["norm_gate"], norm_weight=d["norm_weight"],
+                   norm_act=O.ACT_SIGMOID if norm_act == "sigmoid" else O.ACT_SILU)
+    ro = O.gdn_multi(d["qkv"], d["a"], d["b"], P["A_log"], P["dt_bias"], ref, idx, H=w.H, HV=w.HV, K=w.K, V=w.V,
+                     lengths=lengths, **okw)
+    torch.cuda.synchronize()
+    return out, st_d.cpu(), ro, ref
+
+
+def _check_out(out, ro, tol, what):
+    if out.dtype == torch.float32:
+        assert_mixed(out.cpu(), ro, tol, what)
+    else:
+        assert_16bit(out, ro, tol, what)
+
+
+def test_gdn_multi_b256_of_264_four_tokens():
+    """Verification of 4 speculative tokens at the bandwidth workload's size:
+    256 rows over a 264-slot pool, H=16, HV=32, K=V=128, bf16; every output
+    and state element; unnamed slots bit-identical."""
+    need_gpu()
+    w, T = W.GDN_B256, 4
+    P, idx, st = W.gdn_params(w), W.slot_indices(w), W.gdn_state(w)
+    d = _inputs(w, T)
+    out, got, ro, ref = _run(w, T, d, P, st, idx)
+    _check_out(out, ro, FP32_TOL, "outputs")
+    named = set(idx.tolist())
+    for s in range(w.num_slots):
+        if s in named:
+            assert_mixed(got[s], ref[s], FP32_TOL, f"slot {s}")
+        else:
+            assert torch.equal(got[s], st[s]), f"unnamed slot {s} changed"
+
+
+def test_gdn_multi_one_token_is_the_packed_step():
+    need_gpu()
+    w = W.GDN_B16
+    P, idx, st = W.gdn_params(w), W.slot_indices(w), W.gdn_state(w)
+    d = _inputs(w, 1)
+    out, got, ro, ref = _run(w, 1, d, P, st, idx, out_dtype="f32")
+    st_p = st.to(DEV)
+    out_p = torch.empty(w.B, 1, w.HV, w.V, device=DEV)
+    S.gdn_decode_step(d["qkv"][:, 0].to(DEV), d["a"][:, 0].to(DEV), d["b"][:, 0].to(DEV), P["A_log"].to(DEV),
+                      P["dt_bias"].to(DEV), st_p, idx.to(DEV), out_p)
+    torch.cuda.synchronize()
+    assert_mixed(out.cpu(), ro, FP32_TOL, "output vs oracle")
+    assert_mixed(out.cpu()[:, 0], out_p.cpu().double().numpy()[:, 0], FP32_TOL, "output vs packed step")
+    assert_mixed(got, st_p.cpu().double().numpy(), FP32_TOL, "state vs packed step")
+
+
+def test_gdn_multi_ragged_lengths_and_padding():
+    """Lengths 7, 3, 0, 1 and 7 (padded) over T = 7: tokens past a row's
+    length write nothing, a zero-length row keeps its state, a padded row
+    touches nothing."""
+    need_gpu()
+    w = W.GDNWorkload("gdn_multi_ragged", B=5, H=2, HV=4, K=128, V=128, num_slots=7, act="f32", out="f32")
+    T = 7
+    P, st = W.gdn_params(w), W.gdn_state(w)
+    d = _inputs(w, T)
+    idx = torch.tensor([4, 0, 6, 2, -1], dtype=torch.int32)
+    lengths = torch.tensor([7, 3, 0, 1, 7], dtype=torch.int32)
+    out, got, ro, ref = _run(w, T, d, P, st, idx, out_dtype="f32", lengths=lengths)
+    o = out.cpu()
+    for b in range(4):
+        L = int(lengths[b])
+        if L:
+            assert_mixed(o[b, :L], ro[b, :L], FP32_TOL, f"row {b}")
+        assert (o[b, L:] == 7.0).all(), f"row {b} wrote past its length"
+    assert (o[4] == 7.0).all()
+    for s in (4, 0, 2):
+        assert_mixed(got[s], ref[s], FP32_TOL, f"slot {s}")
+    for s in (1, 3, 5, 6):
+        assert torch.equal(got[s], st[s]), f"slot {s} changed"
+
+
+CASES = [
+    # name, B, H, HV, K, V, slots, act, out, T, norm
+    ("k16_v7_gqa2_f16", 5, 2, 4, 16, 7, 6, "f16", "f16", 6, None),
+    ("k32_v100_tiles_bf16", 3, 2, 2, 32, 100, 4, "bf16", "f32", 5, None),
+    ("k64_v256_norm_8waves", 2, 1, 2, 64, 256, 3, "bf16", "bf16", 4, "silu"),
+    ("k256_v64_gqa4_norm_sigmoid", 2, 1, 4, 256, 64, 3, "f32", "f32", 3, "sigmoid"),
+    ("k128_v200_gqa2_tiles", 3, 2, 4, 128, 200, 5, "bf16", "bf16", 5, None),
+    ("k128_v128_norm_gqa2", 4, 2, 4, 128, 128, 4, "bf16", "bf16", 8, "silu"),
+    ("k256_v300_tiles_f16", 1, 1, 1, 256, 300, 2, "f16", "f32", 4, None),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_gdn_multi_shapes(case):
+    """Every head size, ragged V split into row tiles, GQA 1/2/4, the gated
+    norm at 8 waves per head, every dtype."""
+    need_gpu()
+    name, B, H, HV, K, V, slots, act, outd, T, norm = case
+    w = W.GDNWorkload("gdn_multi_" + name, B=B, H=H, HV=HV, K=K, V=V, num_slots=slots, act=act, out=outd,
+                      idx="perm")
+    P, idx, st = W.gdn_params(w), W.slot_indices(w), W.gdn_state(w)
+    d = _inputs(w, T, norm=norm is not None)
+    out, got, ro, ref = _run(w, T, d, P, st, idx, out_dtype=outd, norm=norm is not None, norm_act=norm or "silu")
+    _check_out(out, ro, FP32_TOL, "outputs")
+    named = idx.tolist()
+    assert_mixed(got[named], ref[named], FP32_TOL, "states")
+
+
+def test_gdn_multi_256_tokens_and_split():
+    """A 256-token run (a short prompt) held in registers, against the
+    oracle's 256 steps at the chained tolerance; the same tokens in two calls
+    of 128 agree with one call."""
+    need_gpu()
+    w = W.GDNWorkload("gdn_multi_long", B=2, H=2, HV=4, K=128, V=128, num_slots=2, out="f32")
+    T = 256
+    P, idx, st = W.gdn_params(w), W.slot_indices(w), W.gdn_state(w)
+    d = _inputs(w, T)
+    out, got, ro, ref = _run(w, T, d, P, st, idx, out_dtype="f32")
+    assert_mixed(out.cpu(), ro, CHAIN_TOL, "outputs over 256 tokens")
+    assert_mixed(got, ref, CHAIN_TOL, "final state")
+    st2 = st.to(DEV)
+    halves = []
+    for lo in (0, 128):
+        oh = torch.empty(w.B, 128, w.HV, w.V, device=DEV)
+        S.gdn_fused_recurrent(*(d[k][:, lo:lo + 128].contiguous().to(DEV) for k in ("qkv", "a", "b")),
+                              P["A_log"].to(DEV), P["dt_bias"].to(DEV), st2, idx.to(DEV), oh)
+        halves.append(oh)
+    torch.cuda.synchronize()
+    assert_mixed(torch.cat(halves, dim=1).cpu(), out.cpu().double().numpy(), FP32_TOL, "two calls vs one")
+    assert_mixed(st2.cpu(), got.double().numpy(), FP32_TOL, "state, two calls vs one")
