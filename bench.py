@@ -326,6 +326,38 @@ def mamba(dev, reps=30):
     return res
 
 
+def gdn_multi(dev, reps=20):
+    """The GDN step over T tokens per row (gdn_fused_recurrent), bf16, H=16,
+    HV=32, K=V=128: verification of 4 and 8 speculative tokens at B=256 and
+    64 (one state round trip for all T tokens; compared with T packed steps),
+    and a 2048-token prompt at B=1. Pools rotated as in the sweep."""
+    import torch
+    import ssm_recurrent_decode_gated_amd as S
+    import workloads as W
+    res = {}
+    for (B, T) in ((256, 4), (64, 8), (1, 2048)):
+        w = W.gdn_sweep(B)
+        pool_bytes = w.num_slots * w.HV * w.V * w.K * 4
+        M = _pools_for(pool_bytes)
+        su = GDNSetup(w, M, dev)
+        g = W.generator(0, w.name, "multi", T)
+        C = 2 * w.H * w.K + w.HV * w.V
+        qkv = W.normal((B, T, C), 1.0, "bf16", g).to(dev)
+        a = W.normal((B, T, w.HV), 0.5, "bf16", g).to(dev)
+        b = W.normal((B, T, w.HV), 1.0, "bf16", g).to(dev)
+        out = torch.empty(B, T, w.HV, w.V, dtype=torch.bfloat16, device=dev)
+
+        def call(i):
+            S.gdn_fused_recurrent(qkv, a, b, su.A_log, su.dt_bias, su.pools[i], su.idx_d, out)
+        us = graph_time_us([lambda i=i: call(i) for i in range(M)], reps, torch.cuda.current_stream())
+        sb = gdn_state_bytes(B, w.HV, w.V, w.K)
+        res[f"B{B}_T{T}"] = {"us_per_call": round(us, 2), "tokens_per_s": round(B * T / us * 1e6),
+                             "state_GBps": round(sb / us / 1e3, 1), "pools": M}
+        del su, qkv, a, b, out
+        torch.cuda.empty_cache()
+    return res
+
+
 def mamba_prefill(dev, reps=20):
     """Mamba-1 multi-token scan (mamba_scan), bf16 activations: one 2048-token
     prompt at the page's model width (chunk-parallel with the workspace the
@@ -537,7 +569,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_extras:
         for key, leg in (("copy_ceiling", copy_ceiling), ("graph_sweep", sweep), ("buffered_b64", buffered),
-                         ("kda_t64_h96", kda), ("gdn_conv_b256", gdn_conv), ("mamba1", mamba), ("mamba1_prefill", mamba_prefill),
+                         ("kda_t64_h96", kda), ("gdn_conv_b256", gdn_conv), ("mamba1", mamba), ("mamba1_prefill", mamba_prefill), ("gdn_multi_token", gdn_multi),
                          ("state16_b256", state16)):
             extra[key] = leg(dev)
             print(f"[bench] {key} done", file=sys.stderr, flush=True)

@@ -296,6 +296,8 @@ int gdn_fused_recurrent(const void* mixed_qkv, int64_t qkv_row_stride, const voi
   int rc = check_gdn(fn, mixed_qkv, qkv_row_stride, a, b, A_log, dt_bias, state, num_slots, ssm_state_indices,
                      out, (int32_t)rows, H, HV, K, V, act_dtype, out_dtype, norm_gate, norm_act);
   if (rc) return rc;
+  if ((int64_t)T * qkv_row_stride >= (1LL << 31) || (int64_t)T * HV * V >= (1LL << 31))
+    return fail(SSMD_ERR_BAD_SHAPE, "%s: one row's T tokens exceed 2^31 elements", fn);
   if (norm_gate && V > ssmd::gdn_multi_max_norm_rows(K))
     return fail(SSMD_ERR_UNSUPPORTED, "%s: with the gated norm V = %d exceeds %d for K = %d", fn, V,
                 ssmd::gdn_multi_max_norm_rows(K), K);

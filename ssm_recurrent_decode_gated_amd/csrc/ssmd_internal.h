@@ -43,7 +43,7 @@ struct GdnMultiParams {
   GdnParams g;
   int32_t T;
   const int32_t* lengths;  // [B] or NULL (all T)
-  int32_t tiles, rows_per_tile;  // set by the launcher
+  int32_t tiles, rows_per_tile, tok_floats;  // set by the launcher
 };
 
 // GDN step with the causal conv1d update in front: g.qkv is the pre-conv row
