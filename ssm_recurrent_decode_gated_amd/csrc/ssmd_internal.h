@@ -137,6 +137,11 @@ hipError_t launch_gdn_pf(const GdnParams& p, const Launch& l, int n_cu, hipStrea
 hipError_t launch_gdn_s16(const GdnParams& p, const Launch& l, int n_cu, hipStream_t s);
 hipError_t launch_gdn_buffered(const GdnParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_kda(const KdaParams& p, const Launch& l, hipStream_t s);
+// Persistent prefetching form of the KDA op for head size 64/128, conv width
+// 4, A_log and dt_bias both given or both NULL (16-byte aligned conv weights
+// and dt_bias); kda_pf_supported says whether a call qualifies.
+bool kda_pf_supported(const KdaParams& p);
+hipError_t launch_kda_pf(const KdaParams& p, const Launch& l, int n_cu, hipStream_t s);
 hipError_t launch_gdn_conv(const GdnConvParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_gdn_multi(const GdnMultiParams& p, const Launch& l, int n_cu, hipStream_t s);
 // Largest V the multi-token kernel takes with the gated RMSNorm (one block per head).

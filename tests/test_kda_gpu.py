@@ -81,6 +81,9 @@ SMALL = [
     ("d16_w2_f16", 7, 3, 16, 2, "f16", torch.float16, True, True, False),
     ("d256_w4_bf16", 3, 2, 256, 4, "bf16", torch.float32, True, False, False),
     ("d128_w4_nonorm", 4, 5, 128, 4, "bf16", torch.bfloat16, False, False, False),
+    ("d128_w4_gates_norm_bias", 9, 3, 128, 4, "bf16", torch.bfloat16, True, True, True),
+    ("d64_w4_gates_f16", 6, 4, 64, 4, "f16", torch.float32, True, True, False),
+    ("d64_w4_f32_nonorm", 5, 2, 64, 4, "f32", torch.float32, False, False, True),
 ]
 
 
@@ -88,7 +91,9 @@ SMALL = [
 def test_kda_shapes_dtypes_options(case):
     """Every head size, conv widths 2-4, fp32/f16 activations (the conv state
     then is that dtype too), conv bias, norm on/off, and the A_log / dt_bias
-    gate form (a reading of the pages; parity against the oracle only)."""
+    gate form (a reading of the pages; parity against the oracle only); head
+    sizes 64 and 128 at width 4 run the persistent kernel, the rest the
+    per-unit one."""
     need_gpu()
     name, T, H, D, Wd, act, outd, norm, gates, bias = case
     w = W.KDAWorkload("kda_" + name, T=T, H=H, D=D, W=Wd, num_slots=T + 3)
@@ -109,4 +114,28 @@ def test_kda_shapes_dtypes_options(case):
         assert_16bit(out[act_t], ro[act_t], FP32_TOL, "output")
     slots = d["idx"].tolist()
     assert_mixed(st[slots], st_ref[slots], FP32_TOL, "state")
+    np.testing.assert_array_equal(cs.double().numpy(), cs_ref)
+
+
+def test_kda_many_tokens_with_skips_interleaved():
+    """More (token, head) units than persistent blocks, with NULL-slot and
+    out-of-range tokens interleaved: every block walks several units and
+    skips some between computed ones, and every computed output and state
+    still matches the oracle."""
+    need_gpu()
+    w = W.KDAWorkload("kda_interleaved_skips", T=600, H=2, D=128, num_slots=460)
+    d = W.kda_inputs(w)
+    idx = torch.arange(1, w.T + 1, dtype=torch.int32)
+    idx[::7] = 0                  # NULL block
+    idx[3::11] = w.num_slots + 5  # out of range
+    idx[idx > w.num_slots - 1] = -1
+    d["idx"] = idx
+    out, st, cs, ro, st_ref, cs_ref = _run_both(w, d)
+    act = _active(d["idx"], w.num_slots)
+    assert len(act) > 300 and len(act) < w.T
+    assert_16bit(out[act], ro[act], FP32_TOL, "active outputs")
+    skipped = [t for t in range(w.T) if t not in set(act)]
+    assert (out[skipped].float().cpu() == 7.0).all(), "a skipped token wrote output"
+    slots = sorted(set(d["idx"][act].tolist()))
+    assert_mixed(st[slots], st_ref[slots], FP32_TOL, "states of named slots")
     np.testing.assert_array_equal(cs.double().numpy(), cs_ref)
