@@ -31,19 +31,30 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 * 2 ** 20
+# What the headline kernel is built from: its source, the device header, and
+# the two parameter structs it takes (other declarations in that header do
+# not change it).
 KERNEL_SOURCES = ["ssm_recurrent_decode_gated_amd/csrc/gdn_decode_pf.hip",
-                  "ssm_recurrent_decode_gated_amd/csrc/ssmd_device.h",
-                  "ssm_recurrent_decode_gated_amd/csrc/ssmd_internal.h"]
+                  "ssm_recurrent_decode_gated_amd/csrc/ssmd_device.h"]
+KERNEL_STRUCTS = ("ssm_recurrent_decode_gated_amd/csrc/ssmd_internal.h", ("GdnParams", "Launch"))
 KERNEL_NAME = "gdn_decode_pf_kernel"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gdn_b256_of264_hbm_counters.txt")
 METRIC = "state GB/s (% of HBM peak) and µs/step, GDN decode HV=32 K=V=128, B=1/16/256"
 
 
 def kernel_source_hash() -> str:
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
+    rel, names = KERNEL_STRUCTS
+    text = open(os.path.join(ROOT, rel)).read()
+    for name in names:
+        m = re.search(r"^struct %s \{.*?^\};" % name, text, re.M | re.S)
+        if m is None:
+            raise SystemExit(f"struct {name} not found in {rel}")
+        h.update(m.group(0).encode())
     return h.hexdigest()[:16]
 
 
