@@ -369,6 +369,38 @@ def gdn_multi(dev, reps=20):
     return res
 
 
+def gdn_prefill(dev, reps=10):
+    """GDN prompts (H=16, HV=32, K=V=128, bf16) through the chunked form
+    (gdn_chunk_prefill, chunks of 64 tokens) and the sequential multi-token
+    kernel (gdn_fused_recurrent): one 2048-token prompt and 8 at once."""
+    import torch
+    import ssm_recurrent_decode_gated_amd as S
+    import workloads as W
+    res = {}
+    for (B, T) in ((1, 2048), (8, 2048)):
+        w = W.gdn_sweep(B)
+        su = GDNSetup(w, 2, dev)
+        g = W.generator(0, w.name, "prefill", T)
+        C = 2 * w.H * w.K + w.HV * w.V
+        qkv = W.normal((B, T, C), 1.0, "bf16", g).to(dev)
+        a = W.normal((B, T, w.HV), 0.5, "bf16", g).to(dev)
+        b = W.normal((B, T, w.HV), 1.0, "bf16", g).to(dev)
+        out = torch.empty(B, T, w.HV, w.V, dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(S.gdn_chunk_workspace_bytes(B, T, w.HV, w.K, w.V) // 4, device=dev)
+        r = {}
+        for name, fn, kw in (("chunked", S.gdn_chunk_prefill, {"workspace": ws}),
+                             ("sequential", S.gdn_fused_recurrent, {})):
+            def call(i, fn=fn, kw=kw):
+                fn(qkv, a, b, su.A_log, su.dt_bias, su.pools[i], su.idx_d, out, **kw)
+            us = graph_time_us([lambda i=i: call(i) for i in range(2)], reps, torch.cuda.current_stream())
+            r[name] = {"us_per_call": round(us, 1), "tokens_per_s": round(B * T / us * 1e6)}
+        r["workspace_bytes"] = ws.numel() * 4
+        res[f"B{B}_T{T}"] = r
+        del su, qkv, a, b, out, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def mamba_prefill(dev, reps=20):
     """Mamba-1 multi-token scan (mamba_scan), bf16 activations: one 2048-token
     prompt at the page's model width (chunk-parallel with the workspace the
@@ -580,7 +612,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_extras:
         for key, leg in (("copy_ceiling", copy_ceiling), ("graph_sweep", sweep), ("buffered_b64", buffered),
-                         ("kda_t64_h96", kda), ("gdn_conv_b256", gdn_conv), ("mamba1", mamba), ("mamba1_prefill", mamba_prefill), ("gdn_multi_token", gdn_multi),
+                         ("kda_t64_h96", kda), ("gdn_conv_b256", gdn_conv), ("mamba1", mamba), ("mamba1_prefill", mamba_prefill), ("gdn_multi_token", gdn_multi), ("gdn_prefill", gdn_prefill),
                          ("state16_b256", state16)):
             extra[key] = leg(dev)
             print(f"[bench] {key} done", file=sys.stderr, flush=True)

@@ -201,6 +201,36 @@ int gdn_fused_recurrent(const void* mixed_qkv, int64_t qkv_row_stride,
                         hipStream_t stream);
 
 /*
+ * gdn_chunk_prefill -- what gdn_fused_recurrent computes (the GDN step over T
+ * tokens per row, state read and written once), in chunked form for long
+ * sequences: tokens in chunks of 64, each chunk's effect reduced to dense
+ * products (a unit lower-triangular solve, W = Tm e^gamma k, U = Tm v) that
+ * run in parallel over chunks, then one pass per 16 state rows walks the
+ * chunks in order (Delta = U - W S^T, o = e^gamma q S^T + P Delta, S <-
+ * e^gamma_C S + Delta e^(gamma_C - gamma) k). [LOG] "Kernel 4: Fused DeltaNet
+ * Recurrent", Math, unrolled over a chunk; [MBU] "Prefill path". The result
+ * equals that of gdn_fused_recurrent up to rounding.
+ *   Arguments, layouts and conventions: those of gdn_fused_recurrent, plus
+ *   workspace (device, 16-byte aligned, caller-owned, contents don't-care
+ *   on entry and exit) of at least gdn_chunk_workspace_bytes(B, T, HV, K, V,
+ *   norm_gate != NULL) bytes. K in {64, 128}; V a multiple of 16, <= 256.
+ */
+int64_t gdn_chunk_workspace_bytes(int32_t B, int32_t T, int32_t HV, int32_t K, int32_t V, int32_t with_norm);
+int gdn_chunk_prefill(const void* mixed_qkv, int64_t qkv_row_stride,
+                      const void* a, const void* b,
+                      const float* A_log, const float* dt_bias,
+                      float* state, int32_t num_slots,
+                      const int32_t* ssm_state_indices, const int32_t* lengths,
+                      void* out,
+                      int32_t B, int32_t T, int32_t H, int32_t HV, int32_t K, int32_t V,
+                      int32_t act_dtype, int32_t out_dtype,
+                      float scale, int32_t use_qk_l2norm, float l2norm_eps,
+                      const void* norm_gate, const float* norm_weight,
+                      float norm_eps, int32_t norm_act,
+                      void* workspace, int64_t workspace_bytes,
+                      hipStream_t stream);
+
+/*
  * gdn_decode_step_conv -- gdn_decode_step with the causal conv1d update + SiLU
  * of its q, k and v channels fused in front, in one launch (the fused op of
  * [KDA] module docstring and `triton_chain` applied to the GDN step; [LOG]

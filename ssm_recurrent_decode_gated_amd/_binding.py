@@ -21,7 +21,7 @@ SSMD_ACT_SILU, SSMD_ACT_SIGMOID = 0, 1
 DTYPE_CODE = {torch.float32: SSMD_F32, torch.bfloat16: SSMD_BF16, torch.float16: SSMD_F16}
 ACT_CODE = {"silu": SSMD_ACT_SILU, "sigmoid": SSMD_ACT_SIGMOID}
 EXPORTS = ("gdn_decode_step", "gdn_decode_step_state16", "gdn_decode_step_buffered", "gdn_decode_step_conv",
-           "gdn_fused_recurrent",
+           "gdn_fused_recurrent", "gdn_chunk_prefill", "gdn_chunk_workspace_bytes",
            "kda_decode_step", "mamba_decode_step", "mamba_scan", "mamba_scan_workspace_bytes", "ssmd_last_error",
            "ssmd_stream_copy")
 
@@ -52,6 +52,8 @@ def load_library() -> ctypes.CDLL:
         L.gdn_decode_step_buffered.argtypes = _GDN_ARGS + [_p, _p, _p, _p, _i32, _p]
         L.gdn_decode_step_state16.argtypes = _GDN_ARGS[:7] + [_i32] + _GDN_ARGS[7:] + [_p]
         L.gdn_fused_recurrent.argtypes = _GDN_ARGS[:9] + [_p] + _GDN_ARGS[9:11] + [_i32] + _GDN_ARGS[11:] + [_p]
+        L.gdn_chunk_prefill.argtypes = L.gdn_fused_recurrent.argtypes[:-1] + [_p, _i64, _p]
+        L.gdn_chunk_workspace_bytes.argtypes = [_i32] * 6
         L.gdn_decode_step_conv.argtypes = [_p, _i64, _p, _p, _p, _i64, _i64, _i64, _i32] + _GDN_ARGS[2:] + [_p]
         L.kda_decode_step.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _f, _p, _i32,
                                       _p, _p, _p, _p, _f, _i32, _i32, _i32, _i32, _i32, _i32, _f,
@@ -67,6 +69,7 @@ def load_library() -> ctypes.CDLL:
                 continue
             getattr(L, f).restype = ctypes.c_int
         L.mamba_scan_workspace_bytes.restype = ctypes.c_int64
+        L.gdn_chunk_workspace_bytes.restype = ctypes.c_int64
         L.ssmd_last_error.argtypes = []
         L.ssmd_last_error.restype = ctypes.c_char_p
         _LIB = L
@@ -206,13 +209,8 @@ def gdn_decode_step_buffered(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_i
     return out
 
 
-def gdn_fused_recurrent(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices, out, *, lengths=None, H=None,
-                        scale=None, use_qk_l2norm=True, l2norm_eps=1e-6, norm_gate=None, norm_weight=None,
-                        norm_eps=1e-5, norm_act="silu", stream=None):
-    """The GDN step over T tokens per row, state read and written once; see
-    gdn_fused_recurrent in include/ssmdec.h. mixed_qkv [B, T, C] with unit
-    column stride and its B*T rows evenly spaced (any row stride >= C);
-    a, b [B, T, HV]; out and norm_gate [B, T, HV, V]."""
+def _gdn_multi_args(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices, out, lengths, H, norm_gate,
+                    norm_weight):
     _dev(state, "state", torch.float32)
     if state.dim() != 4:
         raise ValueError("state must be [num_slots, HV, V, K]")
@@ -244,6 +242,18 @@ def gdn_fused_recurrent(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indice
         _dev(norm_gate, "norm_gate", act, (B, T, HV, V))
     if norm_weight is not None:
         _dev(norm_weight, "norm_weight", torch.float32, (V,))
+    return B, T, H, HV, K, V, num_slots, row_stride, act
+
+
+def gdn_fused_recurrent(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices, out, *, lengths=None, H=None,
+                        scale=None, use_qk_l2norm=True, l2norm_eps=1e-6, norm_gate=None, norm_weight=None,
+                        norm_eps=1e-5, norm_act="silu", stream=None):
+    """The GDN step over T tokens per row, state read and written once; see
+    gdn_fused_recurrent in include/ssmdec.h. mixed_qkv [B, T, C] with unit
+    column stride and its B*T rows evenly spaced (any row stride >= C);
+    a, b [B, T, HV]; out and norm_gate [B, T, HV, V]."""
+    B, T, H, HV, K, V, num_slots, row_stride, act = _gdn_multi_args(
+        mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices, out, lengths, H, norm_gate, norm_weight)
     scale = K ** -0.5 if scale is None else scale
     rc = load_library().gdn_fused_recurrent(
         _ptr(mixed_qkv), row_stride, _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(state), num_slots,
@@ -251,6 +261,37 @@ def gdn_fused_recurrent(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indice
         DTYPE_CODE[out.dtype], scale, int(bool(use_qk_l2norm)), l2norm_eps, _ptr(norm_gate), _ptr(norm_weight),
         norm_eps, ACT_CODE[norm_act], _stream(state, stream))
     _check(rc, "gdn_fused_recurrent")
+    return out
+
+
+def gdn_chunk_workspace_bytes(B, T, HV, K, V, with_norm=False) -> int:
+    n = load_library().gdn_chunk_workspace_bytes(B, T, HV, K, V, int(bool(with_norm)))
+    if n < 0:
+        raise SsmdError(n, ssmd_last_error())
+    return n
+
+
+def gdn_chunk_prefill(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices, out, *, workspace=None,
+                      lengths=None, H=None, scale=None, use_qk_l2norm=True, l2norm_eps=1e-6, norm_gate=None,
+                      norm_weight=None, norm_eps=1e-5, norm_act="silu", stream=None):
+    """gdn_fused_recurrent's result in chunked form (long sequences); see
+    gdn_chunk_prefill in include/ssmdec.h. workspace: a device tensor of at
+    least gdn_chunk_workspace_bytes(...) bytes; when None, one is allocated
+    with torch for this call."""
+    B, T, H, HV, K, V, num_slots, row_stride, act = _gdn_multi_args(
+        mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices, out, lengths, H, norm_gate, norm_weight)
+    need = gdn_chunk_workspace_bytes(B, T, HV, K, V, norm_gate is not None)
+    if workspace is None:
+        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=state.device)
+    _dev(workspace, "workspace")
+    scale = K ** -0.5 if scale is None else scale
+    rc = load_library().gdn_chunk_prefill(
+        _ptr(mixed_qkv), row_stride, _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(state), num_slots,
+        _ptr(ssm_state_indices), _ptr(lengths), _ptr(out), B, T, H, HV, K, V, DTYPE_CODE[act],
+        DTYPE_CODE[out.dtype], scale, int(bool(use_qk_l2norm)), l2norm_eps, _ptr(norm_gate), _ptr(norm_weight),
+        norm_eps, ACT_CODE[norm_act], _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(state, stream))
+    _check(rc, "gdn_chunk_prefill")
     return out
 
 

@@ -313,6 +313,48 @@ int gdn_fused_recurrent(const void* mixed_qkv, int64_t qkv_row_stride, const voi
   return launch_status(ssmd::launch_gdn_multi(mp, launch_for(), n_cu, stream), fn);
 }
 
+int64_t gdn_chunk_workspace_bytes(int32_t B, int32_t T, int32_t HV, int32_t K, int32_t V, int32_t with_norm) {
+  if (B < 0 || T < 0 || HV < 1 || V < 1) return fail(SSMD_ERR_BAD_SHAPE, "gdn_chunk_workspace_bytes: bad sizes");
+  ok();
+  return 4 * ssmd::gdn_chunk_workspace_floats(B, T, HV, K, V, with_norm != 0);
+}
+
+int gdn_chunk_prefill(const void* mixed_qkv, int64_t qkv_row_stride, const void* a, const void* b,
+                      const float* A_log, const float* dt_bias, float* state, int32_t num_slots,
+                      const int32_t* ssm_state_indices, const int32_t* lengths, void* out, int32_t B,
+                      int32_t T, int32_t H, int32_t HV, int32_t K, int32_t V, int32_t act_dtype,
+                      int32_t out_dtype, float scale, int32_t use_qk_l2norm, float l2norm_eps,
+                      const void* norm_gate, const float* norm_weight, float norm_eps, int32_t norm_act,
+                      void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "gdn_chunk_prefill";
+  if (T < 0) return fail(SSMD_ERR_BAD_SHAPE, "%s: T = %d < 0", fn, T);
+  if (B < 0) return fail(SSMD_ERR_BAD_SHAPE, "%s: B = %d < 0", fn, B);
+  const int64_t rows = (int64_t)B * T;
+  if (rows >= (1LL << 31)) return fail(SSMD_ERR_BAD_SHAPE, "%s: B*T too large", fn);
+  int rc = check_gdn(fn, mixed_qkv, qkv_row_stride, a, b, A_log, dt_bias, state, num_slots, ssm_state_indices,
+                     out, (int32_t)rows, H, HV, K, V, act_dtype, out_dtype, norm_gate, norm_act);
+  if (rc) return rc;
+  if (K != 64 && K != 128) return fail(SSMD_ERR_UNSUPPORTED, "%s: K = %d not in {64, 128}", fn, K);
+  if (V % 16 || V > 256) return fail(SSMD_ERR_UNSUPPORTED, "%s: V = %d must be a multiple of 16, <= 256", fn, V);
+  if (rows == 0) return ok();
+  const int64_t need = 4 * ssmd::gdn_chunk_workspace_floats(B, T, HV, K, V, norm_gate != nullptr);
+  if (!workspace || workspace_bytes < need)
+    return fail(SSMD_ERR_BAD_SHAPE, "%s: workspace of %lld bytes needed (got %lld)", fn, (long long)need,
+                (long long)workspace_bytes);
+  if (!aligned(workspace, 16)) return fail(SSMD_ERR_BAD_SHAPE, "%s: workspace must be 16-byte aligned", fn);
+  if ((int64_t)B * HV * ((T + 63) / 64) >= (1LL << 31)) return fail(SSMD_ERR_BAD_SHAPE, "%s: too many chunks", fn);
+  ssmd::GdnChunkParams cp{};
+  cp.g = gdn_params(mixed_qkv, qkv_row_stride, a, b, A_log, dt_bias, state, num_slots, ssm_state_indices, out, B,
+                    H, HV, K, V, act_dtype, out_dtype, scale, use_qk_l2norm, l2norm_eps, norm_gate, norm_weight,
+                    norm_eps, norm_act);
+  cp.T = T;
+  cp.lengths = lengths;
+  cp.nck = (T + 63) / 64;
+  cp.ws = static_cast<float*>(workspace);
+  cp.obuf = norm_gate ? cp.ws + (ssmd::gdn_chunk_workspace_floats(B, T, HV, K, V, false)) : nullptr;
+  return launch_status(ssmd::launch_gdn_chunk(cp, stream), fn);
+}
+
 int kda_decode_step(const void* x, const float* conv_weight, const float* conv_bias, void* conv_state,
                     int64_t cs_slot_stride, int64_t cs_chan_stride, int64_t cs_tap_stride,
                     const void* raw_g, const void* raw_beta, const float* A_log, const float* dt_bias,

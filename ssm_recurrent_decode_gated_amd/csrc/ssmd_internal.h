@@ -46,6 +46,17 @@ struct GdnMultiParams {
   int32_t tiles, rows_per_tile, tok_floats;  // set by the launcher
 };
 
+// Chunked GDN over T tokens: ws holds one record per (row, value head,
+// chunk of 64 tokens), then (gated norm only) fp32 outputs [B][T][HV][V] at obuf.
+struct GdnChunkParams {
+  GdnParams g;
+  int32_t T;
+  const int32_t* lengths;
+  int32_t nck;
+  float* ws;
+  float* obuf;
+};
+
 // GDN step with the causal conv1d update in front: g.qkv is the pre-conv row
 // x (stride g.qkv_stride); the conv state holds the last W - 1 inputs of each
 // channel in the activation dtype.
@@ -144,6 +155,8 @@ bool kda_pf_supported(const KdaParams& p);
 hipError_t launch_kda_pf(const KdaParams& p, const Launch& l, int n_cu, hipStream_t s);
 hipError_t launch_gdn_conv(const GdnConvParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_gdn_multi(const GdnMultiParams& p, const Launch& l, int n_cu, hipStream_t s);
+hipError_t launch_gdn_chunk(const GdnChunkParams& p, hipStream_t s);
+int64_t gdn_chunk_workspace_floats(int B, int T, int HV, int K, int V, bool norm);
 // Largest V the multi-token kernel takes with the gated RMSNorm (one block per head).
 int gdn_multi_max_norm_rows(int K);
 hipError_t launch_mamba(const MambaParams& p, const Launch& l, hipStream_t s);

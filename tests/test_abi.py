@@ -212,3 +212,22 @@ def test_gdn_fused_recurrent_host_validation():
     assert call(ng=0x90000, K=256, V=192) == UNSUPPORTED
     assert call(T=0, qkv=None) == OK
     assert call(B=0, qkv=None) == OK
+
+
+def test_gdn_chunk_prefill_host_validation():
+    L = S.load_library()
+
+    def call(K=128, V=128, ws=0x90000, wsb=1 << 30, T=128, B=2):
+        return L.gdn_chunk_prefill(0x10000, 2 * 16 * K + 32 * V, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000, 16,
+                                   0x70000, None, 0x80000, B, T, 16, 32, K, V, 1, 1, 0.088, 1, 1e-6, None, None, 1e-5,
+                                   0, ws, wsb, None)
+    assert call(K=32) == UNSUPPORTED
+    assert call(V=120) == UNSUPPORTED
+    assert call(V=512) == BAD_SHAPE or call(V=512) == UNSUPPORTED
+    assert call(ws=None) == BAD_SHAPE
+    assert call(wsb=1024) == BAD_SHAPE
+    assert call(ws=0x90004) == BAD_SHAPE
+    assert call(T=0, ws=None) == OK
+    need = L.gdn_chunk_workspace_bytes(2, 128, 32, 128, 128, 0)
+    assert need == 4 * 2 * 32 * 2 * (3 * 64 * 128 + 64 * 128 + 64 * 64 + 4)
+    assert L.gdn_chunk_workspace_bytes(2, 128, 32, 128, 128, 1) == need + 4 * 2 * 128 * 32 * 128
