@@ -23,7 +23,8 @@
 //      per-chunk operands are read from that XCD's L2.
 // With the gated RMSNorm (over a token's V outputs, split across tiles) pass
 // 2 writes fp32 outputs to the workspace and a third pass normalises them.
-// All arithmetic is fp32 (the products are small dense ones on the VALU).
+// All arithmetic is fp32; the dense products run on the matrix cores
+// (v_mfma_f32_16x16x4_f32), the triangular solve on the VALU.
 #include "ssmd_device.h"
 #include "ssmd_internal.h"
 
@@ -32,27 +33,77 @@ namespace ssmd {
 constexpr int GCH = 64;  // tokens per chunk
 constexpr int GCH_VT = 16;  // state rows per pass-2 block
 
-// Per (row, value head, chunk) workspace record, in floats.
+// Per (row, value head, chunk) workspace record, in floats:
+//   W [64][K] | U [64][V] | e^gamma q [64][K] | (e^(gamma_C - gamma) k)^T [K][64] | P [64][64] | gamma_C
 __host__ __device__ inline int64_t gch_rec_floats(int K, int V) {
   return 3LL * GCH * K + (int64_t)GCH * V + GCH * GCH + 4;
 }
 
-template <int K, int ACT>
+// The dense products run on the matrix cores: v_mfma_f32_16x16x4_f32 (fp32
+// in and out). Lane l = x + 16 kk supplies A[x][k] and B[k][x] for one k of
+// each step and holds D[4 kk + r][x] in register r. Four steps cover 16
+// contraction indices; step e takes index k0 + 4 kk + e on lane group kk, so
+// a lane's four A (and B) values are 4 consecutive elements of one row: one
+// 128-bit load.
+typedef float f4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f4v mma16(const f4 a, const f4 b, f4v c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, c, 0, 0, 0);
+  return c;
+}
+__device__ __forceinline__ f4 ld4s(const float* p) { return *reinterpret_cast<const f4*>(p); }
+
+// Loads a [64][L] block of activations (row i = token row rbase + i * stride,
+// columns coff .. coff + L - 1) into LDS at row stride ds, as fp32; rows
+// i >= n are written as zeros. Groups of 4 elements, UM groups per thread
+// (64 L / 4 <= 256 UM): every load of a thread is issued before its LDS
+// writes, so the block waits one memory latency, not one per element.
+template <int ACT, bool VEC, int UM>
+__device__ __forceinline__ void gch_stage(const void* src, int64_t rbase, int64_t stride, int n, int64_t coff, int L,
+                                          float* dst, int ds) {
+  const int tid = threadIdx.x;
+  const int total = GCH * L / 4;
+  float v[UM][4];
+#pragma unroll
+  for (int m = 0; m < UM; ++m) {
+    const int e = min(tid + 256 * m, total - 1);
+    const int i = (4 * e) / L, col = 4 * e - i * L;
+    ld_act4<ACT, VEC>(src, rbase + (int64_t)min(i, n - 1) * stride + coff + col, v[m]);
+  }
+#pragma unroll
+  for (int m = 0; m < UM; ++m) {
+    const int e = tid + 256 * m;
+    if (e < total) {
+      const int i = (4 * e) / L, col = 4 * e - i * L;
+      const bool ok = i < n;
+      float* d = dst + i * ds + col;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) d[q] = ok ? v[m][q] : 0.f;
+    }
+  }
+}
+
+template <int K, int ACT, bool VEC>
 __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(GdnChunkParams cp) {
   const GdnParams& p = cp.g;
-  constexpr int KP = K + 1;  // padded row (LDS banks)
+  constexpr int KP = K + 4;  // row stride: 16-byte aligned rows, staggered banks
+  constexpr int TP = GCH + 4;
   const int V = p.V;
-  const int VP = V + 1;
+  const int VP = V + 4;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int x = lane & 15, kk = lane >> 4;
   extern __shared__ float lds[];
-  float* const Qs = lds;                  // [64][KP]; later V rows [64][VP]
+  float* const Qs = lds;                  // [64][KP]; later the V rows [64][VP]
   float* const Ks = Qs + GCH * (VP > KP ? VP : KP);
-  float* const As = Ks + GCH * KP;        // [64][65]
-  float* const Ts = As + GCH * 65;        // [64][65]
-  float* const gam = Ts + GCH * 65;       // [64]
+  float* const As = Ks + GCH * KP;        // [64][TP]
+  float* const Ts = As + GCH * TP;        // [64][TP]
+  float* const gam = Ts + GCH * TP;       // [64]
   float* const bet = gam + GCH;           // [64]
+  float* const egam = bet + GCH;          // [64] e^gamma
 
   const int c = blockIdx.x % cp.nck;
   const int bh = blockIdx.x / cp.nck;
@@ -69,19 +120,15 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(GdnChunkParams cp) 
   float* const Wg = rec;
   float* const Ug = Wg + GCH * K;
   float* const Qg = Ug + GCH * V;
-  float* const Kg = Qg + GCH * K;
+  float* const Kg = Qg + GCH * K;  // transposed: [K][64]
   float* const Pg = Kg + GCH * K;
   float* const gC = Pg + GCH * GCH;
 
   // ---- q, k of the chunk's tokens -> LDS (fp32)
-  for (int e = tid; e < GCH * K; e += 256) {
-    const int i = e / K, col = e - i * K;
-    const int64_t row = ((int64_t)bi * cp.T + t0 + min(i, n - 1)) * p.qkv_stride;
-    const bool ok = i < n;
-    Qs[i * KP + col] = ok ? ld_act<ACT>(p.qkv, row + (int64_t)h * K + col) : 0.f;
-    Ks[i * KP + col] = ok ? ld_act<ACT>(p.qkv, row + (int64_t)(p.H + h) * K + col) : 0.f;
-  }
-  // gates of token tid (wave 0), inclusive prefix sum of g
+  const int64_t rbase = ((int64_t)bi * cp.T + t0) * p.qkv_stride;
+  gch_stage<ACT, VEC, K / 16>(p.qkv, rbase, p.qkv_stride, n, (int64_t)h * K, K, Qs, KP);
+  gch_stage<ACT, VEC, K / 16>(p.qkv, rbase, p.qkv_stride, n, (int64_t)(p.H + h) * K, K, Ks, KP);
+  // gates of token `lane` (wave 0), inclusive prefix sum of g
   if (wave == 0) {
     float g = 0.f, be = 0.f;
     if (lane < n) {
@@ -96,6 +143,7 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(GdnChunkParams cp) 
     }
     gam[lane] = g;
     bet[lane] = be;
+    egam[lane] = expf(g);
   }
   __syncthreads();
 
@@ -117,124 +165,137 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(GdnChunkParams cp) 
   }
   __syncthreads();
 
-  // ---- Gram products, 4x4 blocks per thread (lower triangle only):
+  // ---- Gram products on the matrix cores, one 16x16 tile (ti, tj) at a time:
   //      A_ij = beta_i e^(g_i - g_j) (k_i . k_j), j < i;  P_ij = e^(g_i - g_j) (q_i . k_j), j <= i
-  {
-    const int bi4 = tid >> 4, bj4 = tid & 15;
-    float qk[4][4] = {}, kk[4][4] = {};
-    if (bj4 <= bi4) {
-      for (int col = 0; col < K; ++col) {
-        float qa[4], ka[4], kb[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          qa[x] = Qs[(4 * bi4 + x) * KP + col];
-          ka[x] = Ks[(4 * bi4 + x) * KP + col];
-          kb[x] = Ks[(4 * bj4 + x) * KP + col];
-        }
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-          for (int y = 0; y < 4; ++y) {
-            qk[x][y] += qa[x] * kb[y];
-            kk[x][y] += ka[x] * kb[y];
-          }
+  for (int t = wave; t < 16; t += 4) {
+    const int ti = t >> 2, tj = t & 3;
+    f4v qk = {0.f, 0.f, 0.f, 0.f}, kkm = {0.f, 0.f, 0.f, 0.f};
+    if (tj <= ti) {
+      for (int k0 = 0; k0 < K; k0 += 16) {
+        const f4 bq = ld4s(Ks + (16 * tj + x) * KP + k0 + 4 * kk);
+        qk = mma16(ld4s(Qs + (16 * ti + x) * KP + k0 + 4 * kk), bq, qk);
+        kkm = mma16(ld4s(Ks + (16 * ti + x) * KP + k0 + 4 * kk), bq, kkm);
       }
     }
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        const int i = 4 * bi4 + x, j = 4 * bj4 + y;
-        const float dec = j <= i ? expf(gam[i] - gam[j]) : 0.f;
-        As[i * 65 + j] = j < i ? bet[i] * dec * kk[x][y] : 0.f;
-        Pg[i * GCH + j] = j <= i ? dec * qk[x][y] : 0.f;
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * ti + 4 * kk + r, j = 16 * tj + x;
+      const float dec = j <= i ? expf(gam[i] - gam[j]) : 0.f;
+      As[i * TP + j] = j < i ? bet[i] * dec * kkm[r] : 0.f;
+      Pg[i * GCH + j] = j <= i ? dec * qk[r] : 0.f;
+    }
   }
-  // e^gamma q and e^(gamma_C - gamma) k to the workspace
+  // e^gamma q and (e^(gamma_C - gamma) k)^T to the workspace
   const float gl = gam[GCH - 1];
   for (int e = tid; e < GCH * K; e += 256) {
     const int i = e / K, col = e - i * K;
-    Qg[e] = expf(gam[i]) * Qs[i * KP + col];
-    Kg[e] = expf(gl - gam[i]) * Ks[i * KP + col];
+    Qg[e] = egam[i] * Qs[i * KP + col];
+    const int kc = e / GCH, j = e - kc * GCH;
+    Kg[e] = expf(gl - gam[j]) * Ks[j * KP + kc];
   }
   if (tid == 0) gC[0] = gl;
   __syncthreads();
 
-  // ---- V rows into the q buffer; Tm = (I + A)^-1 diag(beta) by forward
-  // substitution: wave w owns columns 16w .. 16w + 15, four lanes per column
-  // splitting the sum over j
-  for (int e = tid; e < GCH * V; e += 256) {
-    const int i = e / V, col = e - i * V;
-    const int64_t row = ((int64_t)bi * cp.T + t0 + min(i, n - 1)) * p.qkv_stride;
-    Qs[i * VP + col] = i < n ? ld_act<ACT>(p.qkv, row + 2 * (int64_t)p.H * K + (int64_t)hv * V + col) : 0.f;
-  }
-  {
-    const int m = wave * 16 + (lane & 15);
-    const int part = lane >> 4;
-    for (int i = 0; i < GCH; ++i) {
-      float acc = 0.f;
-      for (int j = part; j < i; j += 4) acc += As[i * 65 + j] * Ts[j * 65 + m];
-      acc += __shfl_xor(acc, 16);
-      acc += __shfl_xor(acc, 32);
-      if (part == 0) Ts[i * 65 + m] = m <= i ? (m == i ? bet[i] : 0.f) - acc : 0.f;
+  // ---- V rows into the q buffer; M = (I + A)^-1 blockwise (Tm = M diag(beta),
+  // with beta folded into the W and U products below). 16x16 blocks: the
+  // diagonal blocks by forward substitution (wave b, lane m: column m of
+  // block b, held in registers), then row block by row block
+  //   M_ij = -M_ii sum_{k=j}^{i-1} A_ik M_kj   (i > j)
+  // on the matrix cores, one (i, j) per wave. An MFMA result in lane layout
+  // (lane x + 16 kk holds D[4 kk + r][x]) is exactly the B operand of the
+  // next product, so Z = sum A_ik M_kj feeds -M_ii Z without a round trip.
+  gch_stage<ACT, VEC, 16>(p.qkv, rbase, p.qkv_stride, n, 2 * (int64_t)p.H * K + (int64_t)hv * V, V, Qs, VP);
+  if (lane < 16) {
+    const int b0 = 16 * wave;
+    float mc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float sacc = i == lane ? 1.f : 0.f;
+#pragma unroll
+      for (int j = 0; j < i; ++j) sacc -= As[(b0 + i) * TP + b0 + j] * mc[j];
+      mc[i] = sacc;
+      Ts[(b0 + i) * TP + b0 + lane] = sacc;
     }
   }
   __syncthreads();
+  for (int ib = 1; ib < 4; ++ib) {
+    if (wave < ib) {
+      const int jb = wave;
+      f4v z = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = jb; kb < ib; ++kb) {  // Z += A_(ib,kb) M_(kb,jb)
+        f4 bm;
+        const float* mcol = Ts + (16 * kb + 4 * kk) * TP + 16 * jb + x;
+        bm.x = mcol[0];
+        bm.y = mcol[TP];
+        bm.z = mcol[2 * TP];
+        bm.w = mcol[3 * TP];
+        z = mma16(ld4s(As + (16 * ib + x) * TP + 16 * kb + 4 * kk), bm, z);
+      }
+      f4v mij = {0.f, 0.f, 0.f, 0.f};
+      mij = mma16(ld4s(Ts + (16 * ib + x) * TP + 16 * ib + 4 * kk), f4{z[0], z[1], z[2], z[3]}, mij);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Ts[(16 * ib + 4 * kk + r) * TP + 16 * jb + x] = -mij[r];
+    }
+    if (wave >= ib) {  // the blocks above the diagonal of this row block are zero
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int jb = wave;  // column blocks ib .. 3 of rows 16 ib ..: only jb > ib are outside the solve
+        if (jb > ib) Ts[(16 * ib + 4 * kk + r) * TP + 16 * jb + x] = 0.f;
+      }
+    }
+    __syncthreads();
+  }
+  if (wave > 0) {  // row block 0: column blocks 1 .. 3 are zero
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Ts[(4 * kk + r) * TP + 16 * wave + x] = 0.f;
+  }
+  __syncthreads();
 
-  // ---- W = Tm (e^gamma k), U = Tm V: 4 rows x 8 columns per thread
-  {
-    const int i4 = tid >> 4, c8 = tid & 15;
-    for (int cb = c8 * 8; cb < K; cb += 128) {
-      float w[4][8] = {};
-      for (int j = 0; j <= 4 * i4 + 3; ++j) {
-        const float ej = expf(gam[j]);
-        float kr[8];
-#pragma unroll
-        for (int y = 0; y < 8; ++y) kr[y] = ej * Ks[j * KP + cb + y];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const float tv = Ts[(4 * i4 + x) * 65 + j];
-#pragma unroll
-          for (int y = 0; y < 8; ++y) w[x][y] += tv * kr[y];
-        }
-      }
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 8; ++y) Wg[(4 * i4 + x) * K + cb + y] = w[x][y];
+  // ---- W = M diag(beta) (e^gamma k) and U = M diag(beta) V on the matrix
+  // cores; M is lower triangular, so row tile ti only contracts over tokens
+  // < 16 (ti + 1)
+  const int ntk = K / 16, ntv = V / 16;
+  for (int t = wave; t < 4 * (ntk + ntv); t += 4) {
+    const bool isw = t < 4 * ntk;
+    const int tt = isw ? t : t - 4 * ntk;
+    const int ti = tt & 3, tc = tt >> 2;
+    const float* Bm = isw ? Ks : Qs;
+    const int bs = isw ? KP : VP;
+    f4v acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < 16 * (ti + 1); j0 += 16) {
+      f4 b;
+      const int j = j0 + 4 * kk;
+      const float* col = Bm + 16 * tc + x;
+      b.x = col[(j + 0) * bs] * bet[j + 0] * (isw ? egam[j + 0] : 1.f);
+      b.y = col[(j + 1) * bs] * bet[j + 1] * (isw ? egam[j + 1] : 1.f);
+      b.z = col[(j + 2) * bs] * bet[j + 2] * (isw ? egam[j + 2] : 1.f);
+      b.w = col[(j + 3) * bs] * bet[j + 3] * (isw ? egam[j + 3] : 1.f);
+      acc = mma16(ld4s(Ts + (16 * ti + x) * TP + j), b, acc);
     }
-    for (int cb = c8 * 8; cb < V; cb += 128) {
-      float u[4][8] = {};
-      for (int j = 0; j <= 4 * i4 + 3; ++j) {
-        float vr[8];
+    float* dst = isw ? Wg : Ug;
+    const int ld = isw ? K : V;
 #pragma unroll
-        for (int y = 0; y < 8; ++y) vr[y] = cb + y < V ? Qs[j * VP + cb + y] : 0.f;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const float tv = Ts[(4 * i4 + x) * 65 + j];
-#pragma unroll
-          for (int y = 0; y < 8; ++y) u[x][y] += tv * vr[y];
-        }
-      }
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 8; ++y)
-          if (cb + y < V) Ug[(4 * i4 + x) * V + cb + y] = u[x][y];
-    }
+    for (int r = 0; r < 4; ++r) dst[(16 * ti + 4 * kk + r) * ld + 16 * tc + x] = acc[r];
   }
 }
 
 // Pass 2: one block per (row, value head, 16 state rows), chunks in order.
+// Wave w takes token tile w (16 tokens) for Delta and O, and column tiles
+// w, w + 4 of the new rows. (Fetching a wave's next-chunk operands ahead
+// was measured: 6% faster at one sequence, 45% slower at eight, from the
+// registers it costs.)
 template <int K, bool NORM>
 __global__ __launch_bounds__(256) void gdn_chunk_state_kernel(GdnChunkParams cp) {
   const GdnParams& p = cp.g;
   const int V = p.V;
   const int nvt = V / GCH_VT;
   const int tid = threadIdx.x;
-  __shared__ float Ss[GCH_VT][K + 4];
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int x = lane & 15, kk = lane >> 4;
+  constexpr int SP = K + 4;
+  __shared__ float Ss[GCH_VT * SP];
   __shared__ float Ds[GCH][GCH_VT + 1];
-  __shared__ float Kh[GCH][K + 4];
 
   // XCD-aware block order: the tiles of one (row, head) share blockIdx % 8
   const int BH = p.B * p.HV;
@@ -251,9 +312,10 @@ __global__ __launch_bounds__(256) void gdn_chunk_state_kernel(GdnChunkParams cp)
   if (len == 0) return;
   const int v0 = vt * GCH_VT;
   float* const Sg = static_cast<float*>(p.state) + (((int64_t)slot * p.HV + hv) * V + v0) * (int64_t)K;
-  for (int e = tid; e < GCH_VT * K; e += 256) Ss[e / K][e % K] = Sg[e];
+  for (int e = tid; e < GCH_VT * K; e += 256) Ss[(e / K) * SP + e % K] = Sg[e];
   __syncthreads();
 
+  const int ti = wave;
   const int nchunks = (len + GCH - 1) / GCH;
   for (int c = 0; c < nchunks; ++c) {
     const float* const rec = cp.ws + ((int64_t)bh * cp.nck + c) * gch_rec_floats(K, V);
@@ -262,59 +324,73 @@ __global__ __launch_bounds__(256) void gdn_chunk_state_kernel(GdnChunkParams cp)
     const float* const Qg = Ug + GCH * V;
     const float* const Kg = Qg + GCH * K;
     const float* const Pg = Kg + GCH * K;
-    const float gl = Pg[GCH * GCH];
+    const float eg = expf(Pg[GCH * GCH]);
     const int t0 = c * GCH;
-    for (int e = tid; e < GCH * K; e += 256) Kh[e / K][e % K] = Kg[e];
-    // X = W S^T, Y = (e^gamma q) S^T: token i, state rows 4 rg .. 4 rg + 3
-    const int i = tid >> 2, rg = tid & 3;
-    float x[4] = {}, y[4] = {};
-    for (int col = 0; col < K; col += 4) {
-      const f4 wv = *reinterpret_cast<const f4*>(Wg + i * K + col);
-      const f4 qv = *reinterpret_cast<const f4*>(Qg + i * K + col);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float* s = &Ss[4 * rg + r][col];
-        x[r] += wv.x * s[0] + wv.y * s[1] + wv.z * s[2] + wv.w * s[3];
-        y[r] += qv.x * s[0] + qv.y * s[1] + qv.z * s[2] + qv.w * s[3];
-      }
+    // X = W S^T, Y = (e^gamma q) S^T for this wave's 16 tokens
+    f4v X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < K; k0 += 16) {
+      const f4 b = ld4s(Ss + x * SP + k0 + 4 * kk);
+      X = mma16(ld4s(Wg + (16 * ti + x) * K + k0 + 4 * kk), b, X);
+      Y = mma16(ld4s(Qg + (16 * ti + x) * K + k0 + 4 * kk), b, Y);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Ds[i][4 * rg + r] = Ug[i * V + v0 + 4 * rg + r] - x[r];
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * ti + 4 * kk + r;
+      Ds[i][x] = Ug[i * V + v0 + x] - X[r];  // Delta^T
+    }
     __syncthreads();
-    // O = Y + P Delta^T (P lower triangular)
-    float o[4] = {y[0], y[1], y[2], y[3]};
-    for (int j = 0; j <= i; ++j) {
-      const float pj = Pg[i * GCH + j];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] += pj * Ds[j][4 * rg + r];
+    // O = Y + P Delta^T (P lower triangular: tokens < 16 (ti + 1))
+    for (int j0 = 0; j0 < 16 * (ti + 1); j0 += 16) {
+      const int j = j0 + 4 * kk;
+      f4 b;
+      b.x = Ds[j][x];
+      b.y = Ds[j + 1][x];
+      b.z = Ds[j + 2][x];
+      b.w = Ds[j + 3][x];
+      Y = mma16(ld4s(Pg + (16 * ti + x) * GCH + j), b, Y);
     }
-    if (t0 + i < len) {
-      const int64_t orow = (((int64_t)bi * cp.T + t0 + i) * p.HV + hv) * V + v0 + 4 * rg;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if constexpr (NORM) cp.obuf[orow + r] = o[r];
-        else store_act1(p.out, orow + r, p.out_dt, o[r]);
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * ti + 4 * kk + r;
+      if (t0 + i < len) {
+        const int64_t o = (((int64_t)bi * cp.T + t0 + i) * p.HV + hv) * V + v0 + x;
+        if constexpr (NORM) cp.obuf[o] = Y[r];
+        else store_act1(p.out, o, p.out_dt, Y[r]);
       }
     }
-    // S <- e^(gamma_C) S + Delta (e^(gamma_C - gamma) k): row r, 8 columns per thread
-    {
-      const int r = tid >> 4, cb = (tid & 15) * (K / 16);
-      const float eg = expf(gl);
-      float acc[K / 16];
+    // S <- e^(gamma_C) S + Delta (e^(gamma_C - gamma) k): column tiles wave, wave + 4
+    f4v Sn[2];
 #pragma unroll
-      for (int q = 0; q < K / 16; ++q) acc[q] = eg * Ss[r][cb + q];
-      for (int j = 0; j < GCH; ++j) {
-        const float d = Ds[j][r];
+    for (int q = 0; q < 2; ++q) {
+      const int tc = wave + 4 * q;
+      if (tc < K / 16) {
+        f4v acc;
 #pragma unroll
-        for (int q = 0; q < K / 16; ++q) acc[q] += d * Kh[j][cb + q];
+        for (int r = 0; r < 4; ++r) acc[r] = eg * Ss[(4 * kk + r) * SP + 16 * tc + x];
+        for (int j0 = 0; j0 < GCH; j0 += 16) {
+          const int j = j0 + 4 * kk;
+          f4 a;
+          a.x = Ds[j][x];
+          a.y = Ds[j + 1][x];
+          a.z = Ds[j + 2][x];
+          a.w = Ds[j + 3][x];
+          acc = mma16(a, ld4s(Kg + (16 * tc + x) * GCH + j), acc);
+        }
+        Sn[q] = acc;
       }
-      __syncthreads();  // every thread is done reading the old rows and Delta
+    }
+    __syncthreads();  // every wave is done reading the old rows and Delta
 #pragma unroll
-      for (int q = 0; q < K / 16; ++q) Ss[r][cb + q] = acc[q];
+    for (int q = 0; q < 2; ++q) {
+      const int tc = wave + 4 * q;
+      if (tc < K / 16) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ss[(4 * kk + r) * SP + 16 * tc + x] = Sn[q][r];
+      }
     }
     __syncthreads();
   }
-  for (int e = tid; e < GCH_VT * K; e += 256) Sg[e] = Ss[e / K][e % K];
+  for (int e = tid; e < GCH_VT * K; e += 256) Sg[e] = Ss[(e / K) * SP + e % K];
 }
 
 // Pass 3 (gated RMSNorm): one wave per (row, token, value head).
@@ -355,10 +431,13 @@ namespace {
 template <int K, int ACT>
 hipError_t launch_gch_k(const GdnChunkParams& cp, hipStream_t st) {
   const GdnParams& p = cp.g;
-  const int KP = K + 1, VP = p.V + 1;
-  const size_t lds = sizeof(float) * ((size_t)GCH * (VP > KP ? VP : KP) + (size_t)GCH * KP + 2 * GCH * 65 + 2 * GCH);
+  const int KP = K + 4, VP = p.V + 4, TP = GCH + 4;
+  const size_t lds = sizeof(float) * ((size_t)GCH * (VP > KP ? VP : KP) + (size_t)GCH * KP + 2 * GCH * TP + 3 * GCH);
   const int64_t prep_blocks = (int64_t)p.B * p.HV * cp.nck;
-  gdn_chunk_prep_kernel<K, ACT><<<dim3((unsigned)prep_blocks), dim3(256), lds, st>>>(cp);
+  if (p.qkv_vec)
+    gdn_chunk_prep_kernel<K, ACT, true><<<dim3((unsigned)prep_blocks), dim3(256), lds, st>>>(cp);
+  else
+    gdn_chunk_prep_kernel<K, ACT, false><<<dim3((unsigned)prep_blocks), dim3(256), lds, st>>>(cp);
   const int nvt = p.V / GCH_VT;
   const int64_t bh8 = ((int64_t)p.B * p.HV + 7) / 8 * 8;
   const int64_t state_blocks = bh8 * nvt;
