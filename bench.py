@@ -271,10 +271,12 @@ def kda(dev, reps=30):
                           pools[i], dd["idx"], out, output_gate=dd["gate"], norm_weight=dd["norm_weight"])
     us = graph_time_us([lambda i=i: call(i) for i in range(M)], reps, torch.cuda.current_stream())
     sb = w.T * w.H * w.D * w.D * 4 * 2
+    ab = kda_alg_bytes(w)
     del pools, cs
     torch.cuda.empty_cache()
     return {"workload": w.name, "us_per_step": round(us, 3), "state_GBps": round(sb / us / 1e3, 1),
-            "pct_hbm_peak": round(100 * sb / us / 1e3 / HBM_PEAK_GBS, 2), "pools": M}
+            "pct_hbm_peak": round(100 * sb / us / 1e3 / HBM_PEAK_GBS, 2), "alg_GBps": round(ab / us / 1e3, 1),
+            "pct_hbm_peak_alg": round(100 * ab / us / 1e3 / HBM_PEAK_GBS, 2), "pools": M}
 
 
 def gdn_conv(dev, reps=30, Wd=4):
@@ -481,24 +483,43 @@ def counters_traffic():
 
 
 # ------------------------------------------------------------ rocprofv3 helpers
-def profile_pass():
-    """A few launches of the headline kernel and one copy of known size."""
+def kda_alg_bytes(w, out_bytes=2, act=2):
+    """All algorithmic bytes of one fused KDA launch: state read + write, conv
+    state read + write, x, raw_g, raw_beta, output gate, output, conv weights."""
+    C = 3 * w.H * w.D
+    return (2 * w.T * w.H * w.D * w.D * 4 + 2 * w.T * C * (w.W - 1) * act + w.T * C * act
+            + w.T * w.H * w.D * act + w.T * w.H * act + w.T * w.H * w.D * act + w.T * w.H * w.D * out_bytes
+            + C * w.W * 4)
+
+
+def profile_pass(which="gdn"):
+    """A few launches of one kernel (the headline GDN step, or the fused KDA
+    op at 64 tokens x 96 heads) and one copy of known size, for rocprofv3
+    counter passes."""
     import torch
     import ssm_recurrent_decode_gated_amd as S
     import workloads as W
     dev = torch.device("cuda:0")
-    su = GDNSetup(W.GDN_B256, 2, dev)
-    for i in range(6):
-        su.call(i)
+    if which == "kda":
+        w = W.KDA_T64
+        d = {k: v.to(dev) for k, v in W.kda_inputs(w).items()}
+        out = torch.empty(w.T, w.H, w.D, dtype=torch.bfloat16, device=dev)
+        for i in range(4):
+            S.kda_decode_step(d["x"], d["conv_weight"], None, d["conv_state"], d["raw_g"], d["raw_beta"], None, None,
+                              d["state"], d["idx"], out, output_gate=d["gate"], norm_weight=d["norm_weight"])
+    else:
+        su = GDNSetup(W.GDN_B256, 2, dev)
+        for i in range(6):
+            su.call(i)
     n = 1 << 30
     src = torch.ones(n // 4, device=dev)
     dst = torch.empty_like(src)
     S.ssmd_stream_copy(src, dst)
     torch.cuda.synchronize()
-    print(f"profile pass done: 6 x gdn_decode_step B=256, 1 x stream copy of {n} bytes", flush=True)
+    print(f"profile pass done: {which} launches, 1 x stream copy of {n} bytes", flush=True)
 
 
-def _read_counter_csv(d, counter):
+def _read_counter_csv(d, counter, kernel=KERNEL_NAME):
     import csv
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
     if not files:
@@ -509,34 +530,40 @@ def _read_counter_csv(d, counter):
             if r.get("Counter_Name") != counter:
                 continue
             name = r.get("Kernel_Name", "")
-            key = "gdn" if KERNEL_NAME in name else ("copy" if "stream_copy_kernel" in name else None)
+            key = "gdn" if kernel in name else ("copy" if "stream_copy_kernel" in name else None)
             if key:
                 per.setdefault(key, {}).setdefault(r.get("Dispatch_Id"), 0.0)
                 per[key][r.get("Dispatch_Id")] += float(r["Counter_Value"])
     return {k: sum(v.values()) / len(v) for k, v in per.items()}
 
 
-def summarize_counters(fetch_dir, write_dir, out, command):
-    f = _read_counter_csv(fetch_dir, "FETCH_SIZE")
-    w = _read_counter_csv(write_dir, "WRITE_SIZE")
+def summarize_counters(fetch_dir, write_dir, out, command, which="gdn"):
     import workloads as W
-    wl = W.GDN_B256
-    alg = gdn_alg_bytes(wl.B, wl.H, wl.HV, wl.K, wl.V)
+    if which == "kda":
+        kernel, wl = "kda_decode_pf_kernel", W.KDA_T64
+        alg = kda_alg_bytes(wl)
+        title = f"# rocprofv3 HBM counters, {kernel} at 64 tokens x 96 heads (D=128, conv width 4, bf16 act, norm)"
+    else:
+        kernel, wl = KERNEL_NAME, W.GDN_B256
+        alg = gdn_alg_bytes(wl.B, wl.H, wl.HV, wl.K, wl.V)
+        title = f"# rocprofv3 HBM counters, {kernel} at B=256 of 264 slots (H=16 HV=32 K=V=128, bf16 act)"
+    f = _read_counter_csv(fetch_dir, "FETCH_SIZE", kernel)
+    w = _read_counter_csv(write_dir, "WRITE_SIZE", kernel)
     copy_bytes = 1 << 30
     ff, wf = copy_bytes / 1024 / f["copy"], copy_bytes / 1024 / w["copy"]
     traffic = f["gdn"] * 1024 * ff + w["gdn"] * 1024 * wf
     lines = [
-        f"# rocprofv3 HBM counters, {KERNEL_NAME} at B=256 of 264 slots (H=16 HV=32 K=V=128, bf16 act)",
+        title,
         f"# command: {command}",
         "# values are KiB per dispatch, averaged over dispatches; the copy kernel moves copy_bytes each way",
-        f"kernel_source_sha256 = {kernel_source_hash()}",
-        f"gdn_fetch_kib = {f['gdn']:.1f}",
-        f"gdn_write_kib = {w['gdn']:.1f}",
+        f"kernel_source_sha256 = {kernel_source_hash()}" if which == "gdn" else f"kernel = {kernel}",
+        f"gdn_fetch_kib = {f['gdn']:.1f}" if which == "gdn" else f"kernel_fetch_kib = {f['gdn']:.1f}",
+        f"gdn_write_kib = {w['gdn']:.1f}" if which == "gdn" else f"kernel_write_kib = {w['gdn']:.1f}",
         f"copy_bytes = {copy_bytes}",
         f"copy_fetch_kib = {f['copy']:.1f}",
         f"copy_write_kib = {w['copy']:.1f}",
         f"# fetch scale {ff:.4f}, write scale {wf:.4f}",
-        f"# scaled HBM traffic per gdn launch = {traffic / 1e6:.2f} MB; algorithmic = {alg / 1e6:.2f} MB "
+        f"# scaled HBM traffic per launch = {traffic / 1e6:.2f} MB; algorithmic = {alg / 1e6:.2f} MB "
         f"(ratio {traffic / alg:.4f})",
     ]
     with open(out, "w") as fh:
@@ -571,16 +598,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline only (no sweep/buffered/KDA/conv/Mamba/copy)")
-    ap.add_argument("--profile-pass", action="store_true")
+    ap.add_argument("--profile-pass", nargs="?", const="gdn", choices=("gdn", "kda"))
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
     ap.add_argument("--title", default="")
+    ap.add_argument("--kernel", default="gdn", choices=("gdn", "kda"), help="which kernel --summarize-counters covers")
     ap.add_argument("--out", default=COUNTERS_FILE)
     ap.add_argument("--command", default="")
     args = ap.parse_args()
 
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters, args.out, args.command)
+        summarize_counters(*args.summarize_counters, args.out, args.command, args.kernel)
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.out, args.command, args.title)
@@ -590,7 +618,7 @@ def main():
               "runs on a single MI355X; --gpus above 1 is not supported.", file=sys.stderr)
         sys.exit(1)
     if args.profile_pass:
-        profile_pass()
+        profile_pass(args.profile_pass)
         return
 
     import torch
