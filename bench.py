@@ -9,12 +9,15 @@ the 256 MB Infinity Cache cannot hold the state between steps.
 The same JSON line also carries the latency-to-bandwidth sweep (B = 1, 16,
 64, 256 under HIP-graph replay of one call per pool), the buffered variant
 (B=64, L = 1/8/16, exact cycle mean), the fused KDA step (T=64, 96 heads),
-a same-size stream-copy ceiling, the roofline entry of the dominant kernel
-and the fp64 oracle's rate on the host cores.
+the conv-fused GDN step, the 16-bit-state step, Mamba-1 decode and prefill
+scan, the multi-token GDN call, the chunked and sequential GDN prefill, a
+same-size stream-copy ceiling, the roofline entry of the dominant kernel and
+the fp64 oracle's rate on the host cores.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-  python bench.py --profile-pass     # short run for rocprofv3 counter passes
-  python bench.py --summarize-counters FETCH_DIR WRITE_DIR --out profiles/X.txt
+  python bench.py --profile-pass [gdn|kda]   # short run for rocprofv3 counter passes
+  python bench.py --summarize-counters FETCH_DIR WRITE_DIR --kernel gdn|kda --out profiles/X.txt
+  python bench.py --summarize-trace TRACE_DIR --title T --command C --out profiles/X.md
 """
 from __future__ import annotations
 
@@ -584,7 +587,10 @@ def summarize_trace(trace_dir, out, command, title):
              f"    {command}", "", "`run_kernel_stats.csv`:", "", "| " + " | ".join(cols) + " |",
              "|" + "---|" * len(cols)]
     for r in rows:
-        vals = [f"`{r['Name']}`"] + [r.get(c, "") for c in cols[1:]]
+        name = r["Name"]
+        if len(name) > 160:  # torch's generated template names; the head names the kernel
+            name = name[:150] + " ..."
+        vals = [f"`{name}`"] + [r.get(c, "") for c in cols[1:]]
         lines.append("| " + " | ".join(vals) + " |")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
