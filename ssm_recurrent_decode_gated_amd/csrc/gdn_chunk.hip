@@ -25,6 +25,8 @@
 // 2 writes fp32 outputs to the workspace and a third pass normalises them.
 // All arithmetic is fp32; the dense products run on the matrix cores
 // (v_mfma_f32_16x16x4_f32), the triangular solve on the VALU.
+#include <type_traits>
+
 #include "ssmd_device.h"
 #include "ssmd_internal.h"
 
@@ -55,55 +57,148 @@ __device__ __forceinline__ f4v mma16(const f4 a, const f4 b, f4v c) {
 }
 __device__ __forceinline__ f4 ld4s(const float* p) { return *reinterpret_cast<const f4*>(p); }
 
-// Loads a [64][L] block of activations (row i = token row rbase + i * stride,
-// columns coff .. coff + L - 1) into LDS at row stride ds, as fp32; rows
-// i >= n are written as zeros. Groups of 4 elements, UM groups per thread
-// (64 L / 4 <= 256 UM): every load of a thread is issued before its LDS
-// writes, so the block waits one memory latency, not one per element.
-template <int ACT, bool VEC, int UM>
-__device__ __forceinline__ void gch_stage(const void* src, int64_t rbase, int64_t stride, int n, int64_t coff, int L,
-                                          float* dst, int ds) {
-  const int tid = threadIdx.x;
-  const int total = GCH * L / 4;
-  float v[UM][4];
-#pragma unroll
-  for (int m = 0; m < UM; ++m) {
-    const int e = min(tid + 256 * m, total - 1);
-    const int i = (4 * e) / L, col = 4 * e - i * L;
-    ld_act4<ACT, VEC>(src, rbase + (int64_t)min(i, n - 1) * stride + coff + col, v[m]);
+// Staged activations keep their input encoding in LDS: raw 16-bit words for
+// bf16/f16 inputs (half the LDS of fp32, so two blocks share a CU), fp32
+// otherwise. Normalisation scales and gate factors are kept per token and
+// applied to products, so the staged values stay the inputs' own.
+template <int ACT>
+using stg_t = typename std::conditional<ACT == SSMD_F32, float, uint16_t>::type;
+template <int ACT>
+using raw4_t = typename std::conditional<ACT == SSMD_F32, f4, uint2>::type;
+
+template <int ACT, bool VEC>
+__device__ __forceinline__ raw4_t<ACT> ld_raw4(const void* base, int64_t off) {
+  if constexpr (ACT == SSMD_F32) {
+    const float* p = static_cast<const float*>(base) + off;
+    if constexpr (VEC) return *reinterpret_cast<const f4*>(p);
+    else return f4{p[0], p[1], p[2], p[3]};
+  } else {
+    const uint16_t* p = static_cast<const uint16_t*>(base) + off;
+    if constexpr (VEC) return *reinterpret_cast<const uint2*>(p);
+    else return uint2{p[0] | ((uint32_t)p[1] << 16), p[2] | ((uint32_t)p[3] << 16)};
   }
+}
+
+template <int ACT>
+__device__ __forceinline__ float raw_to_f(uint32_t h) {
+  if constexpr (ACT == SSMD_BF16) return bf16_bits_to_f32(h);
+  else return f16_bits_to_f32(h);
+}
+
+template <int ACT>
+__device__ __forceinline__ f4 raw4_to_f4(raw4_t<ACT> v) {
+  if constexpr (ACT == SSMD_F32) return v;
+  else return f4{raw_to_f<ACT>(v.x & 0xffffu), raw_to_f<ACT>(v.x >> 16), raw_to_f<ACT>(v.y & 0xffffu),
+                 raw_to_f<ACT>(v.y >> 16)};
+}
+
+template <int ACT>
+__device__ __forceinline__ float stg_ld1(const stg_t<ACT>* p) {
+  if constexpr (ACT == SSMD_F32) return *p;
+  else return raw_to_f<ACT>(*p);
+}
+
+template <int ACT>
+__device__ __forceinline__ void stg_st4(stg_t<ACT>* p, raw4_t<ACT> v) {
+  if constexpr (ACT == SSMD_F32) *reinterpret_cast<f4*>(p) = v;
+  else *reinterpret_cast<uint2*>(p) = v;
+}
+
+// One 16-index step of a Gram tile from two staged rows (each pointer at
+// column k0 + 4 kk of its lane's row): fp32 storage takes four fp32 MFMAs,
+// 16-bit storage one v_mfma_f32_16x16x16 on the raw words (products of 16-bit
+// values are exact in fp32, so this matches the fp32 product up to summation
+// order).
+typedef short s4v __attribute__((ext_vector_type(4)));
+typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+template <int ACT>
+__device__ __forceinline__ f4v gram16(const stg_t<ACT>* a, const stg_t<ACT>* b, f4v c) {
+  if constexpr (ACT == SSMD_F32) {
+    return mma16(ld4s(a), ld4s(b), c);
+  } else {
+    const uint2 ua = *reinterpret_cast<const uint2*>(a), ub = *reinterpret_cast<const uint2*>(b);
+    if constexpr (ACT == SSMD_BF16)
+      return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4v, ua), __builtin_bit_cast(s4v, ub), c,
+                                                        0, 0, 0);
+    else
+      return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4v, ua), __builtin_bit_cast(h4v, ub), c, 0,
+                                                    0, 0);
+  }
+}
+
+// Issues the loads of rows i < n of a [64][L] activation block (row i = element
+// rbase + i * stride, columns coff .. coff + L - 1): 4 elements per group,
+// group e = tid + 256 m, token e / (L / 4). Rows past n re-read row n - 1 (in
+// bounds) and are zeroed when stored.
+template <int ACT, bool VEC, int UM>
+__device__ __forceinline__ void gch_load(const void* src, int64_t rbase, int64_t stride, int n, int64_t coff, int L,
+                                         raw4_t<ACT> (&v)[UM]) {
+  const int g = L / 4;
 #pragma unroll
   for (int m = 0; m < UM; ++m) {
-    const int e = tid + 256 * m;
-    if (e < total) {
-      const int i = (4 * e) / L, col = 4 * e - i * L;
-      const bool ok = i < n;
-      float* d = dst + i * ds + col;
+    const int e = threadIdx.x + 256 * m;
+    const int i = e / g, col = 4 * (e - i * g);
+    v[m] = ld_raw4<ACT, VEC>(src, rbase + (int64_t)min(i, n - 1) * stride + coff + col);
+  }
+}
+
+template <int ACT, int UM>
+__device__ __forceinline__ void gch_store(const raw4_t<ACT> (&v)[UM], int n, int L, stg_t<ACT>* dst, int ds) {
+  const int g = L / 4;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) d[q] = ok ? v[m][q] : 0.f;
-    }
+  for (int m = 0; m < UM; ++m) {
+    const int e = threadIdx.x + 256 * m;
+    const int i = e / g, col = 4 * (e - i * g);
+    raw4_t<ACT> w = v[m];
+    if (i >= n) w = raw4_t<ACT>{};
+    stg_st4<ACT>(dst + i * ds + col, w);
+  }
+}
+
+// Per-token norm scale of a staged q or k block held in registers (L = K, so
+// a token's K / 4 groups sit on K / 4 consecutive lanes of one wave):
+// mul * rsqrt(|x|^2 + eps) with the L2 norm, else mul.
+template <int ACT, int K, int UM>
+__device__ __forceinline__ void gch_norm_scale(const raw4_t<ACT> (&v)[UM], const GdnParams& p, float mul,
+                                               float* sc) {
+  constexpr int g = K / 4;
+#pragma unroll
+  for (int m = 0; m < UM; ++m) {
+    const f4 f = raw4_to_f4<ACT>(v[m]);
+    float s = f.x * f.x + f.y * f.y + f.z * f.z + f.w * f.w;
+    s = group_sum<16>(s);
+    if constexpr (g == 32) s += __shfl_xor(s, 16);
+    const int e = threadIdx.x + 256 * m;
+    if ((e & (g - 1)) == 0) sc[e / g] = mul * (p.use_l2 ? rsqrtf(s + p.l2eps) : 1.f);
   }
 }
 
 template <int K, int ACT, bool VEC>
 __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(GdnChunkParams cp) {
+  using ST = stg_t<ACT>;
   const GdnParams& p = cp.g;
-  constexpr int KP = K + 4;  // row stride: 16-byte aligned rows, staggered banks
+  constexpr int KS = K + 4;  // staged row stride (elements): aligned rows, staggered banks
   constexpr int TP = GCH + 4;
   const int V = p.V;
-  const int VP = V + 4;
+  const int VS = V + 4;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int x = lane & 15, kk = lane >> 4;
   extern __shared__ float lds[];
-  float* const Qs = lds;                  // [64][KP]; later the V rows [64][VP]
-  float* const Ks = Qs + GCH * (VP > KP ? VP : KP);
-  float* const As = Ks + GCH * KP;        // [64][TP]
-  float* const Ts = As + GCH * TP;        // [64][TP]
-  float* const gam = Ts + GCH * TP;       // [64]
-  float* const bet = gam + GCH;           // [64]
-  float* const egam = bet + GCH;          // [64] e^gamma
+  float* const AT = lds;                 // [64][TP]: A, then M (see the inverse below)
+  float* const gam = AT + GCH * TP;      // per token: gamma_i
+  float* const bet = gam + GCH;          //   beta_i
+  float* const egam = bet + GCH;         //   e^gamma_i
+  float* const ekc = egam + GCH;         //   e^(gamma_C - gamma_i)
+  float* const qsc = ekc + GCH;          //   q scale (norm * K^-1/2)
+  float* const ksc = qsc + GCH;          //   k scale (norm)
+  float* const fq = ksc + GCH;           //   e^gamma_i q scale
+  float* const fk = fq + GCH;            //   e^(gamma_C - gamma_i) k scale
+  float* const fw = fk + GCH;            //   beta_i e^gamma_i k scale
+  ST* const Qr = reinterpret_cast<ST*>(fw + GCH);  // [64][KS] raw q
+  ST* const Kr = Qr + GCH * KS;                    // [64][KS] raw k
+  ST* const Vr = Kr + GCH * KS;                    // [64][VS] raw v
 
   const int c = blockIdx.x % cp.nck;
   const int bh = blockIdx.x / cp.nck;
@@ -124,98 +219,121 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(GdnChunkParams cp) 
   float* const Pg = Kg + GCH * K;
   float* const gC = Pg + GCH * GCH;
 
-  // ---- q, k of the chunk's tokens -> LDS (fp32)
+  // ---- q, k, v of the chunk's tokens: every load issued before any store
   const int64_t rbase = ((int64_t)bi * cp.T + t0) * p.qkv_stride;
-  gch_stage<ACT, VEC, K / 16>(p.qkv, rbase, p.qkv_stride, n, (int64_t)h * K, K, Qs, KP);
-  gch_stage<ACT, VEC, K / 16>(p.qkv, rbase, p.qkv_stride, n, (int64_t)(p.H + h) * K, K, Ks, KP);
-  // gates of token `lane` (wave 0), inclusive prefix sum of g
-  if (wave == 0) {
-    float g = 0.f, be = 0.f;
-    if (lane < n) {
-      const int64_t gi = ((int64_t)bi * cp.T + t0 + lane) * p.HV + hv;
-      g = -expf(p.A_log[hv]) * softplus_f(ld_act<ACT>(p.a, gi) + p.dt_bias[hv]);
-      be = sigmoid_f(ld_act<ACT>(p.b, gi));
-    }
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const float o = __shfl_up(g, d);
-      if (lane >= d) g += o;
-    }
-    gam[lane] = g;
-    bet[lane] = be;
-    egam[lane] = expf(g);
-  }
-  __syncthreads();
-
-  // ---- L2 norms (wave w: tokens 16w .. 16w + 15), q scale
-  for (int i = wave * 16; i < wave * 16 + 16; ++i) {
-    float sq = 0.f, sk = 0.f;
-    for (int col = lane; col < K; col += 64) {
-      sq += Qs[i * KP + col] * Qs[i * KP + col];
-      sk += Ks[i * KP + col] * Ks[i * KP + col];
-    }
-    sq = wave_sum(sq);
-    sk = wave_sum(sk);
-    const float qs = p.scale * (p.use_l2 ? rsqrtf(sq + p.l2eps) : 1.f);
-    const float ks = p.use_l2 ? rsqrtf(sk + p.l2eps) : 1.f;
-    for (int col = lane; col < K; col += 64) {
-      Qs[i * KP + col] *= qs;
-      Ks[i * KP + col] *= ks;
-    }
-  }
-  __syncthreads();
-
-  // ---- Gram products on the matrix cores, one 16x16 tile (ti, tj) at a time:
-  //      A_ij = beta_i e^(g_i - g_j) (k_i . k_j), j < i;  P_ij = e^(g_i - g_j) (q_i . k_j), j <= i
-  for (int t = wave; t < 16; t += 4) {
-    const int ti = t >> 2, tj = t & 3;
-    f4v qk = {0.f, 0.f, 0.f, 0.f}, kkm = {0.f, 0.f, 0.f, 0.f};
-    if (tj <= ti) {
-      for (int k0 = 0; k0 < K; k0 += 16) {
-        const f4 bq = ld4s(Ks + (16 * tj + x) * KP + k0 + 4 * kk);
-        qk = mma16(ld4s(Qs + (16 * ti + x) * KP + k0 + 4 * kk), bq, qk);
-        kkm = mma16(ld4s(Ks + (16 * ti + x) * KP + k0 + 4 * kk), bq, kkm);
+  {
+    raw4_t<ACT> rq[K / 16], rk[K / 16];
+    gch_load<ACT, VEC>(p.qkv, rbase, p.qkv_stride, n, (int64_t)h * K, K, rq);
+    gch_load<ACT, VEC>(p.qkv, rbase, p.qkv_stride, n, (int64_t)(p.H + h) * K, K, rk);
+    // gates of token `lane` (wave 0): inclusive prefix sum of g, beta, decay factors
+    if (wave == 0) {
+      float g = 0.f, be = 0.f;
+      if (lane < n) {
+        const int64_t gi = ((int64_t)bi * cp.T + t0 + lane) * p.HV + hv;
+        g = -expf(p.A_log[hv]) * softplus_f(ld_act<ACT>(p.a, gi) + p.dt_bias[hv]);
+        be = sigmoid_f(ld_act<ACT>(p.b, gi));
       }
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const float o = __shfl_up(g, d);
+        if (lane >= d) g += o;
+      }
+      const float gl = __shfl(g, 63);
+      gam[lane] = g;
+      bet[lane] = be;
+      egam[lane] = expf(g);
+      ekc[lane] = expf(gl - g);
+      if (lane == 0) gC[0] = gl;
     }
+    gch_norm_scale<ACT, K>(rq, p, p.scale, qsc);
+    gch_norm_scale<ACT, K>(rk, p, 1.f, ksc);
+    gch_store<ACT>(rq, n, K, Qr, KS);
+    gch_store<ACT>(rk, n, K, Kr, KS);
+  }
+  {
+    raw4_t<ACT> rv[16];  // V <= 256: at most 16 groups per thread
+    const int uv = V / 16;
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+      if (m < uv) {
+        const int e = tid + 256 * m, g = V / 4;
+        const int i = e / g, col = 4 * (e - i * g);
+        rv[m] = ld_raw4<ACT, VEC>(p.qkv, rbase + (int64_t)min(i, n - 1) * p.qkv_stride +
+                                             2 * (int64_t)p.H * K + (int64_t)hv * V + col);
+      }
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+      if (m < uv) {
+        const int e = tid + 256 * m, g = V / 4;
+        const int i = e / g, col = 4 * (e - i * g);
+        stg_st4<ACT>(Vr + i * VS + col, i < n ? rv[m] : raw4_t<ACT>{});
+      }
+  }
+  __syncthreads();
+
+  if (wave == 0) {
+    fq[lane] = egam[lane] * qsc[lane];
+    fk[lane] = ekc[lane] * ksc[lane];
+    fw[lane] = bet[lane] * egam[lane] * ksc[lane];
+  }
+  // ---- Gram tiles (ti, tj), tj <= ti: 10 tiles over 4 waves.
+  //      A_ij = beta_i e^(g_i - g_j) (k_i . k_j), j < i;  P_ij = e^(g_i - g_j) (q_i . k_j), j <= i
+  for (int t = wave; t < 10; t += 4) {
+    const int ti = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
+    const int tj = t - ti * (ti + 1) / 2;
+    f4v qk = {0.f, 0.f, 0.f, 0.f}, kkm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int k0 = 0; k0 < K; k0 += 16) {
+      const ST* bk = Kr + (16 * tj + x) * KS + k0 + 4 * kk;
+      qk = gram16<ACT>(Qr + (16 * ti + x) * KS + k0 + 4 * kk, bk, qk);
+      kkm = gram16<ACT>(Kr + (16 * ti + x) * KS + k0 + 4 * kk, bk, kkm);
+    }
+    const int j = 16 * tj + x;
+    const float gj = gam[j], kj = ksc[j];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int i = 16 * ti + 4 * kk + r, j = 16 * tj + x;
-      const float dec = j <= i ? expf(gam[i] - gam[j]) : 0.f;
-      As[i * TP + j] = j < i ? bet[i] * dec * kkm[r] : 0.f;
-      Pg[i * GCH + j] = j <= i ? dec * qk[r] : 0.f;
+      const int i = 16 * ti + 4 * kk + r;
+      const float dec = j <= i ? expf(gam[i] - gj) * kj : 0.f;
+      AT[i * TP + j] = j < i ? bet[i] * ksc[i] * dec * kkm[r] : 0.f;
+      Pg[i * GCH + j] = qsc[i] * dec * qk[r];
     }
   }
-  // e^gamma q and (e^(gamma_C - gamma) k)^T to the workspace
-  const float gl = gam[GCH - 1];
-  for (int e = tid; e < GCH * K; e += 256) {
-    const int i = e / K, col = e - i * K;
-    Qg[e] = egam[i] * Qs[i * KP + col];
-    const int kc = e / GCH, j = e - kc * GCH;
-    Kg[e] = expf(gl - gam[j]) * Ks[j * KP + kc];
-  }
-  if (tid == 0) gC[0] = gl;
   __syncthreads();
 
-  // ---- V rows into the q buffer; M = (I + A)^-1 blockwise (Tm = M diag(beta),
-  // with beta folded into the W and U products below). 16x16 blocks: the
-  // diagonal blocks by forward substitution (wave b, lane m: column m of
-  // block b, held in registers), then row block by row block
-  //   M_ij = -M_ii sum_{k=j}^{i-1} A_ik M_kj   (i > j)
-  // on the matrix cores, one (i, j) per wave. An MFMA result in lane layout
-  // (lane x + 16 kk holds D[4 kk + r][x]) is exactly the B operand of the
-  // next product, so Z = sum A_ik M_kj feeds -M_ii Z without a round trip.
-  gch_stage<ACT, VEC, 16>(p.qkv, rbase, p.qkv_stride, n, 2 * (int64_t)p.H * K + (int64_t)hv * V, V, Qs, VP);
+  // ---- M = (I + A)^-1 in 16x16 blocks, in place. The diagonal blocks by
+  // forward substitution (wave b, lane m: column m of block b, held in
+  // registers; row i is overwritten only after every lane has read it). The
+  // blocks below the diagonal, row block by row block,
+  //   M_ij = -M_ii sum_{k=j}^{i-1} A_ik M_kj   (i > j),
+  // on the matrix cores, one (i, j) per wave; M_ij is stored in the unused
+  // block above the diagonal, at block position (j, i), so A stays readable.
+  // Hence the rows 16 j + r, columns 16 i + c of AT hold M_ij[r][c] for every
+  // j <= i. An MFMA result in lane layout (lane x + 16 kk holds D[4 kk + r][x])
+  // is exactly the B operand of the next product.
   if (lane < 16) {
     const int b0 = 16 * wave;
     float mc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float sacc = i == lane ? 1.f : 0.f;
+      float s = i == lane ? 1.f : 0.f;
 #pragma unroll
-      for (int j = 0; j < i; ++j) sacc -= As[(b0 + i) * TP + b0 + j] * mc[j];
-      mc[i] = sacc;
-      Ts[(b0 + i) * TP + b0 + lane] = sacc;
+      for (int j = 0; j < i; ++j) s -= AT[(b0 + i) * TP + b0 + j] * mc[j];
+      mc[i] = s;
+      AT[(b0 + i) * TP + b0 + lane] = s;
     }
+  }
+  // e^gamma q and (e^(gamma_C - gamma) k)^T to the workspace (scaled inputs)
+  for (int e = tid; e < GCH * K / 4; e += 256) {
+    const int i = e / (K / 4), col = 4 * (e - i * (K / 4));
+    const float f = fq[i];
+    const ST* s = Qr + i * KS + col;
+    *reinterpret_cast<f4*>(Qg + i * K + col) =
+        f4{f * stg_ld1<ACT>(s), f * stg_ld1<ACT>(s + 1), f * stg_ld1<ACT>(s + 2), f * stg_ld1<ACT>(s + 3)};
+    const int kc = e / (GCH / 4), j = 4 * (e - kc * (GCH / 4));
+    const ST* kr = Kr + j * KS + kc;
+    *reinterpret_cast<f4*>(Kg + kc * GCH + j) = f4{fk[j] * stg_ld1<ACT>(kr), fk[j + 1] * stg_ld1<ACT>(kr + KS),
+                                                   fk[j + 2] * stg_ld1<ACT>(kr + 2 * KS),
+                                                   fk[j + 3] * stg_ld1<ACT>(kr + 3 * KS)};
   }
   __syncthreads();
   for (int ib = 1; ib < 4; ++ib) {
@@ -223,60 +341,54 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(GdnChunkParams cp) 
       const int jb = wave;
       f4v z = {0.f, 0.f, 0.f, 0.f};
       for (int kb = jb; kb < ib; ++kb) {  // Z += A_(ib,kb) M_(kb,jb)
-        f4 bm;
-        const float* mcol = Ts + (16 * kb + 4 * kk) * TP + 16 * jb + x;
-        bm.x = mcol[0];
-        bm.y = mcol[TP];
-        bm.z = mcol[2 * TP];
-        bm.w = mcol[3 * TP];
-        z = mma16(ld4s(As + (16 * ib + x) * TP + 16 * kb + 4 * kk), bm, z);
+        const float* mcol = AT + (16 * jb + 4 * kk) * TP + 16 * kb + x;
+        const f4 bm = {mcol[0], mcol[TP], mcol[2 * TP], mcol[3 * TP]};
+        z = mma16(ld4s(AT + (16 * ib + x) * TP + 16 * kb + 4 * kk), bm, z);
       }
       f4v mij = {0.f, 0.f, 0.f, 0.f};
-      mij = mma16(ld4s(Ts + (16 * ib + x) * TP + 16 * ib + 4 * kk), f4{z[0], z[1], z[2], z[3]}, mij);
+      mij = mma16(ld4s(AT + (16 * ib + x) * TP + 16 * ib + 4 * kk), f4{z[0], z[1], z[2], z[3]}, mij);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Ts[(16 * ib + 4 * kk + r) * TP + 16 * jb + x] = -mij[r];
-    }
-    if (wave >= ib) {  // the blocks above the diagonal of this row block are zero
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int jb = wave;  // column blocks ib .. 3 of rows 16 ib ..: only jb > ib are outside the solve
-        if (jb > ib) Ts[(16 * ib + 4 * kk + r) * TP + 16 * jb + x] = 0.f;
-      }
+      for (int r = 0; r < 4; ++r) AT[(16 * jb + 4 * kk + r) * TP + 16 * ib + x] = -mij[r];
     }
     __syncthreads();
   }
-  if (wave > 0) {  // row block 0: column blocks 1 .. 3 are zero
-#pragma unroll
-    for (int r = 0; r < 4; ++r) Ts[(4 * kk + r) * TP + 16 * wave + x] = 0.f;
-  }
-  __syncthreads();
 
-  // ---- W = M diag(beta) (e^gamma k) and U = M diag(beta) V on the matrix
-  // cores; M is lower triangular, so row tile ti only contracts over tokens
-  // < 16 (ti + 1)
-  const int ntk = K / 16, ntv = V / 16;
-  for (int t = wave; t < 4 * (ntk + ntv); t += 4) {
-    const bool isw = t < 4 * ntk;
-    const int tt = isw ? t : t - 4 * ntk;
-    const int ti = tt & 3, tc = tt >> 2;
-    const float* Bm = isw ? Ks : Qs;
-    const int bs = isw ? KP : VP;
-    f4v acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < 16 * (ti + 1); j0 += 16) {
-      f4 b;
-      const int j = j0 + 4 * kk;
-      const float* col = Bm + 16 * tc + x;
-      b.x = col[(j + 0) * bs] * bet[j + 0] * (isw ? egam[j + 0] : 1.f);
-      b.y = col[(j + 1) * bs] * bet[j + 1] * (isw ? egam[j + 1] : 1.f);
-      b.z = col[(j + 2) * bs] * bet[j + 2] * (isw ? egam[j + 2] : 1.f);
-      b.w = col[(j + 3) * bs] * bet[j + 3] * (isw ? egam[j + 3] : 1.f);
-      acc = mma16(ld4s(Ts + (16 * ti + x) * TP + j), b, acc);
+  // ---- W = M diag(beta e^gamma) k and U = M diag(beta) V on the matrix
+  // cores, one 16-column tile of W or U per task, all four row tiles at once:
+  // the B tile of token block jb is built once and feeds row tiles ti >= jb
+  // (M is lower triangular).
+  const int ntk = K / 16, nt = ntk + V / 16;
+  for (int tc0 = wave; tc0 < nt; tc0 += 4) {
+    const bool isw = tc0 < ntk;
+    const int tc = isw ? tc0 : tc0 - ntk;
+    const ST* const Bm = (isw ? Kr : Vr) + 16 * tc + x;
+    const int bs = isw ? KS : VS;
+    const float* const fac = isw ? fw : bet;
+    f4v acc[4];
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) acc[ti] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      const int j = 16 * jb + 4 * kk;
+      const f4 fj = ld4s(fac + j);
+      const f4 b = {fj.x * stg_ld1<ACT>(Bm + j * bs), fj.y * stg_ld1<ACT>(Bm + (j + 1) * bs),
+                    fj.z * stg_ld1<ACT>(Bm + (j + 2) * bs), fj.w * stg_ld1<ACT>(Bm + (j + 3) * bs)};
+#pragma unroll
+      for (int ti = jb; ti < 4; ++ti) acc[ti] = mma16(ld4s(AT + (16 * jb + x) * TP + 16 * ti + 4 * kk), b, acc[ti]);
     }
     float* dst = isw ? Wg : Ug;
     const int ld = isw ? K : V;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dst[(16 * ti + 4 * kk + r) * ld + 16 * tc + x] = acc[r];
+    for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(16 * ti + 4 * kk + r) * ld + 16 * tc + x] = acc[ti][r];
   }
+}
+
+// LDS bytes of one prep block.
+inline size_t gch_prep_lds_bytes(int K, int V, int act) {
+  const size_t es = act == SSMD_F32 ? 4 : 2;
+  return sizeof(float) * ((size_t)GCH * (GCH + 4) + 9 * GCH) + es * ((size_t)2 * GCH * (K + 4) + (size_t)GCH * (V + 4));
 }
 
 // Pass 2: one block per (row, value head, 16 state rows), chunks in order.
@@ -431,8 +543,7 @@ namespace {
 template <int K, int ACT>
 hipError_t launch_gch_k(const GdnChunkParams& cp, hipStream_t st) {
   const GdnParams& p = cp.g;
-  const int KP = K + 4, VP = p.V + 4, TP = GCH + 4;
-  const size_t lds = sizeof(float) * ((size_t)GCH * (VP > KP ? VP : KP) + (size_t)GCH * KP + 2 * GCH * TP + 3 * GCH);
+  const size_t lds = gch_prep_lds_bytes(K, p.V, ACT);
   const int64_t prep_blocks = (int64_t)p.B * p.HV * cp.nck;
   if (p.qkv_vec)
     gdn_chunk_prep_kernel<K, ACT, true><<<dim3((unsigned)prep_blocks), dim3(256), lds, st>>>(cp);

@@ -91,6 +91,7 @@ CASES = [
     ("k64_v256_norm_sigmoid_f16", 1, 1, 2, 64, 256, "f16", "f32", 100, "sigmoid"),
     ("k128_v64_gqa4_f32", 3, 1, 4, 128, 64, "f32", "f32", 64, None),
     ("k64_v16_bf16_short", 4, 2, 2, 64, 16, "bf16", "bf16", 5, None),
+    ("k128_v128_f16_gqa2_ragged_tail", 2, 2, 4, 128, 128, "f16", "f16", 200, None),
 ]
 
 
