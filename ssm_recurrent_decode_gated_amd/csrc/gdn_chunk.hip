@@ -33,7 +33,6 @@
 namespace ssmd {
 
 constexpr int GCH = 64;  // tokens per chunk
-constexpr int GCH_VT = 16;  // state rows per pass-2 block
 
 // Per (row, value head, chunk) workspace record, in floats:
 //   W [64][K] | U [64][V] | e^gamma q [64][K] | (e^(gamma_C - gamma) k)^T [K][64] | P [64][64] | gamma_C
@@ -391,23 +390,31 @@ inline size_t gch_prep_lds_bytes(int K, int V, int act) {
   return sizeof(float) * ((size_t)GCH * (GCH + 4) + 9 * GCH) + es * ((size_t)2 * GCH * (K + 4) + (size_t)GCH * (V + 4));
 }
 
-// Pass 2: one block per (row, value head, 16 state rows), chunks in order.
-// Wave w takes token tile w (16 tokens) for Delta and O, and column tiles
-// w, w + 4 of the new rows. (Fetching a wave's next-chunk operands ahead
-// was measured: 6% faster at one sequence, 45% slower at eight, from the
-// registers it costs.)
-template <int K, bool NORM>
+// Pass 2: one block per (row, value head, VT state rows), chunks in order,
+// the block's rows held in LDS. Wave w takes token tile w (16 tokens) for
+// Delta and O, over all VT / 16 row tiles, so each W, e^gamma q and P operand
+// it loads feeds VT / 16 products; for the new rows it takes column tiles w,
+// w + 4 over all row tiles, each K-hat operand likewise shared. Larger VT
+// reads the per-chunk operands fewer times (V / VT blocks per head read
+// them), smaller VT gives more blocks; the host picks VT from the grid size.
+// (Fetching a wave's next-chunk operands ahead was measured: 6% faster at one
+// sequence, 45% slower at eight, from the registers it costs.)
+template <int K, int VT, bool NORM>
 __global__ __launch_bounds__(256) void gdn_chunk_state_kernel(GdnChunkParams cp) {
   const GdnParams& p = cp.g;
+  constexpr int NRT = VT / 16;       // row tiles
+  constexpr int NCT = K / 16;        // column tiles of the state
+  constexpr int CPW = (NCT + 3) / 4; // column tiles per wave
   const int V = p.V;
-  const int nvt = V / GCH_VT;
+  const int nvt = V / VT;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int x = lane & 15, kk = lane >> 4;
   constexpr int SP = K + 4;
-  __shared__ float Ss[GCH_VT * SP];
-  __shared__ float Ds[GCH][GCH_VT + 1];
+  constexpr int DP = VT + 1;
+  __shared__ float Ss[VT * SP];
+  __shared__ float Ds[GCH * DP];  // Delta^T: [token][state row]
 
   // XCD-aware block order: the tiles of one (row, head) share blockIdx % 8
   const int BH = p.B * p.HV;
@@ -422,9 +429,12 @@ __global__ __launch_bounds__(256) void gdn_chunk_state_kernel(GdnChunkParams cp)
   if (slot < 0 || slot >= p.num_slots) return;
   const int len = cp.lengths ? min(max(cp.lengths[bi], 0), cp.T) : cp.T;
   if (len == 0) return;
-  const int v0 = vt * GCH_VT;
+  const int v0 = vt * VT;
   float* const Sg = static_cast<float*>(p.state) + (((int64_t)slot * p.HV + hv) * V + v0) * (int64_t)K;
-  for (int e = tid; e < GCH_VT * K; e += 256) Ss[(e / K) * SP + e % K] = Sg[e];
+  for (int e = tid; e < VT * K / 4; e += 256) {
+    const int r = e / (K / 4), col = 4 * (e - r * (K / 4));
+    *reinterpret_cast<f4*>(Ss + r * SP + col) = *reinterpret_cast<const f4*>(Sg + r * K + col);
+  }
   __syncthreads();
 
   const int ti = wave;
@@ -438,71 +448,98 @@ __global__ __launch_bounds__(256) void gdn_chunk_state_kernel(GdnChunkParams cp)
     const float* const Pg = Kg + GCH * K;
     const float eg = expf(Pg[GCH * GCH]);
     const int t0 = c * GCH;
-    // X = W S^T, Y = (e^gamma q) S^T for this wave's 16 tokens
-    f4v X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
+    // X = W S^T and Y = (e^gamma q) S^T for this wave's 16 tokens, every row tile
+    f4v X[NRT], Y[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) X[rt] = Y[rt] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
     for (int k0 = 0; k0 < K; k0 += 16) {
-      const f4 b = ld4s(Ss + x * SP + k0 + 4 * kk);
-      X = mma16(ld4s(Wg + (16 * ti + x) * K + k0 + 4 * kk), b, X);
-      Y = mma16(ld4s(Qg + (16 * ti + x) * K + k0 + 4 * kk), b, Y);
+      const f4 aw = ld4s(Wg + (16 * ti + x) * K + k0 + 4 * kk);
+      const f4 aq = ld4s(Qg + (16 * ti + x) * K + k0 + 4 * kk);
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        const f4 b = ld4s(Ss + (16 * rt + x) * SP + k0 + 4 * kk);
+        X[rt] = mma16(aw, b, X[rt]);
+        Y[rt] = mma16(aq, b, Y[rt]);
+      }
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * ti + 4 * kk + r;
-      Ds[i][x] = Ug[i * V + v0 + x] - X[r];  // Delta^T
-    }
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * ti + 4 * kk + r;
+        Ds[i * DP + 16 * rt + x] = Ug[i * V + v0 + 16 * rt + x] - X[rt][r];  // Delta^T
+      }
     __syncthreads();
     // O = Y + P Delta^T (P lower triangular: tokens < 16 (ti + 1))
     for (int j0 = 0; j0 < 16 * (ti + 1); j0 += 16) {
       const int j = j0 + 4 * kk;
-      f4 b;
-      b.x = Ds[j][x];
-      b.y = Ds[j + 1][x];
-      b.z = Ds[j + 2][x];
-      b.w = Ds[j + 3][x];
-      Y = mma16(ld4s(Pg + (16 * ti + x) * GCH + j), b, Y);
+      const f4 a = ld4s(Pg + (16 * ti + x) * GCH + j);
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        const float* d = Ds + j * DP + 16 * rt + x;
+        Y[rt] = mma16(a, f4{d[0], d[DP], d[2 * DP], d[3 * DP]}, Y[rt]);
+      }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * ti + 4 * kk + r;
       if (t0 + i < len) {
         const int64_t o = (((int64_t)bi * cp.T + t0 + i) * p.HV + hv) * V + v0 + x;
-        if constexpr (NORM) cp.obuf[o] = Y[r];
-        else store_act1(p.out, o, p.out_dt, Y[r]);
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+          if constexpr (NORM) cp.obuf[o + 16 * rt] = Y[rt][r];
+          else store_act1(p.out, o + 16 * rt, p.out_dt, Y[rt][r]);
+        }
       }
     }
-    // S <- e^(gamma_C) S + Delta (e^(gamma_C - gamma) k): column tiles wave, wave + 4
-    f4v Sn[2];
+    // S <- e^(gamma_C) S + Delta (e^(gamma_C - gamma) k): column tiles wave + 4 q, every row tile
+    f4v Sn[CPW][NRT];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < CPW; ++q) {
       const int tc = wave + 4 * q;
-      if (tc < K / 16) {
-        f4v acc;
+      if (tc < NCT) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = eg * Ss[(4 * kk + r) * SP + 16 * tc + x];
-        for (int j0 = 0; j0 < GCH; j0 += 16) {
-          const int j = j0 + 4 * kk;
-          f4 a;
-          a.x = Ds[j][x];
-          a.y = Ds[j + 1][x];
-          a.z = Ds[j + 2][x];
-          a.w = Ds[j + 3][x];
-          acc = mma16(a, ld4s(Kg + (16 * tc + x) * GCH + j), acc);
-        }
-        Sn[q] = acc;
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Sn[q][rt][r] = eg * Ss[(16 * rt + 4 * kk + r) * SP + 16 * tc + x];
+      }
+    }
+#pragma unroll
+    for (int j0 = 0; j0 < GCH; j0 += 16) {
+      const int j = j0 + 4 * kk;
+      f4 bk[CPW];
+#pragma unroll
+      for (int q = 0; q < CPW; ++q) {
+        const int tc = wave + 4 * q;
+        if (tc < NCT) bk[q] = ld4s(Kg + (16 * tc + x) * GCH + j);
+      }
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        const float* d = Ds + j * DP + 16 * rt + x;
+        const f4 a = {d[0], d[DP], d[2 * DP], d[3 * DP]};
+#pragma unroll
+        for (int q = 0; q < CPW; ++q)
+          if (wave + 4 * q < NCT) Sn[q][rt] = mma16(a, bk[q], Sn[q][rt]);
       }
     }
     __syncthreads();  // every wave is done reading the old rows and Delta
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < CPW; ++q) {
       const int tc = wave + 4 * q;
-      if (tc < K / 16) {
+      if (tc < NCT) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Ss[(4 * kk + r) * SP + 16 * tc + x] = Sn[q][r];
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Ss[(16 * rt + 4 * kk + r) * SP + 16 * tc + x] = Sn[q][rt][r];
       }
     }
     __syncthreads();
   }
-  for (int e = tid; e < GCH_VT * K; e += 256) Sg[e] = Ss[(e / K) * SP + e % K];
+  for (int e = tid; e < VT * K / 4; e += 256) {
+    const int r = e / (K / 4), col = 4 * (e - r * (K / 4));
+    *reinterpret_cast<f4*>(Sg + r * K + col) = *reinterpret_cast<const f4*>(Ss + r * SP + col);
+  }
 }
 
 // Pass 3 (gated RMSNorm): one wave per (row, token, value head).
@@ -541,7 +578,7 @@ int64_t gdn_chunk_workspace_floats(int B, int T, int HV, int K, int V, bool norm
 namespace {
 
 template <int K, int ACT>
-hipError_t launch_gch_k(const GdnChunkParams& cp, hipStream_t st) {
+hipError_t launch_gch_k(const GdnChunkParams& cp, int n_cu, hipStream_t st) {
   const GdnParams& p = cp.g;
   const size_t lds = gch_prep_lds_bytes(K, p.V, ACT);
   const int64_t prep_blocks = (int64_t)p.B * p.HV * cp.nck;
@@ -549,34 +586,47 @@ hipError_t launch_gch_k(const GdnChunkParams& cp, hipStream_t st) {
     gdn_chunk_prep_kernel<K, ACT, true><<<dim3((unsigned)prep_blocks), dim3(256), lds, st>>>(cp);
   else
     gdn_chunk_prep_kernel<K, ACT, false><<<dim3((unsigned)prep_blocks), dim3(256), lds, st>>>(cp);
-  const int nvt = p.V / GCH_VT;
+  // state rows per block: the largest of 64 / 32 / 16 dividing V that still
+  // gives two blocks per CU (16 otherwise)
   const int64_t bh8 = ((int64_t)p.B * p.HV + 7) / 8 * 8;
-  const int64_t state_blocks = bh8 * nvt;
-  if (p.norm_gate) {
-    gdn_chunk_state_kernel<K, true><<<dim3((unsigned)state_blocks), dim3(256), 0, st>>>(cp);
+  int vt = 16;
+  for (int c : {64, 32})
+    if (p.V % c == 0 && bh8 * (p.V / c) >= 2LL * n_cu) {
+      vt = c;
+      break;
+    }
+  const dim3 sg((unsigned)(bh8 * (p.V / vt)));
+  const bool nrm = p.norm_gate != nullptr;
+  switch (vt * 2 + (nrm ? 1 : 0)) {
+    case 128: gdn_chunk_state_kernel<K, 64, false><<<sg, dim3(256), 0, st>>>(cp); break;
+    case 129: gdn_chunk_state_kernel<K, 64, true><<<sg, dim3(256), 0, st>>>(cp); break;
+    case 64: gdn_chunk_state_kernel<K, 32, false><<<sg, dim3(256), 0, st>>>(cp); break;
+    case 65: gdn_chunk_state_kernel<K, 32, true><<<sg, dim3(256), 0, st>>>(cp); break;
+    case 32: gdn_chunk_state_kernel<K, 16, false><<<sg, dim3(256), 0, st>>>(cp); break;
+    default: gdn_chunk_state_kernel<K, 16, true><<<sg, dim3(256), 0, st>>>(cp); break;
+  }
+  if (nrm) {
     const int64_t waves = (int64_t)p.B * cp.T * p.HV;
     gdn_chunk_norm_kernel<<<dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st>>>(cp);
-  } else {
-    gdn_chunk_state_kernel<K, false><<<dim3((unsigned)state_blocks), dim3(256), 0, st>>>(cp);
   }
   return hipGetLastError();
 }
 
 template <int K>
-hipError_t launch_gch_act(const GdnChunkParams& cp, hipStream_t st) {
+hipError_t launch_gch_act(const GdnChunkParams& cp, int n_cu, hipStream_t st) {
   switch (cp.g.act_dt) {
-    case SSMD_F32: return launch_gch_k<K, SSMD_F32>(cp, st);
-    case SSMD_BF16: return launch_gch_k<K, SSMD_BF16>(cp, st);
-    default: return launch_gch_k<K, SSMD_F16>(cp, st);
+    case SSMD_F32: return launch_gch_k<K, SSMD_F32>(cp, n_cu, st);
+    case SSMD_BF16: return launch_gch_k<K, SSMD_BF16>(cp, n_cu, st);
+    default: return launch_gch_k<K, SSMD_F16>(cp, n_cu, st);
   }
 }
 
 }  // namespace
 
-hipError_t launch_gdn_chunk(const GdnChunkParams& cp, hipStream_t st) {
+hipError_t launch_gdn_chunk(const GdnChunkParams& cp, int n_cu, hipStream_t st) {
   switch (cp.g.K) {
-    case 64: return launch_gch_act<64>(cp, st);
-    case 128: return launch_gch_act<128>(cp, st);
+    case 64: return launch_gch_act<64>(cp, n_cu, st);
+    case 128: return launch_gch_act<128>(cp, n_cu, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -352,7 +352,9 @@ int gdn_chunk_prefill(const void* mixed_qkv, int64_t qkv_row_stride, const void*
   cp.nck = (T + 63) / 64;
   cp.ws = static_cast<float*>(workspace);
   cp.obuf = norm_gate ? cp.ws + (ssmd::gdn_chunk_workspace_floats(B, T, HV, K, V, false)) : nullptr;
-  return launch_status(ssmd::launch_gdn_chunk(cp, stream), fn);
+  int n_cu = 0;
+  if (int rc2 = cu_count(&n_cu)) return rc2;
+  return launch_status(ssmd::launch_gdn_chunk(cp, n_cu, stream), fn);
 }
 
 int kda_decode_step(const void* x, const float* conv_weight, const float* conv_bias, void* conv_state,

@@ -155,7 +155,7 @@ bool kda_pf_supported(const KdaParams& p);
 hipError_t launch_kda_pf(const KdaParams& p, const Launch& l, int n_cu, hipStream_t s);
 hipError_t launch_gdn_conv(const GdnConvParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_gdn_multi(const GdnMultiParams& p, const Launch& l, int n_cu, hipStream_t s);
-hipError_t launch_gdn_chunk(const GdnChunkParams& p, hipStream_t s);
+hipError_t launch_gdn_chunk(const GdnChunkParams& p, int n_cu, hipStream_t s);
 int64_t gdn_chunk_workspace_floats(int B, int T, int HV, int K, int V, bool norm);
 // Largest V the multi-token kernel takes with the gated RMSNorm (one block per head).
 int gdn_multi_max_norm_rows(int K);

@@ -127,3 +127,55 @@ def test_gdn_chunk_matches_fused_recurrent():
     torch.cuda.synchronize()
     assert_mixed(outs[0], outs[1].double().numpy(), FP32_TOL, "outputs")
     assert_mixed(states[0], states[1].double().numpy(), FP32_TOL, "states")
+
+
+def _rows_per_block(B, HV, V):
+    """The state pass's rows per block as the launcher picks them: the largest
+    of 64 / 32 / 16 dividing V that still gives two blocks per CU."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    bh8 = (B * HV + 7) // 8 * 8
+    for c in (64, 32):
+        if V % c == 0 and bh8 * (V // c) >= 2 * n_cu:
+            return c
+    return 16
+
+
+ROW_TILE_CASES = [
+    # name, B, H, HV, K, V, act, out, T, norm; sized so the launcher takes 64 or 32 state rows per block
+    ("k128_v128_bf16", 8, 16, 32, 128, 128, "bf16", "f32", 130, None),
+    ("k64_v128_f16_norm", 8, 16, 32, 64, 128, "f16", "f16", 70, "silu"),
+    ("k128_v128_bf16_norm", 4, 16, 32, 128, 128, "bf16", "bf16", 100, "sigmoid"),
+    ("k64_v64_f32", 8, 8, 32, 64, 64, "f32", "f32", 66, None),
+]
+
+
+@pytest.mark.parametrize("case", ROW_TILE_CASES, ids=[c[0] for c in ROW_TILE_CASES])
+def test_gdn_chunk_row_tiles(case):
+    """Batched prompts, where the state pass holds 32 or 64 state rows per
+    block: every output and state, with ragged lengths (a zero-length row and
+    a padded row among them)."""
+    need_gpu()
+    name, B, H, HV, K, V, act, outd, T, norm = case
+    vt = _rows_per_block(B, HV, V)
+    if vt == 16:
+        pytest.skip(f"{torch.cuda.get_device_properties(0).multi_processor_count} CUs: 16 rows per block here")
+    w = W.GDNWorkload("gdn_chunk_rows_" + name, B=B, H=H, HV=HV, K=K, V=V, num_slots=B + 2, act=act, out=outd,
+                      idx="perm")
+    P, st = W.gdn_params(w), W.gdn_state(w)
+    idx = W.slot_indices(w).clone()
+    idx[1] = -1
+    lengths = torch.tensor([T - 3 * b if b != 2 else 0 for b in range(B)], dtype=torch.int32)
+    d = _inputs(w, T, norm=norm is not None)
+    out, got, ro, ref = _run(w, T, d, P, st, idx, out_dtype=outd, lengths=lengths, norm=norm)
+    for b in range(B):
+        L = int(lengths[b]) if b != 1 else 0
+        if L:
+            _check(out[b, :L], ro[b, :L], FP32_TOL, f"row {b} (rows per block {vt})")
+        if b != 1 and L < T:
+            assert (out[b, L:].float() == 7.0).all(), f"row {b} wrote past its length"
+    assert (out[1].float() == 7.0).all(), "padded row wrote output"
+    live = [int(idx[b]) for b in range(B) if b != 1]
+    assert_mixed(got[live], ref[live], FP32_TOL, f"states (rows per block {vt})")
+    for s in range(w.num_slots):
+        if s not in live:
+            assert torch.equal(got[s], st[s]), f"slot {s} changed"
