@@ -204,10 +204,11 @@ int gdn_fused_recurrent(const void* mixed_qkv, int64_t qkv_row_stride,
  * gdn_chunk_prefill -- what gdn_fused_recurrent computes (the GDN step over T
  * tokens per row, state read and written once), in chunked form for long
  * sequences: tokens in chunks of 64, each chunk's effect reduced to dense
- * products (a unit lower-triangular solve, W = Tm e^gamma k, U = Tm v) that
- * run in parallel over chunks, then one pass per 16 state rows walks the
- * chunks in order (Delta = U - W S^T, o = e^gamma q S^T + P Delta, S <-
- * e^gamma_C S + Delta e^(gamma_C - gamma) k). [LOG] "Kernel 4: Fused DeltaNet
+ * products (the Gram products and M = (I + A)^-1 of the chunk's unit
+ * lower-triangular system) that run in parallel over chunks, then one pass
+ * per tile of state rows walks the chunks in order (Delta^T = M (beta v -
+ * beta e^gamma k S^T), o = e^gamma q S^T + P Delta^T, S <- e^gamma_C S +
+ * Delta e^(gamma_C - gamma) k). [LOG] "Kernel 4: Fused DeltaNet
  * Recurrent", Math, unrolled over a chunk; [MBU] "Prefill path". The result
  * equals that of gdn_fused_recurrent up to rounding.
  *   Arguments, layouts and conventions: those of gdn_fused_recurrent, plus

@@ -8,23 +8,26 @@
 //   delta_i + beta_i sum_{j<i} e^(gamma_i - gamma_j) (k_i . k_j) delta_j
 //       = beta_i (v_i - e^(gamma_i) S0 k_i)
 // a unit lower-triangular system. With A_ij = beta_i e^(gamma_i - gamma_j)
-// (k_i . k_j) for j < i and Tm = (I + A)^-1 diag(beta):
-//   Delta^T = U - W S0^T,          U = Tm V,   W = Tm (e^gamma k)
-//   O       = (e^gamma q) S0^T + P Delta^T,    P_ij = e^(gamma_i - gamma_j) (q_i . k_j), j <= i
-//   S_C     = e^(gamma_C) S0 + Delta (e^(gamma_C - gamma) k)
-// ("Triton decode kernel + MBU analysis", "Prefill path", leaves prefill to a
-// chunked scan; this is its delta-rule form). Two passes:
+// (k_i . k_j) for j < i and M = (I + A)^-1:
+//   Delta^T = M R,     R = diag(beta) V - diag(beta e^gamma) K S0^T
+//   O       = diag(e^gamma) Q S0^T + P Delta^T,    P_ij = e^(gamma_i - gamma_j) (q_i . k_j), j <= i
+//   S_C     = e^(gamma_C) S0 + Delta diag(e^(gamma_C - gamma)) K
+// (q, k normalised; "Triton decode kernel + MBU analysis", "Prefill path",
+// leaves prefill to a chunked scan; this is its delta-rule form). Two passes:
 //   1. prep, one block per (row, value head, chunk), state-free: q and k
-//      normalised, gamma, beta, the Gram products, the triangular solve, W,
-//      U, e^gamma q, e^(gamma_C - gamma) k and P, written to a workspace;
-//   2. state, one block per (row, value head, 16 state rows), walking the
-//      chunks in order with its 16 rows in LDS: Delta, O and the new rows.
-//      The 16-row tiles of one head are mapped to one XCD, so their shared
-//      per-chunk operands are read from that XCD's L2.
+//      norms, gamma, beta, the Gram products, M by a blockwise triangular
+//      inverse, and P, written to a small per-chunk record (M, P and five
+//      per-token factors, 34 KB);
+//   2. state, one block per (row, value head, VT state rows), walking the
+//      chunks in order with its rows in LDS: R, Delta, O and the new rows,
+//      from the raw q, k, v and the record. The row tiles of one head are
+//      mapped to one XCD, so their shared per-chunk operands are read from
+//      that XCD's L2.
 // With the gated RMSNorm (over a token's V outputs, split across tiles) pass
 // 2 writes fp32 outputs to the workspace and a third pass normalises them.
-// All arithmetic is fp32; the dense products run on the matrix cores
-// (v_mfma_f32_16x16x4_f32), the triangular solve on the VALU.
+// All arithmetic is fp32 (16-bit inputs enter products exactly); the dense
+// products run on the matrix cores, the diagonal blocks of the inverse on
+// the VALU.
 #include <type_traits>
 
 #include "ssmd_device.h"
@@ -35,10 +38,12 @@ namespace ssmd {
 constexpr int GCH = 64;  // tokens per chunk
 
 // Per (row, value head, chunk) workspace record, in floats:
-//   W [64][K] | U [64][V] | e^gamma q [64][K] | (e^(gamma_C - gamma) k)^T [K][64] | P [64][64] | gamma_C
-__host__ __device__ inline int64_t gch_rec_floats(int K, int V) {
-  return 3LL * GCH * K + (int64_t)GCH * V + GCH * GCH + 4;
-}
+//   M [64][64] (blocks on and below the diagonal) | P [64][64] (likewise) |
+//   fq [64] = e^gamma q-scale | fk [64] = e^(gamma_C - gamma) k-scale |
+//   fw [64] = beta e^gamma k-scale | beta [64] | gamma_C, 3 spare
+// Per-token factors are zero past the chunk's last valid token.
+constexpr int GCH_M = 0, GCH_P = GCH * GCH, GCH_F = 2 * GCH * GCH;
+constexpr int64_t GCH_REC = 2 * GCH * GCH + 4 * GCH + 4;
 
 // The dense products run on the matrix cores: v_mfma_f32_16x16x4_f32 (fp32
 // in and out). Lane l = x + 16 kk supplies A[x][k] and B[k][x] for one k of
@@ -172,14 +177,18 @@ __device__ __forceinline__ void gch_norm_scale(const raw4_t<ACT> (&v)[UM], const
   }
 }
 
+template <int ACT>
+__device__ __forceinline__ f4 stg_ld4(const stg_t<ACT>* p) {
+  if constexpr (ACT == SSMD_F32) return ld4s(p);
+  else return raw4_to_f4<ACT>(*reinterpret_cast<const uint2*>(p));
+}
+
 template <int K, int ACT, bool VEC>
 __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(GdnChunkParams cp) {
   using ST = stg_t<ACT>;
   const GdnParams& p = cp.g;
   constexpr int KS = K + 4;  // staged row stride (elements): aligned rows, staggered banks
   constexpr int TP = GCH + 4;
-  const int V = p.V;
-  const int VS = V + 4;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -192,12 +201,8 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(GdnChunkParams cp) 
   float* const ekc = egam + GCH;         //   e^(gamma_C - gamma_i)
   float* const qsc = ekc + GCH;          //   q scale (norm * K^-1/2)
   float* const ksc = qsc + GCH;          //   k scale (norm)
-  float* const fq = ksc + GCH;           //   e^gamma_i q scale
-  float* const fk = fq + GCH;            //   e^(gamma_C - gamma_i) k scale
-  float* const fw = fk + GCH;            //   beta_i e^gamma_i k scale
-  ST* const Qr = reinterpret_cast<ST*>(fw + GCH);  // [64][KS] raw q
-  ST* const Kr = Qr + GCH * KS;                    // [64][KS] raw k
-  ST* const Vr = Kr + GCH * KS;                    // [64][VS] raw v
+  ST* const Qr = reinterpret_cast<ST*>(ksc + GCH);  // [64][KS] raw q
+  ST* const Kr = Qr + GCH * KS;                     // [64][KS] raw k
 
   const int c = blockIdx.x % cp.nck;
   const int bh = blockIdx.x / cp.nck;
@@ -210,15 +215,12 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(GdnChunkParams cp) 
   if (t0 >= len) return;
   const int n = min(GCH, len - t0);  // valid tokens; the rest act as absent (beta = g = 0, k = q = 0)
   const int h = hv / (p.HV / p.H);
-  float* const rec = cp.ws + ((int64_t)bh * cp.nck + c) * gch_rec_floats(K, V);
-  float* const Wg = rec;
-  float* const Ug = Wg + GCH * K;
-  float* const Qg = Ug + GCH * V;
-  float* const Kg = Qg + GCH * K;  // transposed: [K][64]
-  float* const Pg = Kg + GCH * K;
-  float* const gC = Pg + GCH * GCH;
+  float* const rec = cp.ws + ((int64_t)bh * cp.nck + c) * GCH_REC;
+  float* const Mg = rec + GCH_M;
+  float* const Pg = rec + GCH_P;
+  float* const Fg = rec + GCH_F;
 
-  // ---- q, k, v of the chunk's tokens: every load issued before any store
+  // ---- q, k of the chunk's tokens: every load issued before any store
   const int64_t rbase = ((int64_t)bi * cp.T + t0) * p.qkv_stride;
   {
     raw4_t<ACT> rq[K / 16], rk[K / 16];
@@ -242,38 +244,21 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(GdnChunkParams cp) 
       bet[lane] = be;
       egam[lane] = expf(g);
       ekc[lane] = expf(gl - g);
-      if (lane == 0) gC[0] = gl;
+      if (lane < 4) Fg[4 * GCH + lane] = lane == 0 ? gl : 0.f;
     }
     gch_norm_scale<ACT, K>(rq, p, p.scale, qsc);
     gch_norm_scale<ACT, K>(rk, p, 1.f, ksc);
     gch_store<ACT>(rq, n, K, Qr, KS);
     gch_store<ACT>(rk, n, K, Kr, KS);
   }
-  {
-    raw4_t<ACT> rv[16];  // V <= 256: at most 16 groups per thread
-    const int uv = V / 16;
-#pragma unroll
-    for (int m = 0; m < 16; ++m)
-      if (m < uv) {
-        const int e = tid + 256 * m, g = V / 4;
-        const int i = e / g, col = 4 * (e - i * g);
-        rv[m] = ld_raw4<ACT, VEC>(p.qkv, rbase + (int64_t)min(i, n - 1) * p.qkv_stride +
-                                             2 * (int64_t)p.H * K + (int64_t)hv * V + col);
-      }
-#pragma unroll
-    for (int m = 0; m < 16; ++m)
-      if (m < uv) {
-        const int e = tid + 256 * m, g = V / 4;
-        const int i = e / g, col = 4 * (e - i * g);
-        stg_st4<ACT>(Vr + i * VS + col, i < n ? rv[m] : raw4_t<ACT>{});
-      }
-  }
   __syncthreads();
 
-  if (wave == 0) {
-    fq[lane] = egam[lane] * qsc[lane];
-    fk[lane] = ekc[lane] * ksc[lane];
-    fw[lane] = bet[lane] * egam[lane] * ksc[lane];
+  if (wave == 0) {  // the record's per-token factors, zero past the last valid token
+    const bool ok = lane < n;
+    Fg[lane] = ok ? egam[lane] * qsc[lane] : 0.f;
+    Fg[GCH + lane] = ok ? ekc[lane] * ksc[lane] : 0.f;
+    Fg[2 * GCH + lane] = ok ? bet[lane] * egam[lane] * ksc[lane] : 0.f;
+    Fg[3 * GCH + lane] = ok ? bet[lane] : 0.f;
   }
   // ---- Gram tiles (ti, tj), tj <= ti: 10 tiles over 4 waves.
   //      A_ij = beta_i e^(g_i - g_j) (k_i . k_j), j < i;  P_ij = e^(g_i - g_j) (q_i . k_j), j <= i
@@ -321,19 +306,6 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(GdnChunkParams cp) 
       AT[(b0 + i) * TP + b0 + lane] = s;
     }
   }
-  // e^gamma q and (e^(gamma_C - gamma) k)^T to the workspace (scaled inputs)
-  for (int e = tid; e < GCH * K / 4; e += 256) {
-    const int i = e / (K / 4), col = 4 * (e - i * (K / 4));
-    const float f = fq[i];
-    const ST* s = Qr + i * KS + col;
-    *reinterpret_cast<f4*>(Qg + i * K + col) =
-        f4{f * stg_ld1<ACT>(s), f * stg_ld1<ACT>(s + 1), f * stg_ld1<ACT>(s + 2), f * stg_ld1<ACT>(s + 3)};
-    const int kc = e / (GCH / 4), j = 4 * (e - kc * (GCH / 4));
-    const ST* kr = Kr + j * KS + kc;
-    *reinterpret_cast<f4*>(Kg + kc * GCH + j) = f4{fk[j] * stg_ld1<ACT>(kr), fk[j + 1] * stg_ld1<ACT>(kr + KS),
-                                                   fk[j + 2] * stg_ld1<ACT>(kr + 2 * KS),
-                                                   fk[j + 3] * stg_ld1<ACT>(kr + 3 * KS)};
-  }
   __syncthreads();
   for (int ib = 1; ib < 4; ++ib) {
     if (wave < ib) {
@@ -351,70 +323,52 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(GdnChunkParams cp) 
     }
     __syncthreads();
   }
-
-  // ---- W = M diag(beta e^gamma) k and U = M diag(beta) V on the matrix
-  // cores, one 16-column tile of W or U per task, all four row tiles at once:
-  // the B tile of token block jb is built once and feeds row tiles ti >= jb
-  // (M is lower triangular).
-  const int ntk = K / 16, nt = ntk + V / 16;
-  for (int tc0 = wave; tc0 < nt; tc0 += 4) {
-    const bool isw = tc0 < ntk;
-    const int tc = isw ? tc0 : tc0 - ntk;
-    const ST* const Bm = (isw ? Kr : Vr) + 16 * tc + x;
-    const int bs = isw ? KS : VS;
-    const float* const fac = isw ? fw : bet;
-    f4v acc[4];
-#pragma unroll
-    for (int ti = 0; ti < 4; ++ti) acc[ti] = f4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      const int j = 16 * jb + 4 * kk;
-      const f4 fj = ld4s(fac + j);
-      const f4 b = {fj.x * stg_ld1<ACT>(Bm + j * bs), fj.y * stg_ld1<ACT>(Bm + (j + 1) * bs),
-                    fj.z * stg_ld1<ACT>(Bm + (j + 2) * bs), fj.w * stg_ld1<ACT>(Bm + (j + 3) * bs)};
-#pragma unroll
-      for (int ti = jb; ti < 4; ++ti) acc[ti] = mma16(ld4s(AT + (16 * jb + x) * TP + 16 * ti + 4 * kk), b, acc[ti]);
-    }
-    float* dst = isw ? Wg : Ug;
-    const int ld = isw ? K : V;
-#pragma unroll
-    for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(16 * ti + 4 * kk + r) * ld + 16 * tc + x] = acc[ti][r];
+  // ---- M to the workspace, row-major, the 10 blocks on and below the diagonal
+  for (int e = tid; e < 10 * 64; e += 256) {
+    const int t = e >> 6;
+    const int ib = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
+    const int jb = t - ib * (ib + 1) / 2;
+    const int r = (e & 63) >> 2, c4 = 4 * (e & 3);
+    *reinterpret_cast<f4*>(Mg + (16 * ib + r) * GCH + 16 * jb + c4) = ld4s(AT + (16 * jb + r) * TP + 16 * ib + c4);
   }
 }
 
 // LDS bytes of one prep block.
-inline size_t gch_prep_lds_bytes(int K, int V, int act) {
+inline size_t gch_prep_lds_bytes(int K, int act) {
   const size_t es = act == SSMD_F32 ? 4 : 2;
-  return sizeof(float) * ((size_t)GCH * (GCH + 4) + 9 * GCH) + es * ((size_t)2 * GCH * (K + 4) + (size_t)GCH * (V + 4));
+  return sizeof(float) * ((size_t)GCH * (GCH + 4) + 6 * GCH) + es * 2 * (size_t)GCH * (K + 4);
 }
 
 // Pass 2: one block per (row, value head, VT state rows), chunks in order,
-// the block's rows held in LDS. Wave w takes token tile w (16 tokens) for
-// Delta and O, over all VT / 16 row tiles, so each W, e^gamma q and P operand
-// it loads feeds VT / 16 products; for the new rows it takes column tiles w,
-// w + 4 over all row tiles, each K-hat operand likewise shared. Larger VT
-// reads the per-chunk operands fewer times (V / VT blocks per head read
-// them), smaller VT gives more blocks; the host picks VT from the grid size.
-// (Fetching a wave's next-chunk operands ahead was measured: 6% faster at one
-// sequence, 45% slower at eight, from the registers it costs.)
-template <int K, int VT, bool NORM>
+// the block's rows in LDS. Per chunk: the chunk's raw k and the record's
+// factors are staged in LDS; wave w takes token tile w (16 tokens) for
+//   Z = K S^T, Y = Q S^T (q from memory, k from LDS), R = diag(beta) V - diag(fw) Z,
+//   Delta^T = M R, O = diag(fq) Y + P Delta^T
+// over every row tile, so each q, M and P operand it loads feeds VT / 16
+// products; for the new rows S <- e^(gamma_C) S + Delta diag(fk) K it takes
+// column tiles w, w + 4 over every row tile. Larger VT reads the per-chunk
+// operands fewer times (V / VT blocks per head read them), smaller VT gives
+// more blocks; the host picks VT from the grid size.
+template <int K, int VT, bool NORM, int ACT>
 __global__ __launch_bounds__(256) void gdn_chunk_state_kernel(GdnChunkParams cp) {
+  using ST = stg_t<ACT>;
   const GdnParams& p = cp.g;
   constexpr int NRT = VT / 16;       // row tiles
   constexpr int NCT = K / 16;        // column tiles of the state
   constexpr int CPW = (NCT + 3) / 4; // column tiles per wave
+  constexpr int SP = K + 4;
+  constexpr int DP = VT + 1;
+  constexpr int KS = K + 4;
   const int V = p.V;
   const int nvt = V / VT;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int x = lane & 15, kk = lane >> 4;
-  constexpr int SP = K + 4;
-  constexpr int DP = VT + 1;
   __shared__ float Ss[VT * SP];
-  __shared__ float Ds[GCH * DP];  // Delta^T: [token][state row]
+  __shared__ float Rs[GCH * DP];   // R, then Delta^T: [token][state row]
+  __shared__ ST Kst[GCH * KS];     // the chunk's raw k
+  __shared__ float Fs[4 * GCH + 4];  // fq | fk | fw | beta | gamma_C
 
   // XCD-aware block order: the tiles of one (row, head) share blockIdx % 8
   const int BH = p.B * p.HV;
@@ -429,62 +383,113 @@ __global__ __launch_bounds__(256) void gdn_chunk_state_kernel(GdnChunkParams cp)
   if (slot < 0 || slot >= p.num_slots) return;
   const int len = cp.lengths ? min(max(cp.lengths[bi], 0), cp.T) : cp.T;
   if (len == 0) return;
+  const int h = hv / (p.HV / p.H);
+  const bool vec = p.qkv_vec;
   const int v0 = vt * VT;
   float* const Sg = static_cast<float*>(p.state) + (((int64_t)slot * p.HV + hv) * V + v0) * (int64_t)K;
   for (int e = tid; e < VT * K / 4; e += 256) {
     const int r = e / (K / 4), col = 4 * (e - r * (K / 4));
     *reinterpret_cast<f4*>(Ss + r * SP + col) = *reinterpret_cast<const f4*>(Sg + r * K + col);
   }
-  __syncthreads();
 
   const int ti = wave;
   const int nchunks = (len + GCH - 1) / GCH;
   for (int c = 0; c < nchunks; ++c) {
-    const float* const rec = cp.ws + ((int64_t)bh * cp.nck + c) * gch_rec_floats(K, V);
-    const float* const Wg = rec;
-    const float* const Ug = Wg + GCH * K;
-    const float* const Qg = Ug + GCH * V;
-    const float* const Kg = Qg + GCH * K;
-    const float* const Pg = Kg + GCH * K;
-    const float eg = expf(Pg[GCH * GCH]);
+    const float* const rec = cp.ws + ((int64_t)bh * cp.nck + c) * GCH_REC;
     const int t0 = c * GCH;
-    // X = W S^T and Y = (e^gamma q) S^T for this wave's 16 tokens, every row tile
-    f4v X[NRT], Y[NRT];
+    const int n = min(GCH, len - t0);
+    const int64_t rbase = ((int64_t)bi * cp.T + t0) * p.qkv_stride;
+    {
+      raw4_t<ACT> rk[K / 16];
+      if (vec) gch_load<ACT, true>(p.qkv, rbase, p.qkv_stride, n, (int64_t)(p.H + h) * K, K, rk);
+      else gch_load<ACT, false>(p.qkv, rbase, p.qkv_stride, n, (int64_t)(p.H + h) * K, K, rk);
+      f4 fv;
+      if (tid < GCH + 1) fv = ld4s(rec + GCH_F + 4 * tid);
+      gch_store<ACT>(rk, n, K, Kst, KS);
+      if (tid < GCH + 1) *reinterpret_cast<f4*>(Fs + 4 * tid) = fv;
+    }
+    // this wave's rows of M and P (blocks on and below the diagonal)
+    f4 mA[4], pA[4];
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) X[rt] = Y[rt] = f4v{0.f, 0.f, 0.f, 0.f};
+    for (int jb = 0; jb < 4; ++jb)
+      if (jb <= ti) {
+        mA[jb] = ld4s(rec + GCH_M + (16 * ti + x) * GCH + 16 * jb + 4 * kk);
+        pA[jb] = ld4s(rec + GCH_P + (16 * ti + x) * GCH + 16 * jb + 4 * kk);
+      }
+    __syncthreads();  // Kst, Fs and the rows of S in place
+    const float* const fq = Fs;
+    const float* const fk = Fs + GCH;
+    const float* const fw = Fs + 2 * GCH;
+    const float* const bt = Fs + 3 * GCH;
+    const float eg = expf(Fs[4 * GCH]);
+
+    // Z = K S^T and Y = Q S^T for this wave's 16 tokens, every row tile
+    f4v Y[NRT], Z[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) Y[rt] = Z[rt] = f4v{0.f, 0.f, 0.f, 0.f};
+    const int64_t qoff = rbase + (int64_t)min(16 * ti + x, n - 1) * p.qkv_stride + (int64_t)h * K + 4 * kk;
+    const ST* const krow = Kst + (16 * ti + x) * KS + 4 * kk;
 #pragma unroll 4
     for (int k0 = 0; k0 < K; k0 += 16) {
-      const f4 aw = ld4s(Wg + (16 * ti + x) * K + k0 + 4 * kk);
-      const f4 aq = ld4s(Qg + (16 * ti + x) * K + k0 + 4 * kk);
+      const f4 aq = vec ? raw4_to_f4<ACT>(ld_raw4<ACT, true>(p.qkv, qoff + k0))
+                        : raw4_to_f4<ACT>(ld_raw4<ACT, false>(p.qkv, qoff + k0));
+      const f4 ak = stg_ld4<ACT>(krow + k0);
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
         const f4 b = ld4s(Ss + (16 * rt + x) * SP + k0 + 4 * kk);
-        X[rt] = mma16(aw, b, X[rt]);
         Y[rt] = mma16(aq, b, Y[rt]);
+        Z[rt] = mma16(ak, b, Z[rt]);
       }
     }
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * ti + 4 * kk + r;
-        Ds[i * DP + 16 * rt + x] = Ug[i * V + v0 + 16 * rt + x] - X[rt][r];  // Delta^T
-      }
-    __syncthreads();
-    // O = Y + P Delta^T (P lower triangular: tokens < 16 (ti + 1))
-    for (int j0 = 0; j0 < 16 * (ti + 1); j0 += 16) {
-      const int j = j0 + 4 * kk;
-      const f4 a = ld4s(Pg + (16 * ti + x) * GCH + j);
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        const float* d = Ds + j * DP + 16 * rt + x;
-        Y[rt] = mma16(a, f4{d[0], d[DP], d[2 * DP], d[3 * DP]}, Y[rt]);
-      }
-    }
+    // R = diag(beta) V - diag(fw) Z (rows past n are zero: beta = fw = 0)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * ti + 4 * kk + r;
-      if (t0 + i < len) {
+      const float fqi = fq[i], fwi = fw[i], bti = bt[i];
+      const int64_t vo = rbase + (int64_t)min(i, n - 1) * p.qkv_stride + 2 * (int64_t)p.H * K + (int64_t)hv * V +
+                         v0 + x;
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        Rs[i * DP + 16 * rt + x] = bti * ld_act<ACT>(p.qkv, vo + 16 * rt) - fwi * Z[rt][r];
+        Y[rt][r] *= fqi;
+      }
+    }
+    __syncthreads();
+    // Delta^T = M R (M lower triangular: tokens < 16 (ti + 1))
+    f4v D[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) D[rt] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+      if (jb <= ti) {
+        const int j = 16 * jb + 4 * kk;
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+          const float* d = Rs + j * DP + 16 * rt + x;
+          D[rt] = mma16(mA[jb], f4{d[0], d[DP], d[2 * DP], d[3 * DP]}, D[rt]);
+        }
+      }
+    __syncthreads();  // every wave has read R
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Rs[(16 * ti + 4 * kk + r) * DP + 16 * rt + x] = D[rt][r];
+    __syncthreads();
+    // O = Y + P Delta^T
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+      if (jb <= ti) {
+        const int j = 16 * jb + 4 * kk;
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+          const float* d = Rs + j * DP + 16 * rt + x;
+          Y[rt] = mma16(pA[jb], f4{d[0], d[DP], d[2 * DP], d[3 * DP]}, Y[rt]);
+        }
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * ti + 4 * kk + r;
+      if (i < n) {
         const int64_t o = (((int64_t)bi * cp.T + t0 + i) * p.HV + hv) * V + v0 + x;
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
@@ -493,7 +498,7 @@ __global__ __launch_bounds__(256) void gdn_chunk_state_kernel(GdnChunkParams cp)
         }
       }
     }
-    // S <- e^(gamma_C) S + Delta (e^(gamma_C - gamma) k): column tiles wave + 4 q, every row tile
+    // S <- e^(gamma_C) S + Delta diag(fk) K: column tiles wave + 4 q, every row tile
     f4v Sn[CPW][NRT];
 #pragma unroll
     for (int q = 0; q < CPW; ++q) {
@@ -512,18 +517,22 @@ __global__ __launch_bounds__(256) void gdn_chunk_state_kernel(GdnChunkParams cp)
 #pragma unroll
       for (int q = 0; q < CPW; ++q) {
         const int tc = wave + 4 * q;
-        if (tc < NCT) bk[q] = ld4s(Kg + (16 * tc + x) * GCH + j);
+        if (tc < NCT) {
+          const ST* kc = Kst + j * KS + 16 * tc + x;
+          bk[q] = f4{fk[j] * stg_ld1<ACT>(kc), fk[j + 1] * stg_ld1<ACT>(kc + KS),
+                     fk[j + 2] * stg_ld1<ACT>(kc + 2 * KS), fk[j + 3] * stg_ld1<ACT>(kc + 3 * KS)};
+        }
       }
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
-        const float* d = Ds + j * DP + 16 * rt + x;
+        const float* d = Rs + j * DP + 16 * rt + x;
         const f4 a = {d[0], d[DP], d[2 * DP], d[3 * DP]};
 #pragma unroll
         for (int q = 0; q < CPW; ++q)
           if (wave + 4 * q < NCT) Sn[q][rt] = mma16(a, bk[q], Sn[q][rt]);
       }
     }
-    __syncthreads();  // every wave is done reading the old rows and Delta
+    __syncthreads();  // every wave is done reading the old rows, Delta, Kst and Fs
 #pragma unroll
     for (int q = 0; q < CPW; ++q) {
       const int tc = wave + 4 * q;
@@ -534,8 +543,8 @@ __global__ __launch_bounds__(256) void gdn_chunk_state_kernel(GdnChunkParams cp)
           for (int r = 0; r < 4; ++r) Ss[(16 * rt + 4 * kk + r) * SP + 16 * tc + x] = Sn[q][rt][r];
       }
     }
-    __syncthreads();
   }
+  __syncthreads();
   for (int e = tid; e < VT * K / 4; e += 256) {
     const int r = e / (K / 4), col = 4 * (e - r * (K / 4));
     *reinterpret_cast<f4*>(Sg + r * K + col) = *reinterpret_cast<const f4*>(Ss + r * SP + col);
@@ -571,16 +580,23 @@ __global__ __launch_bounds__(256) void gdn_chunk_norm_kernel(GdnChunkParams cp) 
 }
 
 int64_t gdn_chunk_workspace_floats(int B, int T, int HV, int K, int V, bool norm) {
+  (void)K;
   const int64_t nck = (T + GCH - 1) / GCH;
-  return (int64_t)B * HV * nck * gch_rec_floats(K, V) + (norm ? (int64_t)B * T * HV * V : 0);
+  return (int64_t)B * HV * nck * GCH_REC + (norm ? (int64_t)B * T * HV * V : 0);
 }
 
 namespace {
 
+template <int K, int VT, int ACT>
+void launch_gch_state(const GdnChunkParams& cp, dim3 grid, hipStream_t st) {
+  if (cp.g.norm_gate) gdn_chunk_state_kernel<K, VT, true, ACT><<<grid, dim3(256), 0, st>>>(cp);
+  else gdn_chunk_state_kernel<K, VT, false, ACT><<<grid, dim3(256), 0, st>>>(cp);
+}
+
 template <int K, int ACT>
 hipError_t launch_gch_k(const GdnChunkParams& cp, int n_cu, hipStream_t st) {
   const GdnParams& p = cp.g;
-  const size_t lds = gch_prep_lds_bytes(K, p.V, ACT);
+  const size_t lds = gch_prep_lds_bytes(K, ACT);
   const int64_t prep_blocks = (int64_t)p.B * p.HV * cp.nck;
   if (p.qkv_vec)
     gdn_chunk_prep_kernel<K, ACT, true><<<dim3((unsigned)prep_blocks), dim3(256), lds, st>>>(cp);
@@ -596,16 +612,10 @@ hipError_t launch_gch_k(const GdnChunkParams& cp, int n_cu, hipStream_t st) {
       break;
     }
   const dim3 sg((unsigned)(bh8 * (p.V / vt)));
-  const bool nrm = p.norm_gate != nullptr;
-  switch (vt * 2 + (nrm ? 1 : 0)) {
-    case 128: gdn_chunk_state_kernel<K, 64, false><<<sg, dim3(256), 0, st>>>(cp); break;
-    case 129: gdn_chunk_state_kernel<K, 64, true><<<sg, dim3(256), 0, st>>>(cp); break;
-    case 64: gdn_chunk_state_kernel<K, 32, false><<<sg, dim3(256), 0, st>>>(cp); break;
-    case 65: gdn_chunk_state_kernel<K, 32, true><<<sg, dim3(256), 0, st>>>(cp); break;
-    case 32: gdn_chunk_state_kernel<K, 16, false><<<sg, dim3(256), 0, st>>>(cp); break;
-    default: gdn_chunk_state_kernel<K, 16, true><<<sg, dim3(256), 0, st>>>(cp); break;
-  }
-  if (nrm) {
+  if (vt == 64) launch_gch_state<K, 64, ACT>(cp, sg, st);
+  else if (vt == 32) launch_gch_state<K, 32, ACT>(cp, sg, st);
+  else launch_gch_state<K, 16, ACT>(cp, sg, st);
+  if (p.norm_gate) {
     const int64_t waves = (int64_t)p.B * cp.T * p.HV;
     gdn_chunk_norm_kernel<<<dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st>>>(cp);
   }

@@ -229,5 +229,5 @@ def test_gdn_chunk_prefill_host_validation():
     assert call(ws=0x90004) == BAD_SHAPE
     assert call(T=0, ws=None) == OK
     need = L.gdn_chunk_workspace_bytes(2, 128, 32, 128, 128, 0)
-    assert need == 4 * 2 * 32 * 2 * (3 * 64 * 128 + 64 * 128 + 64 * 64 + 4)
+    assert need == 4 * 2 * 32 * 2 * (2 * 64 * 64 + 4 * 64 + 4)  # per chunk: M, P, four token factors, gamma_C
     assert L.gdn_chunk_workspace_bytes(2, 128, 32, 128, 128, 1) == need + 4 * 2 * 128 * 32 * 128
