@@ -365,10 +365,10 @@ __global__ __launch_bounds__(256) void gdn_chunk_state_kernel(GdnChunkParams cp)
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int x = lane & 15, kk = lane >> 4;
-  __shared__ float Ss[VT * SP];
-  __shared__ float Rs[GCH * DP];   // R, then Delta^T: [token][state row]
-  __shared__ ST Kst[GCH * KS];     // the chunk's raw k
-  __shared__ float Fs[4 * GCH + 4];  // fq | fk | fw | beta | gamma_C
+  __shared__ __attribute__((aligned(16))) float Ss[VT * SP];
+  __shared__ __attribute__((aligned(16))) float Rs[GCH * DP];  // R, then Delta^T: [token][state row]
+  __shared__ __attribute__((aligned(16))) ST Kst[GCH * KS];    // the chunk's raw k
+  __shared__ __attribute__((aligned(16))) float Fs[4 * GCH + 4];  // fq | fk | fw | beta | gamma_C
 
   // XCD-aware block order: the tiles of one (row, head) share blockIdx % 8
   const int BH = p.B * p.HV;
@@ -551,6 +551,277 @@ __global__ __launch_bounds__(256) void gdn_chunk_state_kernel(GdnChunkParams cp)
   }
 }
 
+// ---- bf16 inputs: three-way split products
+// An fp32 value v splits exactly into three bf16 values, v = h + m + l: h is v
+// rounded to bf16, m the remainder rounded, l the rest (at most 8 significant
+// bits, so exact). A product of a bf16 operand with v is then the sum of three
+// exact bf16 x bf16 products, accumulated in fp32: fp32 accuracy at the bf16
+// matrix-core rate (v_mfma_f32_16x16x16_bf16 covers 16 contraction indices in
+// the time v_mfma_f32_16x16x4_f32 covers 4 at a quarter of the rate).
+__device__ __forceinline__ void split3(float v, uint32_t& h, uint32_t& m, uint32_t& l) {
+  h = f32_to_bf16_bits(v);
+  const float r1 = v - bf16_bits_to_f32(h);
+  m = f32_to_bf16_bits(r1);
+  l = f32_to_bf16_bits(r1 - bf16_bits_to_f32(m));
+}
+
+__device__ __forceinline__ f4v mma_bf16(uint2 a, uint2 b, f4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4v, a), __builtin_bit_cast(s4v, b), c, 0, 0,
+                                                    0);
+}
+
+// A (bf16, one lane's 4 values) times B given as three bf16 planes.
+__device__ __forceinline__ f4v mma_x3(uint2 a, uint2 bh, uint2 bm, uint2 bl, f4v c) {
+  c = mma_bf16(a, bl, c);
+  c = mma_bf16(a, bm, c);
+  return mma_bf16(a, bh, c);
+}
+
+// Pass 2 for bf16 inputs: the pass above with Z = K S^T, Y = Q S^T and the row
+// update (Delta diag(fk)) K as three-way split products. The block's rows live
+// in registers across chunks (the row-update accumulators: lane x + 16 kk
+// holds rows 16 rt + 4 kk + r, column 16 tc + x) and in LDS only as their
+// three bf16 planes, the B operand of Z and Y; Delta diag(fk) is written as
+// three planes too, row-major over tokens, the A operand of the row update.
+template <int K, int VT, bool NORM>
+__global__ __launch_bounds__(256) void gdn_chunk_state_x3_kernel(GdnChunkParams cp) {
+  const GdnParams& p = cp.g;
+  constexpr int NRT = VT / 16;       // row tiles
+  constexpr int NCT = K / 16;        // column tiles of the state
+  constexpr int CPW = (NCT + 3) / 4; // column tiles per wave
+  constexpr int SB = K + 4;          // plane row stride (16-bit elements)
+  constexpr int DB = GCH + 4;        // Delta-plane row stride
+  constexpr int DP = VT + 1;
+  constexpr int KS = K + 4;
+  const int V = p.V;
+  const int nvt = V / VT;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int x = lane & 15, kk = lane >> 4;
+  __shared__ __attribute__((aligned(16))) uint16_t Sp[3][VT * SB];  // the rows of S as bf16 planes
+  __shared__ __attribute__((aligned(16))) uint16_t Dq[3][VT * DB];  // Delta diag(fk) as bf16 planes: [state row][token]
+  __shared__ __attribute__((aligned(16))) float Rs[GCH * DP];  // R, then Delta^T: [token][state row]
+  __shared__ __attribute__((aligned(16))) uint16_t Kst[GCH * KS];  // the chunk's raw k
+  __shared__ __attribute__((aligned(16))) float Fs[4 * GCH + 4];  // fq | fk | fw | beta | gamma_C
+
+  const int BH = p.B * p.HV;
+  const int id = blockIdx.x;
+  const int lo = id % 8, rest = id / 8;
+  const int vt = rest % nvt;
+  const int bh = (rest / nvt) * 8 + lo;
+  if (bh >= BH) return;
+  const int hv = bh % p.HV;
+  const int bi = bh / p.HV;
+  const int slot = p.idx[bi];
+  if (slot < 0 || slot >= p.num_slots) return;
+  const int len = cp.lengths ? min(max(cp.lengths[bi], 0), cp.T) : cp.T;
+  if (len == 0) return;
+  const int h = hv / (p.HV / p.H);
+  const bool vec = p.qkv_vec;
+  const int v0 = vt * VT;
+  float* const Sg = static_cast<float*>(p.state) + (((int64_t)slot * p.HV + hv) * V + v0) * (int64_t)K;
+
+  // this wave's part of S: column tiles wave + 4 q, every row tile, in registers
+  f4v Sn[CPW][NRT];
+#pragma unroll
+  for (int q = 0; q < CPW; ++q) {
+    const int tc = wave + 4 * q;
+    if (tc < NCT) {
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Sn[q][rt][r] = Sg[(16 * rt + 4 * kk + r) * K + 16 * tc + x];
+    }
+  }
+  auto put_planes = [&]() {
+#pragma unroll
+    for (int q = 0; q < CPW; ++q) {
+      const int tc = wave + 4 * q;
+      if (tc < NCT) {
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            uint32_t a, b, c;
+            split3(Sn[q][rt][r], a, b, c);
+            const int o = (16 * rt + 4 * kk + r) * SB + 16 * tc + x;
+            Sp[0][o] = (uint16_t)a;
+            Sp[1][o] = (uint16_t)b;
+            Sp[2][o] = (uint16_t)c;
+          }
+      }
+    }
+  };
+  put_planes();
+
+  const int ti = wave;
+  const int nchunks = (len + GCH - 1) / GCH;
+  for (int c = 0; c < nchunks; ++c) {
+    const float* const rec = cp.ws + ((int64_t)bh * cp.nck + c) * GCH_REC;
+    const int t0 = c * GCH;
+    const int n = min(GCH, len - t0);
+    const int64_t rbase = ((int64_t)bi * cp.T + t0) * p.qkv_stride;
+    {
+      raw4_t<SSMD_BF16> rk[K / 16];
+      if (vec) gch_load<SSMD_BF16, true>(p.qkv, rbase, p.qkv_stride, n, (int64_t)(p.H + h) * K, K, rk);
+      else gch_load<SSMD_BF16, false>(p.qkv, rbase, p.qkv_stride, n, (int64_t)(p.H + h) * K, K, rk);
+      f4 fv;
+      if (tid < GCH + 1) fv = ld4s(rec + GCH_F + 4 * tid);
+      gch_store<SSMD_BF16>(rk, n, K, Kst, KS);
+      if (tid < GCH + 1) *reinterpret_cast<f4*>(Fs + 4 * tid) = fv;
+    }
+    f4 mA[4], pA[4];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+      if (jb <= ti) {
+        mA[jb] = ld4s(rec + GCH_M + (16 * ti + x) * GCH + 16 * jb + 4 * kk);
+        pA[jb] = ld4s(rec + GCH_P + (16 * ti + x) * GCH + 16 * jb + 4 * kk);
+      }
+    __syncthreads();  // Kst, Fs and the planes of S in place
+    const float* const fq = Fs;
+    const float* const fk = Fs + GCH;
+    const float* const fw = Fs + 2 * GCH;
+    const float* const bt = Fs + 3 * GCH;
+    const float eg = expf(Fs[4 * GCH]);
+
+    // Z = K S^T and Y = Q S^T, three-way split in S
+    f4v Y[NRT], Z[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) Y[rt] = Z[rt] = f4v{0.f, 0.f, 0.f, 0.f};
+    const int64_t qoff = rbase + (int64_t)min(16 * ti + x, n - 1) * p.qkv_stride + (int64_t)h * K + 4 * kk;
+    const uint16_t* const krow = Kst + (16 * ti + x) * KS + 4 * kk;
+#pragma unroll 4
+    for (int k0 = 0; k0 < K; k0 += 16) {
+      const uint2 aq = vec ? ld_raw4<SSMD_BF16, true>(p.qkv, qoff + k0) : ld_raw4<SSMD_BF16, false>(p.qkv, qoff + k0);
+      const uint2 ak = *reinterpret_cast<const uint2*>(krow + k0);
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        const int o = (16 * rt + x) * SB + k0 + 4 * kk;
+        const uint2 bh = *reinterpret_cast<const uint2*>(&Sp[0][o]);
+        const uint2 bm = *reinterpret_cast<const uint2*>(&Sp[1][o]);
+        const uint2 bl = *reinterpret_cast<const uint2*>(&Sp[2][o]);
+        Y[rt] = mma_x3(aq, bh, bm, bl, Y[rt]);
+        Z[rt] = mma_x3(ak, bh, bm, bl, Z[rt]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * ti + 4 * kk + r;
+      const float fqi = fq[i], fwi = fw[i], bti = bt[i];
+      const int64_t vo = rbase + (int64_t)min(i, n - 1) * p.qkv_stride + 2 * (int64_t)p.H * K + (int64_t)hv * V +
+                         v0 + x;
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        Rs[i * DP + 16 * rt + x] = bti * ld_act<SSMD_BF16>(p.qkv, vo + 16 * rt) - fwi * Z[rt][r];
+        Y[rt][r] *= fqi;
+      }
+    }
+    __syncthreads();
+    // Delta^T = M R
+    f4v D[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) D[rt] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+      if (jb <= ti) {
+        const int j = 16 * jb + 4 * kk;
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+          const float* d = Rs + j * DP + 16 * rt + x;
+          D[rt] = mma16(mA[jb], f4{d[0], d[DP], d[2 * DP], d[3 * DP]}, D[rt]);
+        }
+      }
+    __syncthreads();  // every wave has read R
+    {
+      // Delta^T into Rs; Delta diag(fk) as planes: lane x + 16 kk holds tokens
+      // 16 ti + 4 kk .. + 3 of state row 16 rt + x, one 64-bit store per plane
+      const f4 fk4 = ld4s(fk + 16 * ti + 4 * kk);
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        uint32_t a[4], b[4], cc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          Rs[(16 * ti + 4 * kk + r) * DP + 16 * rt + x] = D[rt][r];
+          split3(D[rt][r] * fk4[r], a[r], b[r], cc[r]);
+        }
+        const int o = (16 * rt + x) * DB + 16 * ti + 4 * kk;
+        *reinterpret_cast<uint2*>(&Dq[0][o]) = uint2{a[0] | (a[1] << 16), a[2] | (a[3] << 16)};
+        *reinterpret_cast<uint2*>(&Dq[1][o]) = uint2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+        *reinterpret_cast<uint2*>(&Dq[2][o]) = uint2{cc[0] | (cc[1] << 16), cc[2] | (cc[3] << 16)};
+      }
+    }
+    __syncthreads();
+    // O = Y + P Delta^T
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+      if (jb <= ti) {
+        const int j = 16 * jb + 4 * kk;
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+          const float* d = Rs + j * DP + 16 * rt + x;
+          Y[rt] = mma16(pA[jb], f4{d[0], d[DP], d[2 * DP], d[3 * DP]}, Y[rt]);
+        }
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * ti + 4 * kk + r;
+      if (i < n) {
+        const int64_t o = (((int64_t)bi * cp.T + t0 + i) * p.HV + hv) * V + v0 + x;
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+          if constexpr (NORM) cp.obuf[o + 16 * rt] = Y[rt][r];
+          else store_act1(p.out, o + 16 * rt, p.out_dt, Y[rt][r]);
+        }
+      }
+    }
+    // S <- e^(gamma_C) S + (Delta diag(fk)) K, three-way split in Delta diag(fk)
+#pragma unroll
+    for (int q = 0; q < CPW; ++q)
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) Sn[q][rt] *= eg;
+#pragma unroll
+    for (int j0 = 0; j0 < GCH; j0 += 16) {
+      const int j = j0 + 4 * kk;
+      uint2 bk[CPW];
+#pragma unroll
+      for (int q = 0; q < CPW; ++q) {
+        const int tc = wave + 4 * q;
+        if (tc < NCT) {
+          const uint16_t* kc = Kst + j * KS + 16 * tc + x;
+          bk[q] = uint2{kc[0] | ((uint32_t)kc[KS] << 16), kc[2 * KS] | ((uint32_t)kc[3 * KS] << 16)};
+        }
+      }
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        const int o = (16 * rt + x) * DB + j;
+        const uint2 ah = *reinterpret_cast<const uint2*>(&Dq[0][o]);
+        const uint2 am = *reinterpret_cast<const uint2*>(&Dq[1][o]);
+        const uint2 al = *reinterpret_cast<const uint2*>(&Dq[2][o]);
+#pragma unroll
+        for (int q = 0; q < CPW; ++q)
+          if (wave + 4 * q < NCT) {
+            Sn[q][rt] = mma_bf16(al, bk[q], Sn[q][rt]);
+            Sn[q][rt] = mma_bf16(am, bk[q], Sn[q][rt]);
+            Sn[q][rt] = mma_bf16(ah, bk[q], Sn[q][rt]);
+          }
+      }
+    }
+    __syncthreads();  // every wave is done reading the planes, Delta, Kst and Fs
+    put_planes();
+  }
+#pragma unroll
+  for (int q = 0; q < CPW; ++q) {
+    const int tc = wave + 4 * q;
+    if (tc < NCT) {
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Sg[(16 * rt + 4 * kk + r) * K + 16 * tc + x] = Sn[q][rt][r];
+    }
+  }
+}
+
 // Pass 3 (gated RMSNorm): one wave per (row, token, value head).
 __global__ __launch_bounds__(256) void gdn_chunk_norm_kernel(GdnChunkParams cp) {
   const GdnParams& p = cp.g;
@@ -602,19 +873,33 @@ hipError_t launch_gch_k(const GdnChunkParams& cp, int n_cu, hipStream_t st) {
     gdn_chunk_prep_kernel<K, ACT, true><<<dim3((unsigned)prep_blocks), dim3(256), lds, st>>>(cp);
   else
     gdn_chunk_prep_kernel<K, ACT, false><<<dim3((unsigned)prep_blocks), dim3(256), lds, st>>>(cp);
-  // state rows per block: the largest of 64 / 32 / 16 dividing V that still
-  // gives two blocks per CU (16 otherwise)
+  // state rows per block: the largest of 64 / 32 / 16 (32 / 16 for the bf16
+  // split kernel, whose LDS holds one block per CU at 64) dividing V that
+  // still gives two blocks per CU (16 otherwise)
   const int64_t bh8 = ((int64_t)p.B * p.HV + 7) / 8 * 8;
   int vt = 16;
   for (int c : {64, 32})
-    if (p.V % c == 0 && bh8 * (p.V / c) >= 2LL * n_cu) {
+    if ((ACT != SSMD_BF16 || c < 64) && p.V % c == 0 && bh8 * (p.V / c) >= 2LL * n_cu) {
       vt = c;
       break;
     }
   const dim3 sg((unsigned)(bh8 * (p.V / vt)));
-  if (vt == 64) launch_gch_state<K, 64, ACT>(cp, sg, st);
-  else if (vt == 32) launch_gch_state<K, 32, ACT>(cp, sg, st);
-  else launch_gch_state<K, 16, ACT>(cp, sg, st);
+  if constexpr (ACT == SSMD_BF16) {
+    const bool nrm = p.norm_gate != nullptr;
+    if (vt == 32) {
+      if (nrm) gdn_chunk_state_x3_kernel<K, 32, true><<<sg, dim3(256), 0, st>>>(cp);
+      else gdn_chunk_state_x3_kernel<K, 32, false><<<sg, dim3(256), 0, st>>>(cp);
+    } else {
+      if (nrm) gdn_chunk_state_x3_kernel<K, 16, true><<<sg, dim3(256), 0, st>>>(cp);
+      else gdn_chunk_state_x3_kernel<K, 16, false><<<sg, dim3(256), 0, st>>>(cp);
+    }
+  } else if (vt == 64) {
+    launch_gch_state<K, 64, ACT>(cp, sg, st);
+  } else if (vt == 32) {
+    launch_gch_state<K, 32, ACT>(cp, sg, st);
+  } else {
+    launch_gch_state<K, 16, ACT>(cp, sg, st);
+  }
   if (p.norm_gate) {
     const int64_t waves = (int64_t)p.B * cp.T * p.HV;
     gdn_chunk_norm_kernel<<<dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st>>>(cp);

@@ -129,19 +129,21 @@ def test_gdn_chunk_matches_fused_recurrent():
     assert_mixed(states[0], states[1].double().numpy(), FP32_TOL, "states")
 
 
-def _rows_per_block(B, HV, V):
+def _rows_per_block(B, HV, V, act):
     """The state pass's rows per block as the launcher picks them: the largest
-    of 64 / 32 / 16 dividing V that still gives two blocks per CU."""
+    of 64 / 32 / 16 (32 / 16 for bf16 inputs, which take the split-product
+    kernel) dividing V that still gives two blocks per CU."""
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     bh8 = (B * HV + 7) // 8 * 8
     for c in (64, 32):
-        if V % c == 0 and bh8 * (V // c) >= 2 * n_cu:
+        if (act != "bf16" or c < 64) and V % c == 0 and bh8 * (V // c) >= 2 * n_cu:
             return c
     return 16
 
 
 ROW_TILE_CASES = [
     # name, B, H, HV, K, V, act, out, T, norm; sized so the launcher takes 64 or 32 state rows per block
+    # (bf16: the split-product kernel at 32 rows; f16 / f32: the fp32-product kernel at 64 and 32)
     ("k128_v128_bf16", 8, 16, 32, 128, 128, "bf16", "f32", 130, None),
     ("k64_v128_f16_norm", 8, 16, 32, 64, 128, "f16", "f16", 70, "silu"),
     ("k128_v128_bf16_norm", 4, 16, 32, 128, 128, "bf16", "bf16", 100, "sigmoid"),
@@ -156,7 +158,7 @@ def test_gdn_chunk_row_tiles(case):
     a padded row among them)."""
     need_gpu()
     name, B, H, HV, K, V, act, outd, T, norm = case
-    vt = _rows_per_block(B, HV, V)
+    vt = _rows_per_block(B, HV, V, act)
     if vt == 16:
         pytest.skip(f"{torch.cuda.get_device_properties(0).multi_processor_count} CUs: 16 rows per block here")
     w = W.GDNWorkload("gdn_chunk_rows_" + name, B=B, H=H, HV=HV, K=K, V=V, num_slots=B + 2, act=act, out=outd,
