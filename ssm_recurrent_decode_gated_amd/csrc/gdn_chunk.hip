@@ -662,22 +662,39 @@ __global__ __launch_bounds__(256) void gdn_chunk_state_x3_kernel(GdnChunkParams 
     const int t0 = c * GCH;
     const int n = min(GCH, len - t0);
     const int64_t rbase = ((int64_t)bi * cp.T + t0) * p.qkv_stride;
+    // every global load of the chunk is issued here, before the first wait:
+    // raw k (to LDS), the factors, this wave's rows of M and P, its q operands
+    // and the v values of its R entries
+    const int64_t qoff = rbase + (int64_t)min(16 * ti + x, n - 1) * p.qkv_stride + (int64_t)h * K + 4 * kk;
+    uint2 qa[K / 16];
+    uint32_t vr[4][NRT];
+    f4 mA[4], pA[4];
     {
       raw4_t<SSMD_BF16> rk[K / 16];
       if (vec) gch_load<SSMD_BF16, true>(p.qkv, rbase, p.qkv_stride, n, (int64_t)(p.H + h) * K, K, rk);
       else gch_load<SSMD_BF16, false>(p.qkv, rbase, p.qkv_stride, n, (int64_t)(p.H + h) * K, K, rk);
       f4 fv;
       if (tid < GCH + 1) fv = ld4s(rec + GCH_F + 4 * tid);
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb)
+        if (jb <= ti) {
+          mA[jb] = ld4s(rec + GCH_M + (16 * ti + x) * GCH + 16 * jb + 4 * kk);
+          pA[jb] = ld4s(rec + GCH_P + (16 * ti + x) * GCH + 16 * jb + 4 * kk);
+        }
+#pragma unroll
+      for (int m = 0; m < K / 16; ++m)
+        qa[m] = vec ? ld_raw4<SSMD_BF16, true>(p.qkv, qoff + 16 * m) : ld_raw4<SSMD_BF16, false>(p.qkv, qoff + 16 * m);
+      const uint16_t* const vq = static_cast<const uint16_t*>(p.qkv);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t vo = rbase + (int64_t)min(16 * ti + 4 * kk + r, n - 1) * p.qkv_stride +
+                           2 * (int64_t)p.H * K + (int64_t)hv * V + v0 + x;
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) vr[r][rt] = vq[vo + 16 * rt];
+      }
       gch_store<SSMD_BF16>(rk, n, K, Kst, KS);
       if (tid < GCH + 1) *reinterpret_cast<f4*>(Fs + 4 * tid) = fv;
     }
-    f4 mA[4], pA[4];
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
-      if (jb <= ti) {
-        mA[jb] = ld4s(rec + GCH_M + (16 * ti + x) * GCH + 16 * jb + 4 * kk);
-        pA[jb] = ld4s(rec + GCH_P + (16 * ti + x) * GCH + 16 * jb + 4 * kk);
-      }
     __syncthreads();  // Kst, Fs and the planes of S in place
     const float* const fq = Fs;
     const float* const fk = Fs + GCH;
@@ -689,11 +706,10 @@ __global__ __launch_bounds__(256) void gdn_chunk_state_x3_kernel(GdnChunkParams 
     f4v Y[NRT], Z[NRT];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) Y[rt] = Z[rt] = f4v{0.f, 0.f, 0.f, 0.f};
-    const int64_t qoff = rbase + (int64_t)min(16 * ti + x, n - 1) * p.qkv_stride + (int64_t)h * K + 4 * kk;
     const uint16_t* const krow = Kst + (16 * ti + x) * KS + 4 * kk;
-#pragma unroll 4
+#pragma unroll
     for (int k0 = 0; k0 < K; k0 += 16) {
-      const uint2 aq = vec ? ld_raw4<SSMD_BF16, true>(p.qkv, qoff + k0) : ld_raw4<SSMD_BF16, false>(p.qkv, qoff + k0);
+      const uint2 aq = qa[k0 / 16];
       const uint2 ak = *reinterpret_cast<const uint2*>(krow + k0);
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
@@ -709,11 +725,9 @@ __global__ __launch_bounds__(256) void gdn_chunk_state_x3_kernel(GdnChunkParams 
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * ti + 4 * kk + r;
       const float fqi = fq[i], fwi = fw[i], bti = bt[i];
-      const int64_t vo = rbase + (int64_t)min(i, n - 1) * p.qkv_stride + 2 * (int64_t)p.H * K + (int64_t)hv * V +
-                         v0 + x;
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
-        Rs[i * DP + 16 * rt + x] = bti * ld_act<SSMD_BF16>(p.qkv, vo + 16 * rt) - fwi * Z[rt][r];
+        Rs[i * DP + 16 * rt + x] = bti * bf16_bits_to_f32(vr[r][rt]) - fwi * Z[rt][r];
         Y[rt][r] *= fqi;
       }
     }
