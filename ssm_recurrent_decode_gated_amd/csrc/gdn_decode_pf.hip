@@ -9,6 +9,8 @@
 // plain copy kernel. Fewer concurrent streams with continuous prefetch keep
 // the HBM busier than many short-lived blocks; the grid must match the CU
 // count exactly (a few blocks more or fewer leaves CUs with twice the work).
+// Small batches, with at most two units per CU, launch one block per unit
+// instead (see the launcher).
 #include "ssmd_device.h"
 #include "ssmd_internal.h"
 
@@ -147,14 +149,29 @@ namespace {
 template <int K, int ACT, bool VEC>
 hipError_t launch_pf_k(const GdnParams& p, const Launch& l, int n_cu, hipStream_t st) {
   const int wave_rows = pf_rg<K>() * RowLayout<K>::RPI;
+  auto units_for = [&](int w) {
+    const int rpt = w * wave_rows;
+    return (int64_t)p.B * p.HV * ((p.V + rpt - 1) / rpt);
+  };
   int wpb = l.wpb;
+  int64_t cap = l.grid_cap > 0 ? l.grid_cap : n_cu;
+  if (!l.fixed) {
+    // Small batches (measured at HV = 32, K = V = 128): narrower blocks until
+    // every CU has a unit (B = 1: 4.7 us with 1-wave blocks against 5.5 with
+    // 4), and one block per unit, all state loads in flight at once, while
+    // that is at most two per CU (B = 16: 12.4 us against 13.9 persistent);
+    // beyond that one persistent block per CU (B = 64: 50.2 us against 52.1).
+    wpb = 4;
+    while (wpb > 1 && units_for(wpb) < n_cu) wpb /= 2;
+    const int64_t u = units_for(wpb);
+    cap = u <= 2LL * n_cu ? u : n_cu;
+  }
   const int rows_per_tile = wpb * wave_rows;
   const int tiles = (p.V + rows_per_tile - 1) / rows_per_tile;
   // never launch more waves than a tile has rows for
   const int need = (min(p.V, rows_per_tile) + wave_rows - 1) / wave_rows;
   if (wpb > need) wpb = need;
   const int64_t units = (int64_t)p.B * p.HV * tiles;
-  const int64_t cap = l.grid_cap > 0 ? l.grid_cap : n_cu;
   const int64_t blocks = units < cap ? units : cap;
   gdn_decode_pf_kernel<K, ACT, VEC><<<dim3((unsigned)blocks), dim3(64 * wpb), 0, st>>>(p, tiles, rows_per_tile,
                                                                                     (int)units);

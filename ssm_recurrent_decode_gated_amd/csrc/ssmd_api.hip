@@ -38,15 +38,15 @@ bool aligned(const void* p, int bytes) { return ((uintptr_t)p % (uintptr_t)bytes
 // overrides it (read once) for launch-shape sweeps.
 ssmd::Launch launch_for() {
   static int tuned = -1;
-  static ssmd::Launch override_l{4, 0};
+  static ssmd::Launch override_l{4, 0, 0};
   if (tuned < 0) {
     const char* e = getenv("SSMD_TUNE");
     int wpb = 0, cap = 0;
     const int n = e ? sscanf(e, "%d,%d", &wpb, &cap) : 0;
     tuned = (n >= 1 && wpb >= 1 && wpb <= 8 && cap >= 0) ? 1 : 0;
-    if (tuned) override_l = ssmd::Launch{wpb, cap};
+    if (tuned) override_l = ssmd::Launch{wpb, cap, 1};
   }
-  return tuned == 1 ? override_l : ssmd::Launch{4, 0};
+  return tuned == 1 ? override_l : ssmd::Launch{4, 0, 0};
 }
 
 // Compute units of the current device, cached per device (a host-side query;

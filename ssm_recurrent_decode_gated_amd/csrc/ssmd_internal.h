@@ -137,6 +137,7 @@ struct MambaScanParams {
 struct Launch {
   int wpb;       // waves per workgroup
   int grid_cap;  // > 0: at most this many blocks, each walking units with a grid stride
+  int fixed;     // 1: wpb and grid_cap as given; 0: a launcher with a shape policy picks its own
 };
 
 // Launchers: return a hipError_t from the launch.
