@@ -23,11 +23,10 @@ constexpr int pf_rg() {
   return K == 16 ? 1 : (K == 32 ? 2 : (K == 256 ? 1 : 4));
 }
 
-template <int K, int ACT, bool VEC>
+template <int K, int ACT, bool VEC, int RG>
 __global__ __launch_bounds__(512) void gdn_decode_pf_kernel(GdnParams p, int tiles_per_head,
                                                             int rows_per_tile, int n_units) {
   using RL = RowLayout<K>;
-  constexpr int RG = pf_rg<K>();
   constexpr int LPR = RL::LPR, NV = RL::NV, RPI = RL::RPI;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -146,26 +145,9 @@ __global__ __launch_bounds__(512) void gdn_decode_pf_kernel(GdnParams p, int til
 
 namespace {
 
-template <int K, int ACT, bool VEC>
-hipError_t launch_pf_k(const GdnParams& p, const Launch& l, int n_cu, hipStream_t st) {
-  const int wave_rows = pf_rg<K>() * RowLayout<K>::RPI;
-  auto units_for = [&](int w) {
-    const int rpt = w * wave_rows;
-    return (int64_t)p.B * p.HV * ((p.V + rpt - 1) / rpt);
-  };
-  int wpb = l.wpb;
-  int64_t cap = l.grid_cap > 0 ? l.grid_cap : n_cu;
-  if (!l.fixed) {
-    // Small batches (measured at HV = 32, K = V = 128): narrower blocks until
-    // every CU has a unit (B = 1: 4.7 us with 1-wave blocks against 5.5 with
-    // 4), and one block per unit, all state loads in flight at once, while
-    // that is at most two per CU (B = 16: 12.4 us against 13.9 persistent);
-    // beyond that one persistent block per CU (B = 64: 50.2 us against 52.1).
-    wpb = 4;
-    while (wpb > 1 && units_for(wpb) < n_cu) wpb /= 2;
-    const int64_t u = units_for(wpb);
-    cap = u <= 2LL * n_cu ? u : n_cu;
-  }
+template <int K, int ACT, bool VEC, int RG>
+hipError_t launch_pf_rg(const GdnParams& p, int wpb, int64_t cap, hipStream_t st) {
+  const int wave_rows = RG * RowLayout<K>::RPI;
   const int rows_per_tile = wpb * wave_rows;
   const int tiles = (p.V + rows_per_tile - 1) / rows_per_tile;
   // never launch more waves than a tile has rows for
@@ -173,9 +155,33 @@ hipError_t launch_pf_k(const GdnParams& p, const Launch& l, int n_cu, hipStream_
   if (wpb > need) wpb = need;
   const int64_t units = (int64_t)p.B * p.HV * tiles;
   const int64_t blocks = units < cap ? units : cap;
-  gdn_decode_pf_kernel<K, ACT, VEC><<<dim3((unsigned)blocks), dim3(64 * wpb), 0, st>>>(p, tiles, rows_per_tile,
-                                                                                    (int)units);
+  gdn_decode_pf_kernel<K, ACT, VEC, RG><<<dim3((unsigned)blocks), dim3(64 * wpb), 0, st>>>(p, tiles, rows_per_tile,
+                                                                                        (int)units);
   return hipGetLastError();
+}
+
+template <int K, int ACT, bool VEC>
+hipError_t launch_pf_k(const GdnParams& p, const Launch& l, int n_cu, hipStream_t st) {
+  constexpr int RG = pf_rg<K>();
+  if (l.fixed) return launch_pf_rg<K, ACT, VEC, RG>(p, l.wpb, l.grid_cap > 0 ? l.grid_cap : n_cu, st);
+  // Small batches (measured at HV = 32, K = V = 128): narrower blocks until
+  // every CU has a unit, then, if even 1-wave blocks leave CUs idle, half the
+  // rows per wave (B = 1: 4.1 us against 4.7 with 32-row units and 5.5 with
+  // 4-wave blocks); one block per unit, all state loads in flight at once,
+  // while that is at most two per CU (B = 16: 12.5 us against 13.9
+  // persistent); beyond that one persistent block per CU (B = 64: 50.2 us
+  // against 52.1 with one block per unit).
+  auto units_for = [&](int w, int rg) {
+    const int rpt = w * rg * RowLayout<K>::RPI;
+    return (int64_t)p.B * p.HV * ((p.V + rpt - 1) / rpt);
+  };
+  auto grid_for = [&](int64_t u) { return u <= 2LL * n_cu ? u : (int64_t)n_cu; };
+  if constexpr (RG >= 2) {
+    if (units_for(1, RG) < n_cu) return launch_pf_rg<K, ACT, VEC, RG / 2>(p, 1, grid_for(units_for(1, RG / 2)), st);
+  }
+  int wpb = 4;
+  while (wpb > 1 && units_for(wpb, RG) < n_cu) wpb /= 2;
+  return launch_pf_rg<K, ACT, VEC, RG>(p, wpb, grid_for(units_for(wpb, RG)), st);
 }
 
 template <int K>
