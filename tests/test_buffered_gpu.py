@@ -51,8 +51,34 @@ CASES = [
 ]
 
 
+def _ring_on_device(ring, offset):
+    """The ring on the GPU; with `offset`, the 16-bit records start `offset`
+    elements into a larger allocation (not 8-byte aligned for offset 1)."""
+    out = {}
+    for k, v in ring.items():
+        if offset and v.element_size() == 2:
+            buf = torch.zeros(v.numel() + offset, dtype=v.dtype, device=DEV)
+            out[k] = buf[offset:].view(v.shape)
+            out[k].copy_(v.to(DEV))
+        else:
+            out[k] = v.to(DEV)
+    return out
+
+
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_buffered_single_call_every_phase(case):
+    _single_call_case(case)
+
+
+def test_buffered_long_and_unaligned_rings():
+    """A 32-record ring (more records than the vector staging covers in one
+    go) and 16-bit rings whose base is not 8-byte aligned (element loads)."""
+    _single_call_case(("k128_L32_long", 3, 2, 4, 128, 128, 32, [31, 20, 3], False))
+    _single_call_case(("k128_L8_unaligned", 4, 2, 4, 128, 128, 8, [0, 5, 7, 2], False), ring_offset=1)
+    _single_call_case(("k64_v40_L16_unaligned_norm", 3, 1, 3, 64, 40, 16, [15, 9, 1], True), ring_offset=1)
+
+
+def _single_call_case(case, ring_offset=0):
     need_gpu()
     name, B, H, HV, K, V, L, phases, norm = case
     w = W.GDNWorkload("buf_" + name, B=B, H=H, HV=HV, K=K, V=V, num_slots=B + 2, out="f32", idx="perm")
@@ -61,7 +87,7 @@ def test_buffered_single_call_every_phase(case):
     ring = W.gdn_ring(w, L)
     wp = torch.tensor(phases, dtype=torch.int32)
     st_d = st.to(DEV)
-    ring_d = {k: v.to(DEV) for k, v in ring.items()}
+    ring_d = _ring_on_device(ring, ring_offset)
     out = torch.full((B, 1, HV, V), float("nan"), device=DEV)
     _call(w, x, P, st_d, idx, ring_d, wp, out, norm)
     ref_st = st.double().numpy().copy()
