@@ -187,11 +187,26 @@ __global__ __launch_bounds__(256) void mamba_scan_carry_kernel(MambaScanParams p
   if (slot < 0 || slot >= p.num_slots) return;
   float* hs = p.state + (int64_t)slot * per_row + e;
   float h = p.zero_init ? 0.f : *hs;
-  for (int c = 0; c < p.nck; ++c) {
-    const int64_t o = ((int64_t)bi * p.nck + c) * per_row + e;
-    const float hl = p.ws_h[o];
-    p.ws_h[o] = h;
-    h = p.ws_P[o] * h + hl;
+  // Chunks in groups of CG: the group's loads are all issued before its
+  // stores (a store to ws_h ahead of the next chunk's load would make every
+  // chunk wait a full memory round trip), then the short FMA chain runs.
+  constexpr int CG = 16;
+  const int64_t base = (int64_t)bi * p.nck * per_row + e;
+  for (int c0 = 0; c0 < p.nck; c0 += CG) {
+    float hl[CG], P[CG];
+#pragma unroll
+    for (int j = 0; j < CG; ++j) {
+      const int64_t o = base + (int64_t)min(c0 + j, p.nck - 1) * per_row;
+      hl[j] = p.ws_h[o];
+      P[j] = p.ws_P[o];
+    }
+#pragma unroll
+    for (int j = 0; j < CG; ++j) {
+      if (c0 + j < p.nck) {
+        p.ws_h[base + (int64_t)(c0 + j) * per_row] = h;
+        h = P[j] * h + hl[j];
+      }
+    }
   }
   *hs = h;
 }
