@@ -24,6 +24,8 @@
 // over channels, prefetched one group of 8 tokens ahead; B and C of a token
 // group are shared by the block's channels and staged through LDS (double
 // buffered, one barrier per group). A rows stay in registers.
+#include <type_traits>
+
 #include "ssmd_device.h"
 #include "ssmd_internal.h"
 
@@ -34,6 +36,23 @@ constexpr int MSCAN_SUB = 8;   // tokens per prefetch group
 constexpr int MSCAN_NPL = 16;  // state elements per lane
 
 enum MScanMode { MSCAN_SUMMARY = 0, MSCAN_OUTPUT = 1, MSCAN_SINGLE = 2 };
+
+// One activation value as loaded, converted when staged: a conversion (or a
+// load under a branch) right at the load makes the wave wait for it there,
+// which turns the one-group-ahead prefetch into a wait per token.
+template <int ACT>
+struct ScanRaw {
+  typename std::conditional<ACT == SSMD_F32, float, uint32_t>::type v;
+  __device__ __forceinline__ void load(const void* base, int64_t off) {
+    if constexpr (ACT == SSMD_F32) v = static_cast<const float*>(base)[off];
+    else v = static_cast<const uint16_t*>(base)[off];
+  }
+  __device__ __forceinline__ float get() const {
+    if constexpr (ACT == SSMD_F32) return v;
+    else if constexpr (ACT == SSMD_BF16) return bf16_bits_to_f32(v);
+    else return f16_bits_to_f32(v);
+  }
+};
 
 template <int N, int ACT, int MODE>
 __global__ __launch_bounds__(MSCAN_THREADS) void mamba_scan_kernel(MambaScanParams p) {
@@ -68,6 +87,53 @@ __global__ __launch_bounds__(MSCAN_THREADS) void mamba_scan_kernel(MambaScanPara
   }
   float dt_sum = 0.f;  // chunk decay: prod_t exp(dt_t A) = exp2(a2 sum_t dt_t)
   float* const hs = p.state + ((int64_t)slot * p.Dm + d) * N + MSCAN_NPL * j;
+
+  // ---- token groups: x, dt, z in registers and B, C in LDS, one group ahead
+  const float Dd = (MODE != MSCAN_SUMMARY && p.Dvec) ? p.Dvec[d] : 0.f;
+  const bool has_z = MODE != MSCAN_SUMMARY && p.z != nullptr;
+  float xc[MSCAN_SUB], dc[MSCAN_SUB], zc[MSCAN_SUB];
+  ScanRaw<ACT> xn[MSCAN_SUB], dn[MSCAN_SUB], zn[MSCAN_SUB], bcn[BCT];
+  const void* const zsrc = has_z ? p.z : p.x;  // without a gate: a harmless in-bounds load, unused
+  auto load_group = [&](int g0) {  // tokens g0 .. g0 + SUB - 1 (clamped into the row)
+#pragma unroll
+    for (int u = 0; u < MSCAN_SUB; ++u) {
+      const int t = min(g0 + u, p.T - 1);
+      const int64_t o = ((int64_t)bi * p.T + t) * p.Dm + d;
+      xn[u].load(p.x, o);
+      dn[u].load(p.dt, o);
+      zn[u].load(zsrc, o);
+    }
+#pragma unroll
+    for (int e = 0; e < BCT; ++e) {
+      const int i = min(tid + e * MSCAN_THREADS, BCV - 1);
+      const int u = i / (2 * N), w = (i / N) & 1, n = i % N;
+      const int t = min(g0 + u, p.T - 1);
+      bcn[e].load(w ? p.Cm : p.Bm, ((int64_t)bi * p.T + t) * N + n);
+    }
+  };
+  auto stage_group = [&](int buf) {
+#pragma unroll
+    for (int e = 0; e < BCT; ++e) {
+      const int i = tid + e * MSCAN_THREADS;
+      if (i < BCV) bc_lds[buf][i] = bcn[e].get();
+    }
+#pragma unroll
+    for (int u = 0; u < MSCAN_SUB; ++u) {
+      xc[u] = xn[u].get();
+      dc[u] = dn[u].get();
+      zc[u] = zn[u].get();
+    }
+  };
+
+  int buf = 0;
+  if (t0 < t1) {
+    load_group(t0);
+    stage_group(0);
+    __syncthreads();
+  }
+  // the entering state, loaded after the (conditional) first staging so that
+  // on every path into the loop these are the latest loads: the first use
+  // then waits for them alone, not for the group prefetched ahead of it
   if constexpr (MODE == MSCAN_SUMMARY) {
 #pragma unroll
     for (int n = 0; n < MSCAN_NPL; ++n) h[n] = 0.f;
@@ -79,49 +145,10 @@ __global__ __launch_bounds__(MSCAN_THREADS) void mamba_scan_kernel(MambaScanPara
       const f4 v = zero ? f4{0.f, 0.f, 0.f, 0.f} : *reinterpret_cast<const f4*>(src + 4 * q);
       h[4 * q] = v.x; h[4 * q + 1] = v.y; h[4 * q + 2] = v.z; h[4 * q + 3] = v.w;
     }
-  }
-
-  // ---- token groups: x, dt, z in registers and B, C in LDS, one group ahead
-  const float Dd = (MODE != MSCAN_SUMMARY && p.Dvec) ? p.Dvec[d] : 0.f;
-  const bool has_z = MODE != MSCAN_SUMMARY && p.z != nullptr;
-  float xc[MSCAN_SUB], dc[MSCAN_SUB], zc[MSCAN_SUB], xn[MSCAN_SUB], dn[MSCAN_SUB], zn[MSCAN_SUB];
-  float bcn[BCT];
-  auto load_group = [&](int g0) {  // tokens g0 .. g0 + SUB - 1 (clamped into the row)
-#pragma unroll
-    for (int u = 0; u < MSCAN_SUB; ++u) {
-      const int t = min(g0 + u, p.T - 1);
-      const int64_t o = ((int64_t)bi * p.T + t) * p.Dm + d;
-      xn[u] = ld_act<ACT>(p.x, o);
-      dn[u] = ld_act<ACT>(p.dt, o);
-      zn[u] = has_z ? ld_act<ACT>(p.z, o) : 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < BCT; ++e) {
-      const int i = min(tid + e * MSCAN_THREADS, BCV - 1);
-      const int u = i / (2 * N), w = (i / N) & 1, n = i % N;
-      const int t = min(g0 + u, p.T - 1);
-      bcn[e] = ld_act<ACT>(w ? p.Cm : p.Bm, ((int64_t)bi * p.T + t) * N + n);
-    }
-  };
-  auto stage_group = [&](int buf) {
-#pragma unroll
-    for (int e = 0; e < BCT; ++e) {
-      const int i = tid + e * MSCAN_THREADS;
-      if (i < BCV) bc_lds[buf][i] = bcn[e];
-    }
-#pragma unroll
-    for (int u = 0; u < MSCAN_SUB; ++u) {
-      xc[u] = xn[u];
-      dc[u] = dn[u];
-      zc[u] = zn[u];
-    }
-  };
-
-  int buf = 0;
-  if (t0 < t1) {
-    load_group(t0);
-    stage_group(0);
-    __syncthreads();
+    // settle them here (s_waitcnt vmcnt(0), expcnt and lgkmcnt untouched):
+    // left pending into the loop, the compiler waits for everything in
+    // flight, the next group's prefetch included, at their first use
+    __builtin_amdgcn_s_waitcnt(0x0F70);
   }
   for (int g0 = t0; g0 < t1; g0 += MSCAN_SUB) {
     if (g0 + MSCAN_SUB < t1) load_group(g0 + MSCAN_SUB);
