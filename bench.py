@@ -15,7 +15,7 @@ same-size stream-copy ceiling, the roofline entry of the dominant kernel and
 the fp64 oracle's rate on the host cores.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-  python bench.py --profile-pass [gdn|kda]   # short run for rocprofv3 counter passes
+  python bench.py --profile-pass [gdn|kda|chunk]   # short run for rocprofv3 counter passes
   python bench.py --summarize-counters FETCH_DIR WRITE_DIR --kernel gdn|kda --out profiles/X.txt
   python bench.py --summarize-trace TRACE_DIR --title T --command C --out profiles/X.md
 """
@@ -496,14 +496,30 @@ def kda_alg_bytes(w, out_bytes=2, act=2):
 
 
 def profile_pass(which="gdn"):
-    """A few launches of one kernel (the headline GDN step, or the fused KDA
-    op at 64 tokens x 96 heads) and one copy of known size, for rocprofv3
-    counter passes."""
+    """A few launches of one kernel (the headline GDN step, the fused KDA op at
+    64 tokens x 96 heads, or the chunked GDN prefill of one and of eight
+    2048-token prompts) and one copy of known size, for rocprofv3 counter
+    passes."""
     import torch
     import ssm_recurrent_decode_gated_amd as S
     import workloads as W
     dev = torch.device("cuda:0")
-    if which == "kda":
+    if which == "chunk":
+        for B in (1, 8):
+            w = W.gdn_sweep(B)
+            su = GDNSetup(w, 1, dev)
+            T = 2048
+            g = W.generator(0, w.name, "prefill", T)
+            C = 2 * w.H * w.K + w.HV * w.V
+            qkv = W.normal((B, T, C), 1.0, "bf16", g).to(dev)
+            a = W.normal((B, T, w.HV), 0.5, "bf16", g).to(dev)
+            b = W.normal((B, T, w.HV), 1.0, "bf16", g).to(dev)
+            out = torch.empty(B, T, w.HV, w.V, dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(S.gdn_chunk_workspace_bytes(B, T, w.HV, w.K, w.V) // 4, device=dev)
+            for _ in range(3):
+                S.gdn_chunk_prefill(qkv, a, b, su.A_log, su.dt_bias, su.pools[0], su.idx_d, out, workspace=ws)
+            del su, qkv, a, b, out, ws
+    elif which == "kda":
         w = W.KDA_T64
         d = {k: v.to(dev) for k, v in W.kda_inputs(w).items()}
         out = torch.empty(w.T, w.H, w.D, dtype=torch.bfloat16, device=dev)
@@ -604,7 +620,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline only (no sweep/buffered/KDA/conv/Mamba/copy)")
-    ap.add_argument("--profile-pass", nargs="?", const="gdn", choices=("gdn", "kda"))
+    ap.add_argument("--profile-pass", nargs="?", const="gdn", choices=("gdn", "kda", "chunk"))
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
     ap.add_argument("--title", default="")
