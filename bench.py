@@ -661,7 +661,7 @@ def main():
     del h["setup"]
     torch.cuda.empty_cache()
     if not args.no_extras:
-        for key, leg in (("copy_ceiling", copy_ceiling), ("graph_sweep", sweep), ("buffered_b64", buffered),
+        for key, leg in (("graph_sweep", sweep), ("copy_ceiling", copy_ceiling), ("buffered_b64", buffered),
                          ("kda_t64_h96", kda), ("gdn_conv_b256", gdn_conv), ("mamba1", mamba), ("mamba1_prefill", mamba_prefill), ("gdn_multi_token", gdn_multi), ("gdn_prefill", gdn_prefill),
                          ("state16_b256", state16)):
             extra[key] = leg(dev)
