@@ -71,3 +71,27 @@ def need_gpu():
     import pytest
     if not torch.cuda.is_available():
         pytest.skip("no GPU visible")
+
+
+MIDPOINT_REL = 2.0 ** -16  # far above fp32 rounding error, far below half a bf16 ulp (2^-9)
+
+
+def assert_ring16(got, ref, what, exact):
+    """A stored 16-bit record may differ from the oracle's rounding by one ulp
+    only where the exact (unrounded) value sits at the rounding midpoint
+    between the two neighbours, to within fp32 arithmetic error (2^-16 of
+    max(|value|, rms of its record)): there both neighbours are correct
+    roundings of what an fp32 kernel computes. Elements that share a mantissa
+    flip together, so no count of flips is imposed."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    exact = np.asarray(exact, dtype=np.float64)
+    diff = np.abs(got - ref)
+    assert (diff <= ulp16(ref, 7) * 1.0000001).all(), f"{what}: record off by more than one ulp"
+    flip = diff != 0
+    # fp32 error is measured against the record's scale, as in the fp32 parity
+    # metric: delta = beta (v - S k) can cancel, so its error tracks the row, not itself
+    scale = np.maximum(np.abs(exact), np.sqrt(np.mean(exact * exact, axis=-1, keepdims=True)))
+    off_mid = np.abs(exact - 0.5 * (got + ref)) > MIDPOINT_REL * scale
+    assert not (flip & off_mid).any(), \
+        f"{what}: {(flip & off_mid).sum()} record(s) differ where the exact value is not at a midpoint"
