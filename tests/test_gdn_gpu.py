@@ -131,6 +131,7 @@ RAGGED = [
     ("k128_v200_two_tiles", 3, 2, 4, 128, 200, 5, "bf16", "f32"),
     ("k128_v1", 4, 1, 2, 128, 1, 4, "f32", "f32"),
     ("k64_gqa4_v128", 6, 2, 8, 64, 128, 6, "bf16", "bf16"),
+    ("k256_v1024_max", 2, 1, 2, 256, 1024, 3, "bf16", "f32"),  # largest head the ABI takes
 ]
 
 
@@ -151,7 +152,8 @@ def test_gdn_shapes_and_dtypes(case):
 
 
 NORM = [("k128_v128_silu", 128, 128, "silu", "bf16"), ("k64_v96_sigmoid", 64, 96, "sigmoid", "f32"),
-        ("k128_v300_silu_looped", 128, 300, "silu", "f32"), ("k16_v16_sigmoid", 16, 16, "sigmoid", "bf16")]
+        ("k128_v300_silu_looped", 128, 300, "silu", "f32"), ("k16_v16_sigmoid", 16, 16, "sigmoid", "bf16"),
+        ("k256_v1024_sigmoid_max", 256, 1024, "sigmoid", "f32")]
 
 
 @pytest.mark.parametrize("case", NORM, ids=[c[0] for c in NORM])
