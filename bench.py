@@ -206,6 +206,11 @@ def sweep(dev, batches=(1, 16, 64, 256), reps=50):
         res[f"B{B}"] = {"us_per_step": round(us, 3), "state_GBps": round(sb / us / 1e3, 1),
                         "pct_hbm_peak": round(100 * sb / us / 1e3 / HBM_PEAK_GBS, 2), "pools": M,
                         "eager_us_per_step": round(eager, 3)}
+        if pool_bytes <= MALL_BYTES // 2:
+            # one pool stepped over and over: its state stays in the Infinity
+            # Cache, so this is a cache rate, not an HBM one
+            hot = graph_time_us([lambda: su.call(0)] * M, reps, torch.cuda.current_stream())
+            res[f"B{B}"]["hot_single_pool_MALL_resident_us"] = round(hot, 3)
         del su
         torch.cuda.empty_cache()
     return res
@@ -448,26 +453,37 @@ def mamba_prefill(dev, reps=20):
     return res
 
 
-def cpu_baseline(su, target_s=10.0):
+def cpu_baseline(su, target_s=10.0, single_s=5.0):
     """The fp64 oracle, as it stands, on the host cores: the full B=256 step
-    repeated (state evolving) until about target_s seconds have passed."""
+    repeated (state evolving) until about target_s seconds have passed on all
+    threads, then single_s seconds on one thread."""
     import numpy as np
     import oracle as O
     w = su.w
     ref = su.state_host.double().numpy().copy()
     q, a, b = O.f64(su.x["qkv"]), O.f64(su.x["a"]), O.f64(su.x["b"])
     idx = su.idx.numpy().astype(np.int32)
-    n, t0 = 0, time.perf_counter()
-    while True:
-        O.gdn_step(q, a, b, su.P["A_log"], su.P["dt_bias"], ref, idx, H=w.H, HV=w.HV, K=w.K, V=w.V)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= target_s:
-            break
-    sb = gdn_state_bytes(w.B, w.HV, w.V, w.K) * n
-    return {"value": round(sb / el / 1e9, 3), "unit": "GB/s", "cores": O.num_threads(), "kind": "oracle",
-            "sample": f"full B=256-of-264 step (H=16, HV=32, K=V=128) repeated {n} times in {el:.1f} s; "
-                      "fp32-state byte model"}
+    sb1 = gdn_state_bytes(w.B, w.HV, w.V, w.K)
+
+    def run(limit):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            O.gdn_step(q, a, b, su.P["A_log"], su.P["dt_bias"], ref, idx, H=w.H, HV=w.HV, K=w.K, V=w.V)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= limit:
+                return n, el
+    cores = O.num_threads()
+    n, el = run(target_s)
+    O.set_threads(1)
+    n1, el1 = run(single_s)
+    O.set_threads(cores)
+    return {"value": round(sb1 * n / el / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "us_per_step": round(el / n * 1e6, 1),
+            "single_thread": {"value": round(sb1 * n1 / el1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                              "us_per_step": round(el1 / n1 * 1e6, 1), "steps": n1},
+            "sample": f"full B=256-of-264 step (H=16, HV=32, K=V=128) repeated {n} times in {el:.1f} s on "
+                      f"{cores} threads, then {n1} times in {el1:.1f} s on one; fp32-state byte model"}
 
 
 def counters_traffic():

@@ -51,6 +51,8 @@ def configure(L: ctypes.CDLL) -> ctypes.CDLL:
                                                                         _d, _i]
     L.orc_mamba_scan.argtypes = [_i] * 5 + [_dp] * 8 + [_ip, _ip, _i, _dp]
     L.orc_gdn_step_conv.argtypes = [_i] * 7 + [_dp] * 9 + [_ip, _dp, _d, _i, _d, _dp, _dp, _d, _i, _dp]
+    L.orc_set_threads.argtypes = [_i]
+    L.orc_set_threads.restype = None
     for f in ("orc_gdn_step", "orc_gdn_step_buffered", "orc_conv1d_update", "orc_gdn_step_conv",
               "orc_kda_step", "orc_kda_decode", "orc_mamba_step", "orc_mamba_scan", "orc_gdn_multi", "orc_num_threads"):
         getattr(L, f).restype = _i
@@ -134,6 +136,11 @@ def kda_gate(raw_g, A_log, dt_bias, lower_bound):
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_threads(n: int) -> None:
+    """Thread count of the parallel loops (timing only; results do not depend on it)."""
+    lib().orc_set_threads(int(n))
 
 
 # ----------------------------------------------------------------- GDN

@@ -634,6 +634,17 @@ int orc_mamba_scan(int B, int T, int Dm, int N, int num_slots, const double *x,
     return ORC_OK;
 }
 
+/* thread count for the parallel loops above (timing runs only: the
+   arithmetic of every unit is the same at any count); n < 1 is ignored */
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* number of OpenMP threads the parallel loops above use */
 int orc_num_threads(void)
 {
