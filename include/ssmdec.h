@@ -396,6 +396,30 @@ const char* ssmd_last_error(void);
  */
 int ssmd_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
 
+/*
+ * ssmd_check_slot_indices -- debug check of a slot-index vector before a
+ * decode call. Every step above reads and writes the slot its row names, so
+ * two active rows naming one slot in a call race on it (the result is
+ * undefined); the pages' pools ([REPLAY] `_bench_cfg`, [KDA] `Inputs`) give
+ * each active row its own slot. This counts the active rows whose slot an
+ * earlier active row already names and writes the count to *dup_count
+ * (0: the vector is valid).
+ *
+ *   slot_indices [B] int32 (device); B >= 0 (B == 0 writes 0)
+ *   num_slots    pool size: indices outside [0, num_slots) are padded rows
+ *   null_slot_zero  non-zero for kda_decode_step's convention, where slot 0
+ *                is the NULL block and pads the row too
+ *   dup_count    [1] int32 (device), written by the kernel on `stream`
+ *
+ * One workgroup compares each row with every earlier one (O(B^2)): a debug
+ * aid, not meant for the timed path. Enqueued asynchronously like the
+ * steps; the caller reads *dup_count after synchronising. Errors:
+ * SSMD_ERR_NULL_ARG, SSMD_ERR_BAD_SHAPE (B < 0, num_slots < 1, misaligned
+ * pointers), SSMD_ERR_LAUNCH.
+ */
+int ssmd_check_slot_indices(const int32_t* slot_indices, int32_t B, int32_t num_slots,
+                            int32_t null_slot_zero, int32_t* dup_count, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     mamba_decode_step,
     mamba_scan,
     mamba_scan_workspace_bytes,
+    ssmd_check_slot_indices,
     ssmd_last_error,
     ssmd_stream_copy,
 )

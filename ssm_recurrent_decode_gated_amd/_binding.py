@@ -23,7 +23,7 @@ ACT_CODE = {"silu": SSMD_ACT_SILU, "sigmoid": SSMD_ACT_SIGMOID}
 EXPORTS = ("gdn_decode_step", "gdn_decode_step_state16", "gdn_decode_step_buffered", "gdn_decode_step_conv",
            "gdn_fused_recurrent", "gdn_chunk_prefill", "gdn_chunk_workspace_bytes",
            "kda_decode_step", "mamba_decode_step", "mamba_scan", "mamba_scan_workspace_bytes", "ssmd_last_error",
-           "ssmd_stream_copy")
+           "ssmd_stream_copy", "ssmd_check_slot_indices")
 
 
 class SsmdError(RuntimeError):
@@ -64,6 +64,7 @@ def load_library() -> ctypes.CDLL:
                                  _i32, _i32, _i32, _i32, _p]
         L.mamba_scan_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
         L.ssmd_stream_copy.argtypes = [_p, _p, _i64, _p]
+        L.ssmd_check_slot_indices.argtypes = [_p, _i32, _i32, _i32, _p, _p]
         for f in EXPORTS:
             if f == "ssmd_last_error":
                 continue
@@ -465,3 +466,18 @@ def ssmd_stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
     _check(load_library().ssmd_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(src, stream)),
            "ssmd_stream_copy")
     return dst
+
+
+def ssmd_check_slot_indices(idx: torch.Tensor, num_slots: int, null_slot_zero: bool = False,
+                            dup_count: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """Debug check: count the active rows of idx ([B] int32) whose slot an
+    earlier active row already names, into dup_count ([1] int32 on the same
+    device, allocated if None). Asynchronous; read the result after a sync."""
+    _dev(idx, "idx", torch.int32)
+    if dup_count is None:
+        dup_count = torch.empty(1, dtype=torch.int32, device=idx.device)
+    _dev(dup_count, "dup_count", torch.int32, (1,))
+    _check(load_library().ssmd_check_slot_indices(_ptr(idx), idx.numel(), int(num_slots), int(bool(null_slot_zero)),
+                                                  _ptr(dup_count), _stream(idx, stream)),
+           "ssmd_check_slot_indices")
+    return dup_count

@@ -149,6 +149,31 @@ __global__ __launch_bounds__(256) void stream_copy_kernel(const ssmd::f4* __rest
     ssmd::st4<true>(reinterpret_cast<float*>(dst + i), ssmd::ld4<true>(reinterpret_cast<const float*>(src + i)));
 }
 
+// Debug check of a slot-index vector: one block counts the active rows
+// (lo <= idx < num_slots) whose slot an earlier active row already names,
+// by direct comparison with every earlier row (O(B^2), a debug aid), and
+// writes the count to *dups (no pre-zeroed memory needed).
+__global__ __launch_bounds__(256) void check_slot_indices_kernel(const int32_t* __restrict__ idx, int32_t B,
+                                                                 int32_t num_slots, int32_t lo,
+                                                                 int32_t* __restrict__ dups) {
+  __shared__ int total;
+  if (threadIdx.x == 0) total = 0;
+  __syncthreads();
+  int mine = 0;
+  for (int i = threadIdx.x; i < B; i += blockDim.x) {
+    const int s = idx[i];
+    if (s < lo || s >= num_slots) continue;  // padded row
+    for (int j = 0; j < i; ++j)
+      if (idx[j] == s) {
+        ++mine;
+        break;
+      }
+  }
+  if (mine) atomicAdd(&total, mine);  // LDS atomic
+  __syncthreads();
+  if (threadIdx.x == 0) *dups = total;
+}
+
 }  // namespace
 
 namespace ssmd {
@@ -527,6 +552,20 @@ int ssmd_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stre
   int n_cu = 0;
   if (int rc = cu_count(&n_cu)) return rc;
   return launch_status(ssmd::launch_stream_copy(src, dst, bytes, n_cu, stream), "ssmd_stream_copy");
+}
+
+int ssmd_check_slot_indices(const int32_t* slot_indices, int32_t B, int32_t num_slots, int32_t null_slot_zero,
+                            int32_t* dup_count, hipStream_t stream) {
+  const char* fn = "ssmd_check_slot_indices";
+  if (B < 0) return fail(SSMD_ERR_BAD_SHAPE, "%s: B = %d < 0", fn, B);
+  if (num_slots < 1) return fail(SSMD_ERR_BAD_SHAPE, "%s: num_slots = %d < 1", fn, num_slots);
+  if (!dup_count) return fail(SSMD_ERR_NULL_ARG, "%s: dup_count is NULL", fn);
+  if (B > 0 && !slot_indices) return fail(SSMD_ERR_NULL_ARG, "%s: slot_indices is NULL", fn);
+  if (!aligned(dup_count, 4) || (B > 0 && !aligned(slot_indices, 4)))
+    return fail(SSMD_ERR_BAD_SHAPE, "%s: int32 pointers must be 4-byte aligned", fn);
+  check_slot_indices_kernel<<<dim3(1), dim3(256), 0, stream>>>(slot_indices, B, num_slots, null_slot_zero ? 1 : 0,
+                                                                dup_count);
+  return launch_status(hipGetLastError(), fn);
 }
 
 }  // extern "C"

@@ -231,3 +231,13 @@ def test_gdn_chunk_prefill_host_validation():
     need = L.gdn_chunk_workspace_bytes(2, 128, 32, 128, 128, 0)
     assert need == 4 * 2 * 32 * 2 * (2 * 64 * 64 + 4 * 64 + 4)  # per chunk: M, P, four token factors, gamma_C
     assert L.gdn_chunk_workspace_bytes(2, 128, 32, 128, 128, 1) == need + 4 * 2 * 128 * 32 * 128
+
+
+def test_check_slot_indices_host_validation():
+    L = S.load_library()
+    f = L.ssmd_check_slot_indices
+    assert f(0x1000, -1, 4, 0, 0x2000, None) == BAD_SHAPE
+    assert f(0x1000, 4, 0, 0, 0x2000, None) == BAD_SHAPE
+    assert f(0x1000, 4, 4, 0, None, None) == NULL_ARG
+    assert f(None, 4, 4, 0, 0x2000, None) == NULL_ARG
+    assert f(0x1001, 4, 4, 0, 0x2000, None) == BAD_SHAPE
