@@ -266,11 +266,13 @@ def buffered(dev, Ls=(1, 8, 16), reps=30):
     return out
 
 
-def kda(dev, reps=30):
+def kda(dev, reps=30, w=None):
+    """The fused KDA op at T = 64 tokens x 96 heads; with `w`, another shape
+    (one tensor-parallel rank's 12 heads)."""
     import torch
     import ssm_recurrent_decode_gated_amd as S
     import workloads as W
-    w = W.KDA_T64
+    w = w or W.KDA_T64
     d = W.kda_inputs(w)
     pool_bytes = w.num_slots * w.H * w.D * w.D * 4
     M = _pools_for(pool_bytes)
@@ -288,9 +290,14 @@ def kda(dev, reps=30):
     ab = kda_alg_bytes(w)
     del pools, cs
     torch.cuda.empty_cache()
-    return {"workload": w.name, "us_per_step": round(us, 3), "state_GBps": round(sb / us / 1e3, 1),
-            "pct_hbm_peak": round(100 * sb / us / 1e3 / HBM_PEAK_GBS, 2), "alg_GBps": round(ab / us / 1e3, 1),
-            "pct_hbm_peak_alg": round(100 * ab / us / 1e3 / HBM_PEAK_GBS, 2), "pools": M}
+    res = {"workload": w.name, "us_per_step": round(us, 3), "state_GBps": round(sb / us / 1e3, 1),
+           "pct_hbm_peak": round(100 * sb / us / 1e3 / HBM_PEAK_GBS, 2), "alg_GBps": round(ab / us / 1e3, 1),
+           "pct_hbm_peak_alg": round(100 * ab / us / 1e3 / HBM_PEAK_GBS, 2), "pools": M}
+    if w is W.KDA_T64:
+        # one rank's share when the 96 heads are split over 8 GPUs: the same
+        # kernel at 12 heads (the step has no exchange between heads)
+        res["tp8_rank_h12"] = kda(dev, reps, W.KDAWorkload("kda_t64_h12_d128_w4", T=64, H=12, num_slots=72))
+    return res
 
 
 def gdn_conv(dev, reps=30, Wd=4):
