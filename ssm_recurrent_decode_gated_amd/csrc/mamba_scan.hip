@@ -33,7 +33,7 @@ namespace ssmd {
 
 constexpr int MSCAN_THREADS = 256;
 constexpr int MSCAN_SUB = 8;   // tokens per prefetch group
-constexpr int MSCAN_NPL = 16;  // state elements per lane
+constexpr int MSCAN_NPL = 16;  // state elements per lane (chunked passes)
 
 enum MScanMode { MSCAN_SUMMARY = 0, MSCAN_OUTPUT = 1, MSCAN_SINGLE = 2 };
 
@@ -54,9 +54,11 @@ struct ScanRaw {
   }
 };
 
-template <int N, int ACT, int MODE>
+// NPL: state elements per lane (16; 4 for a single pass that would leave
+// SIMDs idle).
+template <int N, int ACT, int MODE, int NPL = MSCAN_NPL>
 __global__ __launch_bounds__(MSCAN_THREADS) void mamba_scan_kernel(MambaScanParams p) {
-  constexpr int LPN = N / MSCAN_NPL;
+  constexpr int LPN = N / NPL;
   constexpr int CPB = MSCAN_THREADS / LPN;            // channels per block
   constexpr int BCV = MSCAN_SUB * N * 2;              // B and C values of a token group
   constexpr int BCT = (BCV + MSCAN_THREADS - 1) / MSCAN_THREADS;  // per thread
@@ -73,20 +75,20 @@ __global__ __launch_bounds__(MSCAN_THREADS) void mamba_scan_kernel(MambaScanPara
   const int len = p.lengths ? min(max(p.lengths[bi], 0), p.T) : p.T;
   const int t0 = chunk * p.Lc;
   const int t1 = min(t0 + p.Lc, len);
-  const int64_t ws_off = (((int64_t)bi * p.nck + chunk) * p.Dm + d) * N + MSCAN_NPL * j;
+  const int64_t ws_off = (((int64_t)bi * p.nck + chunk) * p.Dm + d) * N + NPL * j;
 
   // a2 = A log2(e): exp(dt A) = exp2(dt a2), one multiply and one v_exp_f32
   // (about 1 ulp) per element and token instead of the ~14 instructions of
   // expf; the scan is bound by this arithmetic, not by memory.
   constexpr float LOG2E = 1.44269504088896341f;
-  float h[MSCAN_NPL], a2[MSCAN_NPL];
+  float h[NPL], a2[NPL];
 #pragma unroll
-  for (int q = 0; q < MSCAN_NPL / 4; ++q) {
-    const f4 av = *reinterpret_cast<const f4*>(p.A + (int64_t)d * N + MSCAN_NPL * j + 4 * q);
+  for (int q = 0; q < NPL / 4; ++q) {
+    const f4 av = *reinterpret_cast<const f4*>(p.A + (int64_t)d * N + NPL * j + 4 * q);
     a2[4 * q] = av.x * LOG2E; a2[4 * q + 1] = av.y * LOG2E; a2[4 * q + 2] = av.z * LOG2E; a2[4 * q + 3] = av.w * LOG2E;
   }
   float dt_sum = 0.f;  // chunk decay: prod_t exp(dt_t A) = exp2(a2 sum_t dt_t)
-  float* const hs = p.state + ((int64_t)slot * p.Dm + d) * N + MSCAN_NPL * j;
+  float* const hs = p.state + ((int64_t)slot * p.Dm + d) * N + NPL * j;
 
   // ---- token groups: x, dt, z in registers and B, C in LDS, one group ahead
   const float Dd = (MODE != MSCAN_SUMMARY && p.Dvec) ? p.Dvec[d] : 0.f;
@@ -136,12 +138,12 @@ __global__ __launch_bounds__(MSCAN_THREADS) void mamba_scan_kernel(MambaScanPara
   // then waits for them alone, not for the group prefetched ahead of it
   if constexpr (MODE == MSCAN_SUMMARY) {
 #pragma unroll
-    for (int n = 0; n < MSCAN_NPL; ++n) h[n] = 0.f;
+    for (int n = 0; n < NPL; ++n) h[n] = 0.f;
   } else {
     const float* src = MODE == MSCAN_OUTPUT ? p.ws_h + ws_off : hs;
     const bool zero = MODE == MSCAN_SINGLE && p.zero_init;
 #pragma unroll
-    for (int q = 0; q < MSCAN_NPL / 4; ++q) {
+    for (int q = 0; q < NPL / 4; ++q) {
       const f4 v = zero ? f4{0.f, 0.f, 0.f, 0.f} : *reinterpret_cast<const f4*>(src + 4 * q);
       h[4 * q] = v.x; h[4 * q + 1] = v.y; h[4 * q + 2] = v.z; h[4 * q + 3] = v.w;
     }
@@ -159,12 +161,12 @@ __global__ __launch_bounds__(MSCAN_THREADS) void mamba_scan_kernel(MambaScanPara
       if (t < t1) {  // uniform over the block
         const float dtv = dc[u], xv = xc[u];
         const float dtx = dtv * xv;
-        const float* Bt = bc + u * 2 * N + MSCAN_NPL * j;
+        const float* Bt = bc + u * 2 * N + NPL * j;
         const float* Ct = Bt + N;
         float acc = 0.f;
         if constexpr (MODE == MSCAN_SUMMARY) dt_sum += dtv;
 #pragma unroll
-        for (int n = 0; n < MSCAN_NPL; ++n) {
+        for (int n = 0; n < NPL; ++n) {
           const float dA = __builtin_amdgcn_exp2f(dtv * a2[n]);
           h[n] = dA * h[n] + dtx * Bt[n];
           if constexpr (MODE != MSCAN_SUMMARY) acc += Ct[n] * h[n];
@@ -186,17 +188,17 @@ __global__ __launch_bounds__(MSCAN_THREADS) void mamba_scan_kernel(MambaScanPara
 
   if (!live) return;
   if constexpr (MODE == MSCAN_SUMMARY) {
-    float P[MSCAN_NPL];
+    float P[NPL];
 #pragma unroll
-    for (int n = 0; n < MSCAN_NPL; ++n) P[n] = __builtin_amdgcn_exp2f(dt_sum * a2[n]);
+    for (int n = 0; n < NPL; ++n) P[n] = __builtin_amdgcn_exp2f(dt_sum * a2[n]);
 #pragma unroll
-    for (int q = 0; q < MSCAN_NPL / 4; ++q) {
+    for (int q = 0; q < NPL / 4; ++q) {
       *reinterpret_cast<f4*>(p.ws_P + ws_off + 4 * q) = f4{P[4 * q], P[4 * q + 1], P[4 * q + 2], P[4 * q + 3]};
       *reinterpret_cast<f4*>(p.ws_h + ws_off + 4 * q) = f4{h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]};
     }
   } else if constexpr (MODE == MSCAN_SINGLE) {
 #pragma unroll
-    for (int q = 0; q < MSCAN_NPL / 4; ++q)
+    for (int q = 0; q < NPL / 4; ++q)
       *reinterpret_cast<f4*>(hs + 4 * q) = f4{h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]};
   }
 }
@@ -241,10 +243,25 @@ __global__ __launch_bounds__(256) void mamba_scan_carry_kernel(MambaScanParams p
 namespace {
 
 template <int N, int ACT>
-hipError_t launch_ms(const MambaScanParams& p, hipStream_t st) {
+hipError_t launch_ms(const MambaScanParams& p, int n_cu, hipStream_t st) {
   constexpr int CPB = MSCAN_THREADS / (N / MSCAN_NPL);
   const dim3 grid((unsigned)((p.Dm + CPB - 1) / CPB), (unsigned)p.nck, (unsigned)p.B);
   if (p.nck == 1) {
+    // A single pass over few rows and channels: 4 elements per lane (N/4
+    // lanes per channel) while 16 would leave SIMDs without 4 waves (one
+    // 2048-token prompt, D = 1536, N = 16: 1014 -> 739 us). The chunked
+    // passes keep 16 (at 4 they measured 3% slower for one prompt and 52%
+    // for eight: the lanes of a channel repeat its x, dt, z loads).
+    constexpr int NPL4 = 4;
+    if constexpr (N / NPL4 <= 16) {
+      const int64_t waves16 = (int64_t)p.B * p.Dm * (N / MSCAN_NPL) / 64;
+      if (waves16 < 16LL * n_cu) {
+        constexpr int CPB4 = MSCAN_THREADS / (N / NPL4);
+        const dim3 grid4((unsigned)((p.Dm + CPB4 - 1) / CPB4), 1u, (unsigned)p.B);
+        mamba_scan_kernel<N, ACT, MSCAN_SINGLE, NPL4><<<grid4, dim3(MSCAN_THREADS), 0, st>>>(p);
+        return hipGetLastError();
+      }
+    }
     mamba_scan_kernel<N, ACT, MSCAN_SINGLE><<<grid, dim3(MSCAN_THREADS), 0, st>>>(p);
     return hipGetLastError();
   }
@@ -256,11 +273,11 @@ hipError_t launch_ms(const MambaScanParams& p, hipStream_t st) {
 }
 
 template <int N>
-hipError_t launch_ms_act(const MambaScanParams& p, hipStream_t st) {
+hipError_t launch_ms_act(const MambaScanParams& p, int n_cu, hipStream_t st) {
   switch (p.act_dt) {
-    case SSMD_F32: return launch_ms<N, SSMD_F32>(p, st);
-    case SSMD_BF16: return launch_ms<N, SSMD_BF16>(p, st);
-    default: return launch_ms<N, SSMD_F16>(p, st);
+    case SSMD_F32: return launch_ms<N, SSMD_F32>(p, n_cu, st);
+    case SSMD_BF16: return launch_ms<N, SSMD_BF16>(p, n_cu, st);
+    default: return launch_ms<N, SSMD_F16>(p, n_cu, st);
   }
 }
 
@@ -287,13 +304,13 @@ void mamba_scan_chunking(int B, int T, int Dm, int N, int n_cu, int64_t ws_bytes
   *nck = T == 0 ? 1 : (T + L - 1) / L;
 }
 
-hipError_t launch_mamba_scan(const MambaScanParams& p, hipStream_t st) {
+hipError_t launch_mamba_scan(const MambaScanParams& p, int n_cu, hipStream_t st) {
   switch (p.N) {
-    case 16: return launch_ms_act<16>(p, st);
-    case 32: return launch_ms_act<32>(p, st);
-    case 64: return launch_ms_act<64>(p, st);
-    case 128: return launch_ms_act<128>(p, st);
-    case 256: return launch_ms_act<256>(p, st);
+    case 16: return launch_ms_act<16>(p, n_cu, st);
+    case 32: return launch_ms_act<32>(p, n_cu, st);
+    case 64: return launch_ms_act<64>(p, n_cu, st);
+    case 128: return launch_ms_act<128>(p, n_cu, st);
+    case 256: return launch_ms_act<256>(p, n_cu, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -540,7 +540,7 @@ int mamba_scan(const void* x, const void* dt, const float* A, const void* Bm, co
   p.N = N;
   p.act_dt = act_dtype;
   p.out_dt = out_dtype;
-  return launch_status(ssmd::launch_mamba_scan(p, stream), fn);
+  return launch_status(ssmd::launch_mamba_scan(p, n_cu, stream), fn);
 }
 
 int ssmd_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {

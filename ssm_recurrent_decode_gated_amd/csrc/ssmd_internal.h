@@ -161,7 +161,7 @@ int64_t gdn_chunk_workspace_floats(int B, int T, int HV, int K, int V, bool norm
 // Largest V the multi-token kernel takes with the gated RMSNorm (one block per head).
 int gdn_multi_max_norm_rows(int K);
 hipError_t launch_mamba(const MambaParams& p, const Launch& l, hipStream_t s);
-hipError_t launch_mamba_scan(const MambaScanParams& p, hipStream_t s);
+hipError_t launch_mamba_scan(const MambaScanParams& p, int n_cu, hipStream_t s);
 // Chunking of a Mamba scan on a device of n_cu compute units with ws_bytes of
 // workspace: chunk length *Lc and count *nck (1 when ws_bytes is too small).
 void mamba_scan_chunking(int B, int T, int Dm, int N, int n_cu, int64_t ws_bytes, int* Lc, int* nck);
