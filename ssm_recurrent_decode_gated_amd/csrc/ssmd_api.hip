@@ -2,6 +2,7 @@
 // host-side validation, launch-shape choice, and the stream-copy
 // measurement aid. Nothing here touches device memory from the host,
 // synchronises or allocates.
+#include <atomic>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -37,33 +38,36 @@ bool aligned(const void* p, int bytes) { return ((uintptr_t)p % (uintptr_t)bytes
 // other kernels run one block per work unit. SSMD_TUNE="wpb[,grid_cap]"
 // overrides it (read once) for launch-shape sweeps.
 ssmd::Launch launch_for() {
-  static int tuned = -1;
-  static ssmd::Launch override_l{4, 0, 0};
-  if (tuned < 0) {
+  // read once; a function-local static is initialised exactly once even
+  // when several host threads make their first call together
+  static const ssmd::Launch l = [] {
     const char* e = getenv("SSMD_TUNE");
     int wpb = 0, cap = 0;
     const int n = e ? sscanf(e, "%d,%d", &wpb, &cap) : 0;
-    tuned = (n >= 1 && wpb >= 1 && wpb <= 8 && cap >= 0) ? 1 : 0;
-    if (tuned) override_l = ssmd::Launch{wpb, cap, 1};
-  }
-  return tuned == 1 ? override_l : ssmd::Launch{4, 0, 0};
+    return (n >= 1 && wpb >= 1 && wpb <= 8 && cap >= 0) ? ssmd::Launch{wpb, cap, 1} : ssmd::Launch{4, 0, 0};
+  }();
+  return l;
 }
 
 // Compute units of the current device, cached per device (a host-side query;
 // nothing is enqueued, so it is safe under stream capture).
 int cu_count(int* n) {
-  static int cache[64] = {0};
+  // per-device cache; concurrent first calls store the same value
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0)
     return fail(SSMD_ERR_LAUNCH, "hipGetDevice failed");
-  if (dev < 64 && cache[dev] > 0) {
-    *n = cache[dev];
-    return SSMD_OK;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *n = c;
+      return SSMD_OK;
+    }
   }
   int v = 0;
   if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
     return fail(SSMD_ERR_LAUNCH, "cannot read the compute-unit count of device %d", dev);
-  if (dev < 64) cache[dev] = v;
+  if (dev < 64) cache[dev].store(v, std::memory_order_relaxed);
   *n = v;
   return SSMD_OK;
 }

@@ -241,3 +241,29 @@ def test_check_slot_indices_host_validation():
     assert f(0x1000, 4, 4, 0, None, None) == NULL_ARG
     assert f(None, 4, 4, 0, 0x2000, None) == NULL_ARG
     assert f(0x1001, 4, 4, 0, 0x2000, None) == BAD_SHAPE
+
+
+def test_error_message_is_per_thread():
+    """Validation failures on several host threads at once: each thread reads
+    back its own message from ssmd_last_error (the error string is the only
+    mutable state, and it is thread-local)."""
+    import threading
+    L = S.load_library()
+    cases = {"H": (dict(HV=24, H=16), b"HV % H"), "K": (dict(K=48), b"K = 48"), "V": (dict(V=0), b"V = 0"),
+             "stride": (dict(stride=8191), b"qkv_row_stride")}
+    got, barrier = {}, threading.Barrier(len(cases))
+
+    def run(name, kw, needle):
+        barrier.wait()
+        ok = True
+        for _ in range(200):
+            rc = _gdn(L, **kw)
+            ok &= rc < 0 and needle in L.ssmd_last_error()
+        got[name] = ok
+
+    threads = [threading.Thread(target=run, args=(n, kw, nd)) for n, (kw, nd) in cases.items()]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert got == {n: True for n in cases}, got
