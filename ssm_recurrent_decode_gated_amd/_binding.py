@@ -9,6 +9,7 @@ and a missing library is an error, not a fallback.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import torch  # loads torch's HIP runtime first, so libssmdec.so binds to that one
@@ -113,6 +114,35 @@ def _stream(t: torch.Tensor, stream):
 _ACTS = (torch.float32, torch.bfloat16, torch.float16)
 
 
+def _one_device(fn):
+    """Entry-point wrapper: every tensor argument (and a torch stream, if
+    given) must be on one HIP device, which is made current for the call
+    (the library launches on the current device). Kept to integer device
+    ids on the common path: it runs on every eager call."""
+    @functools.wraps(fn)
+    def call(*args, **kwargs):
+        dev = None
+        for t in (*args, *kwargs.values()) if kwargs else args:
+            if isinstance(t, torch.Tensor):
+                g = t.get_device()
+                if g < 0:
+                    g = t.device.type  # host or meta tensor: rejected by the call's checks if alone
+                if dev is None:
+                    dev = g
+                elif g != dev:
+                    raise ValueError(f"{fn.__name__}: arguments on several devices ({dev} and {g})")
+        st = kwargs.get("stream")
+        if st is not None and hasattr(st, "device") and dev is not None:
+            sd = torch.device(st.device)
+            if sd.type != "cuda" or sd.index != dev:
+                raise ValueError(f"{fn.__name__}: stream on {sd}, tensors on {dev}")
+        if type(dev) is int and dev != torch.cuda.current_device():
+            with torch.cuda.device(dev):
+                return fn(*args, **kwargs)
+        return fn(*args, **kwargs)
+    return call
+
+
 def _gdn_common(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices, out, H, norm_gate,
                 norm_weight, state_dtypes=(torch.float32,)):
     _dev(state, "state", state_dtypes)
@@ -146,6 +176,7 @@ def _gdn_common(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices, out, 
     return B, H, HV, K, V, num_slots, DTYPE_CODE[act], DTYPE_CODE[out.dtype]
 
 
+@_one_device
 def gdn_decode_step(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices, out, *, H=None,
                     scale=None, use_qk_l2norm=True, l2norm_eps=1e-6, norm_gate=None,
                     norm_weight=None, norm_eps=1e-5, norm_act="silu", stream=None):
@@ -164,6 +195,7 @@ def gdn_decode_step(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices, o
     return out
 
 
+@_one_device
 def gdn_decode_step_state16(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices, out, *, H=None,
                             scale=None, use_qk_l2norm=True, l2norm_eps=1e-6, norm_gate=None,
                             norm_weight=None, norm_eps=1e-5, norm_act="silu", stream=None):
@@ -183,6 +215,7 @@ def gdn_decode_step_state16(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_in
     return out
 
 
+@_one_device
 def gdn_decode_step_buffered(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices, out,
                              d_cache, k_cache, g_cache, write_pos, *, H=None, scale=None,
                              use_qk_l2norm=True, l2norm_eps=1e-6, norm_gate=None, norm_weight=None,
@@ -246,6 +279,7 @@ def _gdn_multi_args(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices, o
     return B, T, H, HV, K, V, num_slots, row_stride, act
 
 
+@_one_device
 def gdn_fused_recurrent(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices, out, *, lengths=None, H=None,
                         scale=None, use_qk_l2norm=True, l2norm_eps=1e-6, norm_gate=None, norm_weight=None,
                         norm_eps=1e-5, norm_act="silu", stream=None):
@@ -272,6 +306,7 @@ def gdn_chunk_workspace_bytes(B, T, HV, K, V, with_norm=False) -> int:
     return n
 
 
+@_one_device
 def gdn_chunk_prefill(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices, out, *, workspace=None,
                       lengths=None, H=None, scale=None, use_qk_l2norm=True, l2norm_eps=1e-6, norm_gate=None,
                       norm_weight=None, norm_eps=1e-5, norm_act="silu", stream=None):
@@ -296,6 +331,7 @@ def gdn_chunk_prefill(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices,
     return out
 
 
+@_one_device
 def gdn_decode_step_conv(x, conv_weight, conv_bias, conv_state, a, b, A_log, dt_bias, state,
                          ssm_state_indices, out, *, H=None, scale=None, use_qk_l2norm=True,
                          l2norm_eps=1e-6, norm_gate=None, norm_weight=None, norm_eps=1e-5,
@@ -325,6 +361,7 @@ def gdn_decode_step_conv(x, conv_weight, conv_bias, conv_state, a, b, A_log, dt_
     return out
 
 
+@_one_device
 def kda_decode_step(x, conv_weight, conv_bias, conv_state, raw_g, raw_beta, A_log, dt_bias, state,
                     state_indices, out, *, output_gate=None, norm_weight=None, lower_bound=-5.0,
                     norm_eps=1e-5, scale=None, use_qk_l2norm=True, l2norm_eps=1e-6, stream=None):
@@ -380,6 +417,7 @@ def kda_decode_step(x, conv_weight, conv_bias, conv_state, raw_g, raw_beta, A_lo
     return out
 
 
+@_one_device
 def mamba_decode_step(x, dt, A, Bm, Cm, Dvec, z, state, state_indices, out, *, stream=None):
     """One Mamba-1 selective-scan decode step (state and out updated in
     place); see mamba_decode_step in include/ssmdec.h."""
@@ -417,6 +455,7 @@ def mamba_scan_workspace_bytes(B, T, Dm, N) -> int:
     return n
 
 
+@_one_device
 def mamba_scan(x, dt, A, Bm, Cm, Dvec, z, state, state_indices, out, *, lengths=None, zero_init=False,
                workspace=None, stream=None):
     """Mamba-1 over T tokens per row (prefill); see mamba_scan in
@@ -456,6 +495,7 @@ def mamba_scan(x, dt, A, Bm, Cm, Dvec, z, state, state_indices, out, *, lengths=
     return out
 
 
+@_one_device
 def ssmd_stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
     """Copy src to dst (same byte size) with the library's 128-bit stream kernel."""
     _dev(src, "src")
@@ -468,6 +508,7 @@ def ssmd_stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
     return dst
 
 
+@_one_device
 def ssmd_check_slot_indices(idx: torch.Tensor, num_slots: int, null_slot_zero: bool = False,
                             dup_count: torch.Tensor = None, stream=None) -> torch.Tensor:
     """Debug check: count the active rows of idx ([B] int32) whose slot an

@@ -8,6 +8,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import ssm_recurrent_decode_gated_amd as S
 from ssm_recurrent_decode_gated_amd import _binding as Bd
@@ -267,3 +268,15 @@ def test_error_message_is_per_thread():
     for t in threads:
         t.join()
     assert got == {n: True for n in cases}, got
+
+
+def test_binding_rejects_tensors_on_several_devices():
+    """The binding refuses a call whose tensors live on different devices
+    before anything reaches the library (host and meta tensors stand in for
+    two devices here)."""
+    src, dst = torch.zeros(4), torch.empty(4, device="meta")
+    with pytest.raises(ValueError, match="several devices"):
+        S.ssmd_stream_copy(src, dst)
+    with pytest.raises(ValueError, match="several devices"):
+        S.ssmd_check_slot_indices(torch.zeros(4, dtype=torch.int32), 4,
+                                  dup_count=torch.empty(1, dtype=torch.int32, device="meta"))
