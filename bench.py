@@ -15,7 +15,7 @@ same-size stream-copy ceiling, the roofline entry of the dominant kernel and
 the fp64 oracle's rate on the host cores.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-  python bench.py --profile-pass [gdn|kda|chunk]   # short run for rocprofv3 counter passes
+  python bench.py --profile-pass [gdn|kda|chunk|buffered]   # short run for rocprofv3 counter passes
   python bench.py --summarize-counters FETCH_DIR WRITE_DIR --kernel gdn|kda --out profiles/X.txt
   python bench.py --summarize-trace TRACE_DIR --title T --command C --out profiles/X.md
 """
@@ -524,6 +524,20 @@ def kda_alg_bytes(w, out_bytes=2, act=2):
             + C * w.W * 4)
 
 
+BUF_PROF_L, BUF_PROF_P = 8, 3  # ring length and phase of the buffered counter pass
+
+
+def buffered_nonflush_alg_bytes(w, p, act=2, outb=2):
+    """Bytes a non-flush buffered step at phase p must move: the checkpoint
+    and the p ring records read; q/k/v, a, b, A_log, dt_bias, indices and
+    phases read; the output and this step's record (delta, key, g) written."""
+    state = w.B * w.HV * w.V * w.K * 4
+    ring_rd = p * w.B * (w.HV * w.V * act + w.H * w.K * act + w.HV * 4)
+    inputs = w.B * (2 * w.H * w.K + w.HV * w.V) * act + 2 * w.B * w.HV * act + 2 * w.HV * 4 + 2 * w.B * 4
+    writes = w.B * w.HV * w.V * outb + w.B * (w.HV * w.V * act + w.H * w.K * act + w.HV * 4)
+    return state + ring_rd + inputs + writes
+
+
 def profile_pass(which="gdn"):
     """A few launches of one kernel (the headline GDN step, the fused KDA op at
     64 tokens x 96 heads, or the chunked GDN prefill of one and of eight
@@ -548,6 +562,16 @@ def profile_pass(which="gdn"):
             for _ in range(3):
                 S.gdn_chunk_prefill(qkv, a, b, su.A_log, su.dt_bias, su.pools[0], su.idx_d, out, workspace=ws)
             del su, qkv, a, b, out, ws
+    elif which == "buffered":
+        # non-flush steps of the buffered form: B = 64, phase 3 of an 8-record ring
+        w = W.GDN_B64_CHAIN
+        su = GDNSetup(w, 1, dev)
+        ring = {k: v.to(dev) for k, v in W.gdn_ring(w, BUF_PROF_L).items()}
+        wp = torch.full((w.B,), BUF_PROF_P, dtype=torch.int32, device=dev)
+        for _ in range(4):
+            S.gdn_decode_step_buffered(su.qkv, su.a, su.b, su.A_log, su.dt_bias, su.pools[0], su.idx_d, su.out,
+                                       ring["d_cache"], ring["k_cache"], ring["g_cache"], wp)
+        del su, ring
     elif which == "kda":
         w = W.KDA_T64
         d = {k: v.to(dev) for k, v in W.kda_inputs(w).items()}
@@ -591,6 +615,11 @@ def summarize_counters(fetch_dir, write_dir, out, command, which="gdn"):
         kernel, wl = "kda_decode_pf_kernel", W.KDA_T64
         alg = kda_alg_bytes(wl)
         title = f"# rocprofv3 HBM counters, {kernel} at 64 tokens x 96 heads (D=128, conv width 4, bf16 act, norm)"
+    elif which == "buffered":
+        kernel, wl = "gdn_buffered_kernel", W.GDN_B64_CHAIN
+        alg = buffered_nonflush_alg_bytes(wl, BUF_PROF_P)
+        title = (f"# rocprofv3 HBM counters, {kernel} at B=64 (H=16 HV=32 K=V=128, bf16 act and ring), "
+                 f"non-flush phase {BUF_PROF_P} of L={BUF_PROF_L}")
     else:
         kernel, wl = KERNEL_NAME, W.GDN_B256
         alg = gdn_alg_bytes(wl.B, wl.H, wl.HV, wl.K, wl.V)
@@ -649,11 +678,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline only (no sweep/buffered/KDA/conv/Mamba/copy)")
-    ap.add_argument("--profile-pass", nargs="?", const="gdn", choices=("gdn", "kda", "chunk"))
+    ap.add_argument("--profile-pass", nargs="?", const="gdn", choices=("gdn", "kda", "chunk", "buffered"))
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
     ap.add_argument("--title", default="")
-    ap.add_argument("--kernel", default="gdn", choices=("gdn", "kda"), help="which kernel --summarize-counters covers")
+    ap.add_argument("--kernel", default="gdn", choices=("gdn", "kda", "buffered"),
+                    help="which kernel --summarize-counters covers")
     ap.add_argument("--out", default=COUNTERS_FILE)
     ap.add_argument("--command", default="")
     args = ap.parse_args()
