@@ -15,7 +15,7 @@ same-size stream-copy ceiling, the roofline entry of the dominant kernel and
 the fp64 oracle's rate on the host cores.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-  python bench.py --profile-pass [gdn|kda|chunk|buffered]   # short run for rocprofv3 counter passes
+  python bench.py --profile-pass [gdn|kda|chunk|buffered|conv]   # short run for rocprofv3 counter passes
   python bench.py --summarize-counters FETCH_DIR WRITE_DIR --kernel gdn|kda --out profiles/X.txt
   python bench.py --summarize-trace TRACE_DIR --title T --command C --out profiles/X.md
 """
@@ -300,6 +300,13 @@ def kda(dev, reps=30, w=None):
     return res
 
 
+def gdn_conv_alg_bytes(w, Wd=4):
+    """The packed step's algorithmic bytes plus the conv state read and
+    written (16-bit) and the conv weights and bias read once (fp32)."""
+    C = 2 * w.H * w.K + w.HV * w.V
+    return gdn_alg_bytes(w.B, w.H, w.HV, w.K, w.V) + 2 * w.B * C * (Wd - 1) * 2 + C * (Wd + 1) * 4
+
+
 def gdn_conv(dev, reps=30, Wd=4):
     """The B=256-of-264 GDN step with its causal conv1d update fused in front
     (gdn_decode_step_conv, conv width 4, bf16 conv state in the [slots, C,
@@ -321,9 +328,8 @@ def gdn_conv(dev, reps=30, Wd=4):
         S.gdn_decode_step_conv(su.qkv, cw, cb, cs[i], su.a, su.b, su.A_log, su.dt_bias, su.pools[i], su.idx_d,
                                su.out)
     us = graph_time_us([lambda i=i: call(i) for i in range(M)], reps, torch.cuda.current_stream())
-    C = 2 * w.H * w.K + w.HV * w.V
     sb = gdn_state_bytes(w.B, w.HV, w.V, w.K)
-    ab = gdn_alg_bytes(w.B, w.H, w.HV, w.K, w.V) + 2 * w.B * C * (Wd - 1) * 2 + C * (Wd + 1) * 4
+    ab = gdn_conv_alg_bytes(w, Wd)
     del su, cs
     torch.cuda.empty_cache()
     return {"workload": w.name + f"_conv{Wd}", "us_per_step": round(us, 3), "state_GBps": round(sb / us / 1e3, 1),
@@ -562,6 +568,14 @@ def profile_pass(which="gdn"):
             for _ in range(3):
                 S.gdn_chunk_prefill(qkv, a, b, su.A_log, su.dt_bias, su.pools[0], su.idx_d, out, workspace=ws)
             del su, qkv, a, b, out, ws
+    elif which == "conv":
+        w = W.GDN_B256
+        su = GDNSetup(w, 1, dev)
+        cv = {k: v.to(dev) for k, v in W.gdn_conv(w, 4).items()}
+        for _ in range(4):
+            S.gdn_decode_step_conv(su.qkv, cv["conv_weight"], cv["conv_bias"], cv["conv_state"], su.a, su.b,
+                                   su.A_log, su.dt_bias, su.pools[0], su.idx_d, su.out)
+        del su, cv
     elif which == "buffered":
         # non-flush steps of the buffered form: B = 64, phase 3 of an 8-record ring
         w = W.GDN_B64_CHAIN
@@ -615,6 +629,10 @@ def summarize_counters(fetch_dir, write_dir, out, command, which="gdn"):
         kernel, wl = "kda_decode_pf_kernel", W.KDA_T64
         alg = kda_alg_bytes(wl)
         title = f"# rocprofv3 HBM counters, {kernel} at 64 tokens x 96 heads (D=128, conv width 4, bf16 act, norm)"
+    elif which == "conv":
+        kernel, wl = "gdn_conv_decode_kernel", W.GDN_B256
+        alg = gdn_conv_alg_bytes(wl, 4)
+        title = f"# rocprofv3 HBM counters, {kernel} at B=256 of 264 slots (H=16 HV=32 K=V=128, bf16 act, conv width 4)"
     elif which == "buffered":
         kernel, wl = "gdn_buffered_kernel", W.GDN_B64_CHAIN
         alg = buffered_nonflush_alg_bytes(wl, BUF_PROF_P)
@@ -678,11 +696,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline only (no sweep/buffered/KDA/conv/Mamba/copy)")
-    ap.add_argument("--profile-pass", nargs="?", const="gdn", choices=("gdn", "kda", "chunk", "buffered"))
+    ap.add_argument("--profile-pass", nargs="?", const="gdn", choices=("gdn", "kda", "chunk", "buffered", "conv"))
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
     ap.add_argument("--title", default="")
-    ap.add_argument("--kernel", default="gdn", choices=("gdn", "kda", "buffered"),
+    ap.add_argument("--kernel", default="gdn", choices=("gdn", "kda", "buffered", "conv"),
                     help="which kernel --summarize-counters covers")
     ap.add_argument("--out", default=COUNTERS_FILE)
     ap.add_argument("--command", default="")
