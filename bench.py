@@ -15,7 +15,7 @@ same-size stream-copy ceiling, the roofline entry of the dominant kernel and
 the fp64 oracle's rate on the host cores.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-  python bench.py --profile-pass [gdn|kda|chunk|buffered|conv]   # short run for rocprofv3 counter passes
+  python bench.py --profile-pass [gdn|kda|chunk|buffered|conv|state16|multi]   # rocprofv3 counter passes
   python bench.py --summarize-counters FETCH_DIR WRITE_DIR --kernel gdn|kda --out profiles/X.txt
   python bench.py --summarize-trace TRACE_DIR --title T --command C --out profiles/X.md
 """
@@ -531,6 +531,7 @@ def kda_alg_bytes(w, out_bytes=2, act=2):
 
 
 BUF_PROF_L, BUF_PROF_P = 8, 3  # ring length and phase of the buffered counter pass
+MULTI_PROF_T = 4  # tokens per row in the multi-token counter pass
 
 
 def buffered_nonflush_alg_bytes(w, p, act=2, outb=2):
@@ -568,6 +569,25 @@ def profile_pass(which="gdn"):
             for _ in range(3):
                 S.gdn_chunk_prefill(qkv, a, b, su.A_log, su.dt_bias, su.pools[0], su.idx_d, out, workspace=ws)
             del su, qkv, a, b, out, ws
+    elif which == "state16":
+        w = W.GDN_B256
+        su = GDNSetup(w, 1, dev)
+        st16 = su.pools[0].to(torch.bfloat16)
+        for _ in range(4):
+            S.gdn_decode_step_state16(su.qkv, su.a, su.b, su.A_log, su.dt_bias, st16, su.idx_d, su.out)
+        del su, st16
+    elif which == "multi":
+        w = W.GDN_B256
+        su = GDNSetup(w, 1, dev)
+        g = W.generator(0, w.name, "multi", MULTI_PROF_T)
+        C = 2 * w.H * w.K + w.HV * w.V
+        qkv = W.normal((w.B, MULTI_PROF_T, C), 1.0, "bf16", g).to(dev)
+        a = W.normal((w.B, MULTI_PROF_T, w.HV), 0.5, "bf16", g).to(dev)
+        b = W.normal((w.B, MULTI_PROF_T, w.HV), 1.0, "bf16", g).to(dev)
+        out = torch.empty(w.B, MULTI_PROF_T, w.HV, w.V, dtype=torch.bfloat16, device=dev)
+        for _ in range(4):
+            S.gdn_fused_recurrent(qkv, a, b, su.A_log, su.dt_bias, su.pools[0], su.idx_d, out)
+        del su, qkv, a, b, out
     elif which == "conv":
         w = W.GDN_B256
         su = GDNSetup(w, 1, dev)
@@ -629,6 +649,16 @@ def summarize_counters(fetch_dir, write_dir, out, command, which="gdn"):
         kernel, wl = "kda_decode_pf_kernel", W.KDA_T64
         alg = kda_alg_bytes(wl)
         title = f"# rocprofv3 HBM counters, {kernel} at 64 tokens x 96 heads (D=128, conv width 4, bf16 act, norm)"
+    elif which == "state16":
+        kernel, wl = "gdn_decode_s16_kernel", W.GDN_B256
+        alg = gdn_alg_bytes(wl.B, wl.H, wl.HV, wl.K, wl.V) - gdn_state_bytes(wl.B, wl.HV, wl.V, wl.K) // 2
+        title = f"# rocprofv3 HBM counters, {kernel} at B=256 of 264 slots (H=16 HV=32 K=V=128, bf16 act, bf16 state)"
+    elif which == "multi":
+        kernel, wl = "gdn_multi_kernel", W.GDN_B256
+        T = MULTI_PROF_T
+        alg = (gdn_state_bytes(wl.B, wl.HV, wl.V, wl.K) + T * wl.B * (2 * wl.H * wl.K + wl.HV * wl.V) * 2
+               + 2 * T * wl.B * wl.HV * 2 + T * wl.B * wl.HV * wl.V * 2 + 2 * wl.HV * 4 + wl.B * 4)
+        title = f"# rocprofv3 HBM counters, {kernel} at B=256 of 264 slots x {T} tokens (H=16 HV=32 K=V=128, bf16)"
     elif which == "conv":
         kernel, wl = "gdn_conv_decode_kernel", W.GDN_B256
         alg = gdn_conv_alg_bytes(wl, 4)
@@ -696,11 +726,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline only (no sweep/buffered/KDA/conv/Mamba/copy)")
-    ap.add_argument("--profile-pass", nargs="?", const="gdn", choices=("gdn", "kda", "chunk", "buffered", "conv"))
+    ap.add_argument("--profile-pass", nargs="?", const="gdn",
+                    choices=("gdn", "kda", "chunk", "buffered", "conv", "state16", "multi"))
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
     ap.add_argument("--title", default="")
-    ap.add_argument("--kernel", default="gdn", choices=("gdn", "kda", "buffered", "conv"),
+    ap.add_argument("--kernel", default="gdn", choices=("gdn", "kda", "buffered", "conv", "state16", "multi"),
                     help="which kernel --summarize-counters covers")
     ap.add_argument("--out", default=COUNTERS_FILE)
     ap.add_argument("--command", default="")
