@@ -405,7 +405,7 @@ int ssmd_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stre
  * earlier active row already names and writes the count to *dup_count
  * (0: the vector is valid).
  *
- *   slot_indices [B] int32 (device); B >= 0 (B == 0 writes 0)
+ *   slot_indices [B] int32 (device); 0 <= B <= 65536 (B == 0 writes 0)
  *   num_slots    pool size: indices outside [0, num_slots) are padded rows
  *   null_slot_zero  non-zero for kda_decode_step's convention, where slot 0
  *                is the NULL block and pads the row too
@@ -414,8 +414,8 @@ int ssmd_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stre
  * One workgroup compares each row with every earlier one (O(B^2)): a debug
  * aid, not meant for the timed path. Enqueued asynchronously like the
  * steps; the caller reads *dup_count after synchronising. Errors:
- * SSMD_ERR_NULL_ARG, SSMD_ERR_BAD_SHAPE (B < 0, num_slots < 1, misaligned
- * pointers), SSMD_ERR_LAUNCH.
+ * SSMD_ERR_NULL_ARG, SSMD_ERR_BAD_SHAPE (B outside [0, 65536], num_slots < 1,
+ * misaligned pointers), SSMD_ERR_LAUNCH.
  */
 int ssmd_check_slot_indices(const int32_t* slot_indices, int32_t B, int32_t num_slots,
                             int32_t null_slot_zero, int32_t* dup_count, hipStream_t stream);

@@ -561,7 +561,8 @@ int ssmd_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stre
 int ssmd_check_slot_indices(const int32_t* slot_indices, int32_t B, int32_t num_slots, int32_t null_slot_zero,
                             int32_t* dup_count, hipStream_t stream) {
   const char* fn = "ssmd_check_slot_indices";
-  if (B < 0) return fail(SSMD_ERR_BAD_SHAPE, "%s: B = %d < 0", fn, B);
+  // one workgroup compares every pair: 65536 rows is about 2^31 comparisons
+  if (B < 0 || B > 65536) return fail(SSMD_ERR_BAD_SHAPE, "%s: B = %d outside [0, 65536]", fn, B);
   if (num_slots < 1) return fail(SSMD_ERR_BAD_SHAPE, "%s: num_slots = %d < 1", fn, num_slots);
   if (!dup_count) return fail(SSMD_ERR_NULL_ARG, "%s: dup_count is NULL", fn);
   if (B > 0 && !slot_indices) return fail(SSMD_ERR_NULL_ARG, "%s: slot_indices is NULL", fn);

@@ -238,6 +238,7 @@ def test_check_slot_indices_host_validation():
     L = S.load_library()
     f = L.ssmd_check_slot_indices
     assert f(0x1000, -1, 4, 0, 0x2000, None) == BAD_SHAPE
+    assert f(0x1000, 65537, 4, 0, 0x2000, None) == BAD_SHAPE
     assert f(0x1000, 4, 0, 0, 0x2000, None) == BAD_SHAPE
     assert f(0x1000, 4, 4, 0, None, None) == NULL_ARG
     assert f(None, 4, 4, 0, 0x2000, None) == NULL_ARG
