@@ -141,3 +141,26 @@ def test_graph_gdn_multi_and_chunked():
     _replay_matches_eager(make, lambda d: S.gdn_chunk_prefill(d["qkv"], d["a"], d["b"], d["A_log"], d["dt_bias"],
                                                               d["st"], d["idx"], d["out"], workspace=d["ws"]),
                           lambda d: (d["st"], d["out"]))
+
+
+def test_graph_slot_index_check_and_stream_copy():
+    """The two helper entry points captured too: the duplicate-slot count
+    (into a result the graph overwrites each replay) and the stream copy."""
+    need_gpu()
+
+    def make():
+        idx = W.slot_indices(W.GDN_B256).clone()
+        idx[7] = idx[3]  # one planted duplicate
+        return {"idx": idx.to(DEV), "dups": torch.full((1,), -1, dtype=torch.int32, device=DEV),
+                "src": torch.arange(4096, dtype=torch.float32, device=DEV),
+                "dst": torch.zeros(4096, dtype=torch.float32, device=DEV)}
+
+    def call(d):
+        S.ssmd_check_slot_indices(d["idx"], 264, dup_count=d["dups"])
+        S.ssmd_stream_copy(d["src"], d["dst"])
+
+    _replay_matches_eager(make, call, lambda d: (d["dups"], d["dst"]))
+    d = make()
+    call(d)
+    torch.cuda.synchronize()
+    assert int(d["dups"].item()) == 1
