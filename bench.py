@@ -206,6 +206,11 @@ def sweep(dev, batches=(1, 16, 64, 256), reps=50):
         res[f"B{B}"] = {"us_per_step": round(us, 3), "state_GBps": round(sb / us / 1e3, 1),
                         "pct_hbm_peak": round(100 * sb / us / 1e3 / HBM_PEAK_GBS, 2), "pools": M,
                         "eager_us_per_step": round(eager, 3)}
+        if B == 1:
+            # a graph holding one call, replayed: what one graph launch costs
+            # when nothing amortises it (the page's one-call KDA graph)
+            res["B1"]["one_call_graph_us"] = round(
+                graph_time_us([lambda: su.call(0)], reps, torch.cuda.current_stream()), 3)
         if pool_bytes <= MALL_BYTES // 2:
             # one pool stepped over and over: its state stays in the Infinity
             # Cache, so this is a cache rate, not an HBM one
