@@ -363,7 +363,10 @@ def mamba(dev, reps=30):
             S.mamba_decode_step(dd["x"], dd["dt"], dd["A"], dd["Bm"], dd["Cm"], dd["Dv"], dd["z"], pools[i],
                                 dd["idx"], out)
         us = graph_time_us([lambda i=i: call(i) for i in range(M)], reps, torch.cuda.current_stream())
-        res[f"B{B}_D{Dm}_N{N}"] = {"us_per_step": round(us, 3),
+        # launched one by one from Python, as the write-up's table times its calls
+        it = iter(range(10 ** 9))
+        eager = _events_ms(lambda: call(next(it) % M), M * reps, torch.cuda.current_stream()) * 1e3 / (M * reps)
+        res[f"B{B}_D{Dm}_N{N}"] = {"us_per_step": round(us, 3), "eager_us_per_step": round(eager, 3),
                                    "page_model_GBps": round(B * Dm * (20 * N + 24) / us / 1e3, 1),
                                    "state_GBps": round(B * Dm * N * 8 / us / 1e3, 1), "pools": M}
         del pools, dd
