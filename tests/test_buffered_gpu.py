@@ -60,6 +60,15 @@ def test_buffered_single_call_every_phase(case):
     _single_call_case(case)
 
 
+def test_buffered_f16_ring_every_phase():
+    """f16 activations and ring records (the other 16-bit format): outputs,
+    flushed states and records against the oracle's f16 ring, with rows at
+    every phase of L = 8 in one launch, aligned and unaligned ring bases."""
+    _single_call_case(("k128_L8_f16", 8, 2, 4, 128, 128, 8, [0, 1, 2, 3, 4, 5, 6, 7], False), act="f16")
+    _single_call_case(("k64_v40_L5_f16_unaligned", 5, 1, 3, 64, 40, 5, [4, 2, 0, 1, 3], False), ring_offset=1,
+                      act="f16")
+
+
 def test_buffered_long_and_unaligned_rings():
     """A 32-record ring (more records than the vector staging covers in one
     go) and 16-bit rings whose base is not 8-byte aligned (element loads)."""
@@ -78,10 +87,11 @@ def _exact_records(w, x, P, st, idx, ring, wp, L, kw):
     return ex
 
 
-def _single_call_case(case, ring_offset=0):
+def _single_call_case(case, ring_offset=0, act="bf16"):
     need_gpu()
     name, B, H, HV, K, V, L, phases, norm = case
-    w = W.GDNWorkload("buf_" + name, B=B, H=H, HV=HV, K=K, V=V, num_slots=B + 2, out="f32", idx="perm")
+    w = W.GDNWorkload("buf_" + name, B=B, H=H, HV=HV, K=K, V=V, num_slots=B + 2, out="f32", idx="perm", act=act)
+    fmt, mant = {"bf16": (O.FMT_BF16, 7), "f16": (O.FMT_F16, 10)}[act]
     P, idx, x = W.gdn_params(w), W.slot_indices(w), W.gdn_step_inputs(w, norm=norm)
     st = W.gdn_state(w)
     ring = W.gdn_ring(w, L)
@@ -95,7 +105,7 @@ def _single_call_case(case, ring_offset=0):
     kw = dict(norm_gate=x["norm_gate"], norm_weight=x["norm_weight"]) if norm else {}
     ro = O.gdn_step_buffered(x["qkv"], x["a"], x["b"], P["A_log"], P["dt_bias"], ref_st, idx,
                              ref_ring["d_cache"], ref_ring["k_cache"], ref_ring["g_cache"], wp, L,
-                             H=H, HV=HV, K=K, V=V, ring_fmt=O.FMT_BF16, **kw)
+                             H=H, HV=HV, K=K, V=V, ring_fmt=fmt, **kw)
     ex_ring = _exact_records(w, x, P, st, idx, ring, wp, L, kw)
     torch.cuda.synchronize()
     assert_mixed(out.reshape(B, HV, V), ro, FP32_TOL, "output")
@@ -110,9 +120,9 @@ def _single_call_case(case, ring_offset=0):
         else:
             assert torch.equal(got_st[s], st[s]), f"non-flush row {b} wrote the checkpoint"
         assert_ring16(got["d_cache"][s, :, p], ref_ring["d_cache"][s, :, p], f"delta record row {b}",
-                       ex_ring["d_cache"][s, :, p])
+                       ex_ring["d_cache"][s, :, p], mant)
         assert_ring16(got["k_cache"][s, :, p], ref_ring["k_cache"][s, :, p], f"key record row {b}",
-                       ex_ring["k_cache"][s, :, p])
+                       ex_ring["k_cache"][s, :, p], mant)
         np.testing.assert_allclose(got["g_cache"][s, :, p], ref_ring["g_cache"][s, :, p], rtol=1e-5)
         others = [j for j in range(L) if j != p]
         for k in ring0:
