@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 import torch
 
-from tests._helpers import assert_ring16
+from tests._helpers import assert_ring16, ulp16
 
 
 def _bf16_rne(x):
@@ -52,3 +52,27 @@ def test_ring16_rejects_a_two_ulp_error():
     bad[5, 7] += 2 * 2.0 ** (np.floor(np.log2(abs(ref[5, 7]))) - 7)
     with pytest.raises(AssertionError):
         assert_ring16(bad, ref, "two ulp", ex)
+
+
+def test_ulp16_spacing_including_subnormals():
+    """The 16-bit spacings the checks allow, against the formats' own
+    neighbours (torch's conversions): normal range and f16 subnormals."""
+    def rnd(v, dt):
+        return float(torch.tensor([v], dtype=torch.float64).to(dt).double().item())
+
+    for x, mant, dt in ((1.0, 7, torch.bfloat16), (0.3, 7, torch.bfloat16), (1.0, 10, torch.float16),
+                        (0.3, 10, torch.float16), (4.9e-6, 10, torch.float16), (2.0 ** -20, 10, torch.float16)):
+        v = rnd(x, dt)  # a representable value
+        u = float(ulp16(np.array([v]), mant)[0])
+        assert rnd(v + u, dt) == v + u, (x, mant)  # one spacing up is the next representable value
+        assert rnd(v + 0.49 * u, dt) == v, (x, mant)  # under half a spacing rounds back
+
+
+def test_ring16_f16_subnormal_neighbour_accepted():
+    """A tiny f16 record (subnormal) one spacing from the oracle's rounding,
+    with its exact value at the midpoint: accepted."""
+    ex = np.array([[1.0, -0.5, 4.9e-6 + 2.0 ** -25 * 1.0000001, 0.25]])
+    ref = torch.from_numpy(ex).to(torch.float16).double().numpy()
+    got = ref.copy()
+    got[0, 2] = ref[0, 2] + 2.0 ** -24 if ref[0, 2] < ex[0, 2] else ref[0, 2] - 2.0 ** -24
+    assert_ring16(got, ref, "f16 subnormal", ex, 10)

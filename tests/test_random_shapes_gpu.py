@@ -1,0 +1,188 @@
+"""Seeded random-shape parity sweep of the decode entry points against the
+fp64 oracle: head sizes, ragged value dims, GQA ratios, dtypes, gated norm
+on/off, padded rows and (buffered) mixed and out-of-range phases drawn from a
+fixed generator, so every run checks the same cases. Complements the
+hand-picked cases of the per-entry-point tests with combinations nobody chose.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import ssm_recurrent_decode_gated_amd as S
+import workloads as W
+from tests._helpers import FP32_TOL, assert_16bit, assert_mixed, assert_ring16, need_gpu, to_np64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TD = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+FMT = {"f32": O.FMT_F32, "bf16": O.FMT_BF16, "f16": O.FMT_F16}
+MANT = {"bf16": 7, "f16": 10}
+
+
+def _draw(rng, i):
+    K = int(rng.choice([16, 32, 64, 128, 256]))
+    H = int(rng.integers(1, 4))
+    G = int(rng.choice([1, 2, 4]))
+    V = int(rng.choice([1, 3, 16, 40, 64, 100, 128, 200, 300]))
+    B = int(rng.integers(1, 10))
+    slots = B + int(rng.integers(0, 5))
+    act = str(rng.choice(["f32", "bf16", "f16"]))
+    out = str(rng.choice(["f32", "bf16", "f16"]))
+    norm = str(rng.choice(["none", "silu", "sigmoid"]))
+    w = W.GDNWorkload(f"rand{i}_k{K}_h{H}_g{G}_v{V}_b{B}_{act}", B=B, H=H, HV=G * H, K=K, V=V, num_slots=slots,
+                      act=act, out=out, idx="perm")
+    idx = W.slot_indices(w).clone()
+    for b in range(B):  # about one row in five padded, both ways
+        if rng.random() < 0.2:
+            idx[b] = -1 if rng.random() < 0.5 else slots + int(rng.integers(0, 3))
+    return w, idx, norm
+
+
+def _check(out, ref, live, what):
+    if not live:
+        return
+    o = out[live]
+    if o.dtype == torch.float32:
+        assert_mixed(o, ref[live], FP32_TOL, what)
+    else:
+        assert_16bit(o, ref[live], FP32_TOL, what)
+
+
+CASES = list(range(24))
+
+
+@pytest.mark.parametrize("i", CASES)
+def test_random_gdn_step(i):
+    need_gpu()
+    rng = np.random.default_rng(1000 + i)
+    w, idx, norm = _draw(rng, i)
+    P, x = W.gdn_params(w), W.gdn_step_inputs(w, norm=norm != "none")
+    st = W.gdn_state(w)
+    st_d = st.to(DEV)
+    out = torch.full((w.B, 1, w.HV, w.V), float("nan"), dtype=TD[w.out], device=DEV)
+    kw, okw = {}, {}
+    if norm != "none":
+        kw = dict(norm_gate=x["norm_gate"].to(DEV), norm_weight=x["norm_weight"].to(DEV), norm_act=norm)
+        okw = dict(norm_gate=x["norm_gate"], norm_weight=x["norm_weight"],
+                   norm_act=O.ACT_SIGMOID if norm == "sigmoid" else O.ACT_SILU)
+    S.gdn_decode_step(x["qkv"].to(DEV), x["a"].to(DEV), x["b"].to(DEV), P["A_log"].to(DEV), P["dt_bias"].to(DEV),
+                      st_d, idx.to(DEV), out, **kw)
+    ref = st.double().numpy().copy()
+    ro = O.gdn_step(x["qkv"], x["a"], x["b"], P["A_log"], P["dt_bias"], ref, idx, H=w.H, HV=w.HV, K=w.K, V=w.V,
+                    **okw)
+    torch.cuda.synchronize()
+    live = [b for b in range(w.B) if 0 <= int(idx[b]) < w.num_slots]
+    o = out.reshape(w.B, w.HV, w.V)
+    _check(o, ro, live, f"case {i} ({w.name}, norm {norm}) output")
+    dead = [b for b in range(w.B) if b not in live]
+    if dead:
+        assert torch.isnan(o[dead].float()).all(), f"case {i}: a padded row wrote its output"
+    got = st_d.cpu()
+    named = {int(idx[b]) for b in live}
+    for s in range(w.num_slots):
+        if s in named:
+            assert_mixed(got[s], ref[s], FP32_TOL, f"case {i} slot {s}")
+        else:
+            assert torch.equal(got[s], st[s]), f"case {i}: slot {s} changed"
+
+
+@pytest.mark.parametrize("i", CASES)
+def test_random_gdn_buffered(i):
+    need_gpu()
+    rng = np.random.default_rng(2000 + i)
+    w, idx, norm = _draw(rng, 100 + i)
+    L = int(rng.integers(1, 17))
+    phases = [int(rng.integers(0, L)) if rng.random() > 0.1 else L for _ in range(w.B)]
+    P, x = W.gdn_params(w), W.gdn_step_inputs(w, norm=norm != "none")
+    st = W.gdn_state(w)
+    ring = W.gdn_ring(w, L)
+    st_d = st.to(DEV)
+    ring_d = {k: v.to(DEV) for k, v in ring.items()}
+    wp = torch.tensor(phases, dtype=torch.int32)
+    out = torch.full((w.B, 1, w.HV, w.V), float("nan"), dtype=TD[w.out], device=DEV)
+    kw, okw = {}, {}
+    if norm != "none":
+        kw = dict(norm_gate=x["norm_gate"].to(DEV), norm_weight=x["norm_weight"].to(DEV), norm_act=norm)
+        okw = dict(norm_gate=x["norm_gate"], norm_weight=x["norm_weight"],
+                   norm_act=O.ACT_SIGMOID if norm == "sigmoid" else O.ACT_SILU)
+    S.gdn_decode_step_buffered(x["qkv"].to(DEV), x["a"].to(DEV), x["b"].to(DEV), P["A_log"].to(DEV),
+                               P["dt_bias"].to(DEV), st_d, idx.to(DEV), out, ring_d["d_cache"], ring_d["k_cache"],
+                               ring_d["g_cache"], wp.to(DEV), **kw)
+    ref = st.double().numpy().copy()
+    rr = {k: v.double().numpy().copy() for k, v in ring.items()}
+    ro = O.gdn_step_buffered(x["qkv"], x["a"], x["b"], P["A_log"], P["dt_bias"], ref, idx, rr["d_cache"],
+                             rr["k_cache"], rr["g_cache"], wp, L, H=w.H, HV=w.HV, K=w.K, V=w.V,
+                             ring_fmt=FMT[w.act], **okw)
+    ex = {k: v.double().numpy().copy() for k, v in ring.items()}
+    O.gdn_step_buffered(x["qkv"], x["a"], x["b"], P["A_log"], P["dt_bias"], st.double().numpy().copy(), idx,
+                        ex["d_cache"], ex["k_cache"], ex["g_cache"], wp, L, H=w.H, HV=w.HV, K=w.K, V=w.V,
+                        ring_fmt=O.FMT_NONE, **okw)
+    torch.cuda.synchronize()
+    live = [b for b in range(w.B) if 0 <= int(idx[b]) < w.num_slots and 0 <= phases[b] < L]
+    o = out.reshape(w.B, w.HV, w.V)
+    _check(o, ro, live, f"case {i} ({w.name}, L {L}, norm {norm}) output")
+    got_st = st_d.cpu()
+    got = {k: to_np64(v) for k, v in ring_d.items()}
+    for b in live:
+        s, p = int(idx[b]), phases[b]
+        if p == L - 1:
+            assert_mixed(got_st[s], ref[s], FP32_TOL, f"case {i} flushed slot {s}")
+        else:
+            assert torch.equal(got_st[s], st[s]), f"case {i}: non-flush slot {s} written"
+        for k in ("d_cache", "k_cache"):
+            if w.act == "f32":
+                assert_mixed(got[k][s][:, p], rr[k][s][:, p], FP32_TOL, f"case {i} {k} row {b}")
+            else:
+                assert_ring16(got[k][s][:, p], rr[k][s][:, p], f"case {i} {k} row {b}", ex[k][s][:, p],
+                              MANT[w.act])
+        np.testing.assert_allclose(got["g_cache"][s][:, p], rr["g_cache"][s][:, p], rtol=1e-5)
+    touched = {int(idx[b]) for b in live}
+    for s in set(range(w.num_slots)) - touched:
+        assert torch.equal(got_st[s], st[s]), f"case {i}: slot {s} changed"
+
+
+@pytest.mark.parametrize("i", CASES[:12])
+def test_random_kda(i):
+    need_gpu()
+    rng = np.random.default_rng(3000 + i)
+    D = int(rng.choice([16, 32, 64, 128, 256]))
+    H = int(rng.integers(1, 5))
+    T = int(rng.integers(1, 9))
+    Wd = int(rng.choice([2, 3, 4, 4]))
+    w = W.KDAWorkload(f"kda_rand{i}_d{D}_h{H}_t{T}_w{Wd}", T=T, H=H, D=D, W=Wd, num_slots=T + 3)
+    layout = str(rng.choice(["SD", "DS"]))
+    d = W.kda_inputs(w, layout=layout)
+    for t in range(T):  # about one token in five skipped: the NULL slot 0 or past the pool
+        if rng.random() < 0.2:
+            d["idx"][t] = 0 if rng.random() < 0.5 else w.num_slots
+    norm = bool(rng.random() < 0.6)
+    cs_d = d["conv_state"].to(DEV)
+    st_d = d["state"].to(DEV)
+    out = torch.full((T, H, D), 7.0, dtype=torch.float32, device=DEV)
+    S.kda_decode_step(d["x"].to(DEV), d["conv_weight"].to(DEV), None, cs_d, d["raw_g"].to(DEV),
+                      d["raw_beta"].to(DEV), None, None, st_d, d["idx"].to(DEV), out,
+                      output_gate=d["gate"].to(DEV) if norm else None,
+                      norm_weight=d["norm_weight"].to(DEV) if norm else None,
+                      lower_bound=w.lower_bound, norm_eps=w.norm_eps)
+    cs_ref = d["conv_state"].double().numpy().copy()
+    st_ref = d["state"].double().numpy().copy()
+    ro = O.kda_decode(d["x"], d["conv_weight"], None, cs_ref, d["raw_g"], d["raw_beta"], st_ref, d["idx"], H=H, D=D,
+                      lower_bound=w.lower_bound, gate=d["gate"] if norm else None,
+                      norm_weight=d["norm_weight"] if norm else None, norm_eps=w.norm_eps)
+    torch.cuda.synchronize()
+    live = [t for t, s in enumerate(d["idx"].tolist()) if 0 < s < w.num_slots]
+    if live:
+        assert_mixed(out[live], ro[live], FP32_TOL, f"case {i} ({w.name}, {layout}, norm {norm}) output")
+    got = st_d.cpu()
+    named = {int(d["idx"][t]) for t in live}
+    for s in range(w.num_slots):
+        if s in named:
+            assert_mixed(got[s], st_ref[s], FP32_TOL, f"case {i} state slot {s}")
+        else:
+            assert torch.equal(got[s], d["state"][s]), f"case {i}: slot {s} changed"
+    skipped = [t for t in range(T) if t not in live]
+    if skipped:
+        assert (out[skipped] == 7.0).all(), f"case {i}: a skipped token wrote its output"
+    # the conv state holds raw inputs: bit for bit
+    assert np.array_equal(to_np64(cs_d), cs_ref), f"case {i}: conv state differs"
