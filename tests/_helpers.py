@@ -79,8 +79,9 @@ def need_gpu():
 MIDPOINT_REL = 2.0 ** -16  # far above fp32 rounding error, far below half a 16-bit ulp (2^-9 bf16, 2^-12 f16)
 
 
-def assert_ring16(got, ref, what, exact, mant_bits=7):
-    """A stored 16-bit record may differ from the oracle's rounding by one ulp
+def assert_rounded16(got, ref, what, exact, mant_bits=7):
+    """A stored 16-bit value (a ring record, a 16-bit state row) may differ
+    from the oracle's rounding by one ulp
     only where the exact (unrounded) value sits at the rounding midpoint
     between the two neighbours, to within fp32 arithmetic error (2^-16 of
     max(|value|, rms of its record)): there both neighbours are correct
@@ -94,7 +95,7 @@ def assert_ring16(got, ref, what, exact, mant_bits=7):
     # metric: delta = beta (v - S k) can cancel, so its error tracks the row, not itself
     scale = np.maximum(np.abs(exact), np.sqrt(np.mean(exact * exact, axis=-1, keepdims=True)))
     assert (diff <= ulp16(ref, mant_bits) * 1.0000001 + MIDPOINT_REL * scale).all(), \
-        f"{what}: record off by more than one ulp"
+        f"{what}: stored value off by more than one ulp"
     flip = diff != 0
     off_mid = np.abs(exact - 0.5 * (got + ref)) > MIDPOINT_REL * scale
     assert not (flip & off_mid).any(), \

@@ -16,7 +16,7 @@ import torch
 import oracle as O
 import ssm_recurrent_decode_gated_amd as S
 import workloads as W
-from tests._helpers import CHAIN_TOL, FP32_TOL, assert_mixed, assert_ring16, need_gpu, to_np64
+from tests._helpers import CHAIN_TOL, FP32_TOL, assert_mixed, assert_rounded16, need_gpu, to_np64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -119,9 +119,9 @@ def _single_call_case(case, ring_offset=0, act="bf16"):
             assert_mixed(got_st[s], ref_st[s], FP32_TOL, f"flushed state row {b}")
         else:
             assert torch.equal(got_st[s], st[s]), f"non-flush row {b} wrote the checkpoint"
-        assert_ring16(got["d_cache"][s, :, p], ref_ring["d_cache"][s, :, p], f"delta record row {b}",
+        assert_rounded16(got["d_cache"][s, :, p], ref_ring["d_cache"][s, :, p], f"delta record row {b}",
                        ex_ring["d_cache"][s, :, p], mant)
-        assert_ring16(got["k_cache"][s, :, p], ref_ring["k_cache"][s, :, p], f"key record row {b}",
+        assert_rounded16(got["k_cache"][s, :, p], ref_ring["k_cache"][s, :, p], f"key record row {b}",
                        ex_ring["k_cache"][s, :, p], mant)
         np.testing.assert_allclose(got["g_cache"][s, :, p], ref_ring["g_cache"][s, :, p], rtol=1e-5)
         others = [j for j in range(L) if j != p]
@@ -259,9 +259,9 @@ def test_buffered_many_rows_with_padding(K, V, HV, L):
             assert_mixed(got_st[s], ref_st[s], FP32_TOL, f"flushed state row {b}")
         else:
             assert torch.equal(got_st[s], st[s]), f"non-flush row {b} wrote the checkpoint"
-        assert_ring16(got["d_cache"][s, :, p], ref_ring["d_cache"][s, :, p], f"delta record row {b}",
+        assert_rounded16(got["d_cache"][s, :, p], ref_ring["d_cache"][s, :, p], f"delta record row {b}",
                        ex_ring["d_cache"][s, :, p])
-        assert_ring16(got["k_cache"][s, :, p], ref_ring["k_cache"][s, :, p], f"key record row {b}",
+        assert_rounded16(got["k_cache"][s, :, p], ref_ring["k_cache"][s, :, p], f"key record row {b}",
                        ex_ring["k_cache"][s, :, p])
         np.testing.assert_allclose(got["g_cache"][s, :, p], ref_ring["g_cache"][s, :, p], rtol=1e-5)
     touched = {int(idx[b]) for b in live}

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 import torch
 
-from tests._helpers import assert_ring16, ulp16
+from tests._helpers import assert_rounded16, ulp16
 
 
 def _bf16_rne(x):
@@ -25,7 +25,7 @@ def _records(seed=0):
 def test_ring16_accepts_the_correct_rounding():
     ex = _records()
     ref = _bf16_rne(ex)
-    assert_ring16(ref, ref, "identical", ex)
+    assert_rounded16(ref, ref, "identical", ex)
 
 
 def test_ring16_accepts_the_other_neighbour_at_a_midpoint():
@@ -36,13 +36,13 @@ def test_ring16_accepts_the_other_neighbour_at_a_midpoint():
     ex = lo + 0.5 * ulp * np.sign(lo) * (1 + 1e-7)
     ref = _bf16_rne(ex)
     other = np.where(ref == lo, lo + ulp * np.sign(lo), lo)
-    assert_ring16(other, ref, "midpoints", ex)
+    assert_rounded16(other, ref, "midpoints", ex)
 
 
 def test_ring16_rejects_truncation():
     ex = _records(2)
     with pytest.raises(AssertionError):
-        assert_ring16(_bf16_trunc(ex), _bf16_rne(ex), "truncated", ex)
+        assert_rounded16(_bf16_trunc(ex), _bf16_rne(ex), "truncated", ex)
 
 
 def test_ring16_rejects_a_two_ulp_error():
@@ -51,7 +51,7 @@ def test_ring16_rejects_a_two_ulp_error():
     bad = ref.copy()
     bad[5, 7] += 2 * 2.0 ** (np.floor(np.log2(abs(ref[5, 7]))) - 7)
     with pytest.raises(AssertionError):
-        assert_ring16(bad, ref, "two ulp", ex)
+        assert_rounded16(bad, ref, "two ulp", ex)
 
 
 def test_ulp16_spacing_including_subnormals():
@@ -75,4 +75,4 @@ def test_ring16_f16_subnormal_neighbour_accepted():
     ref = torch.from_numpy(ex).to(torch.float16).double().numpy()
     got = ref.copy()
     got[0, 2] = ref[0, 2] + 2.0 ** -24 if ref[0, 2] < ex[0, 2] else ref[0, 2] - 2.0 ** -24
-    assert_ring16(got, ref, "f16 subnormal", ex, 10)
+    assert_rounded16(got, ref, "f16 subnormal", ex, 10)

@@ -11,7 +11,7 @@ import torch
 import oracle as O
 import ssm_recurrent_decode_gated_amd as S
 import workloads as W
-from tests._helpers import FP32_TOL, assert_16bit, assert_mixed, assert_ring16, need_gpu, to_np64
+from tests._helpers import FP32_TOL, assert_16bit, assert_mixed, assert_rounded16, need_gpu, to_np64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -134,7 +134,7 @@ def test_random_gdn_buffered(i):
             if w.act == "f32":
                 assert_mixed(got[k][s][:, p], rr[k][s][:, p], FP32_TOL, f"case {i} {k} row {b}")
             else:
-                assert_ring16(got[k][s][:, p], rr[k][s][:, p], f"case {i} {k} row {b}", ex[k][s][:, p],
+                assert_rounded16(got[k][s][:, p], rr[k][s][:, p], f"case {i} {k} row {b}", ex[k][s][:, p],
                               MANT[w.act])
         np.testing.assert_allclose(got["g_cache"][s][:, p], rr["g_cache"][s][:, p], rtol=1e-5)
     touched = {int(idx[b]) for b in live}
@@ -186,3 +186,157 @@ def test_random_kda(i):
         assert (out[skipped] == 7.0).all(), f"case {i}: a skipped token wrote its output"
     # the conv state holds raw inputs: bit for bit
     assert np.array_equal(to_np64(cs_d), cs_ref), f"case {i}: conv state differs"
+
+
+def _norm_kw(x, norm):
+    if norm == "none":
+        return {}, {}
+    return (dict(norm_gate=x["norm_gate"].to(DEV), norm_weight=x["norm_weight"].to(DEV), norm_act=norm),
+            dict(norm_gate=x["norm_gate"], norm_weight=x["norm_weight"],
+                 norm_act=O.ACT_SIGMOID if norm == "sigmoid" else O.ACT_SILU))
+
+
+@pytest.mark.parametrize("i", CASES[:12])
+def test_random_gdn_conv(i):
+    need_gpu()
+    rng = np.random.default_rng(4000 + i)
+    w, idx, norm = _draw(rng, 200 + i)
+    Wd = int(rng.integers(2, 9))
+    layout = str(rng.choice(["DS", "SD"]))
+    P, x = W.gdn_params(w), W.gdn_step_inputs(w, norm=norm != "none")
+    st, cv = W.gdn_state(w), W.gdn_conv(w, Wd, layout=layout, bias=bool(rng.random() < 0.5))
+    st_d, cs_d = st.to(DEV), cv["conv_state"].to(DEV)
+    out = torch.full((w.B, 1, w.HV, w.V), float("nan"), dtype=TD[w.out], device=DEV)
+    kw, okw = _norm_kw(x, norm)
+    cb = cv["conv_bias"]
+    S.gdn_decode_step_conv(x["qkv"].to(DEV), cv["conv_weight"].to(DEV), None if cb is None else cb.to(DEV), cs_d,
+                           x["a"].to(DEV), x["b"].to(DEV), P["A_log"].to(DEV), P["dt_bias"].to(DEV), st_d,
+                           idx.to(DEV), out, **kw)
+    ref, ref_cs = st.double().numpy().copy(), cv["conv_state"].double().numpy().copy()
+    ro = O.gdn_step_conv(x["qkv"], cv["conv_weight"], cb, ref_cs, x["a"], x["b"], P["A_log"], P["dt_bias"], ref, idx,
+                         H=w.H, HV=w.HV, K=w.K, V=w.V, **okw)
+    torch.cuda.synchronize()
+    live = [b for b in range(w.B) if 0 <= int(idx[b]) < w.num_slots]
+    _check(out.reshape(w.B, w.HV, w.V), ro, live, f"case {i} ({w.name}, W {Wd}, {layout}, norm {norm}) output")
+    got, got_cs = st_d.cpu(), cs_d.cpu()
+    named = {int(idx[b]) for b in live}
+    for s in range(w.num_slots):
+        if s in named:
+            assert_mixed(got[s], ref[s], FP32_TOL, f"case {i} slot {s}")
+        else:
+            assert torch.equal(got[s], st[s]), f"case {i}: slot {s} changed"
+    # the conv state holds raw inputs: bit for bit, touched and untouched slots alike
+    assert np.array_equal(to_np64(got_cs), ref_cs), f"case {i}: conv state differs"
+
+
+@pytest.mark.parametrize("i", CASES[:12])
+def test_random_gdn_state16(i):
+    need_gpu()
+    rng = np.random.default_rng(5000 + i)
+    w, idx, norm = _draw(rng, 300 + i)
+    sdt = torch.bfloat16 if rng.random() < 0.5 else torch.float16
+    P, x = W.gdn_params(w), W.gdn_step_inputs(w, norm=norm != "none")
+    st = W.gdn_state(w).to(sdt)
+    st_d = st.to(DEV)
+    out = torch.full((w.B, 1, w.HV, w.V), float("nan"), dtype=TD[w.out], device=DEV)
+    kw, okw = _norm_kw(x, norm)
+    S.gdn_decode_step_state16(x["qkv"].to(DEV), x["a"].to(DEV), x["b"].to(DEV), P["A_log"].to(DEV),
+                              P["dt_bias"].to(DEV), st_d, idx.to(DEV), out, **kw)
+    fmt = O.FMT_BF16 if sdt == torch.bfloat16 else O.FMT_F16
+    ref, exact = st.double().numpy().copy(), st.double().numpy().copy()
+    ro = O.gdn_step(x["qkv"], x["a"], x["b"], P["A_log"], P["dt_bias"], ref, idx, H=w.H, HV=w.HV, K=w.K, V=w.V,
+                    state_fmt=fmt, **okw)
+    O.gdn_step(x["qkv"], x["a"], x["b"], P["A_log"], P["dt_bias"], exact, idx, H=w.H, HV=w.HV, K=w.K, V=w.V,
+               state_fmt=O.FMT_NONE, **okw)
+    torch.cuda.synchronize()
+    live = [b for b in range(w.B) if 0 <= int(idx[b]) < w.num_slots]
+    _check(out.reshape(w.B, w.HV, w.V), ro, live, f"case {i} ({w.name}, {sdt}, norm {norm}) output")
+    got = st_d.cpu()
+    named = {int(idx[b]) for b in live}
+    for s in range(w.num_slots):
+        if s in named:
+            assert_rounded16(to_np64(got[s]), ref[s], f"case {i} slot {s}", exact[s],
+                             7 if sdt == torch.bfloat16 else 10)
+        else:
+            assert torch.equal(got[s], st[s]), f"case {i}: slot {s} changed"
+
+
+@pytest.mark.parametrize("i", CASES[:12])
+def test_random_gdn_multi(i):
+    need_gpu()
+    rng = np.random.default_rng(6000 + i)
+    w, idx, norm = _draw(rng, 400 + i)
+    T = int(rng.integers(1, 12))
+    lengths = torch.tensor([int(rng.integers(0, T + 1)) for _ in range(w.B)], dtype=torch.int32)
+    P = W.gdn_params(w)
+    g = W.generator(0, w.name, "rand_multi", T)
+    C = 2 * w.H * w.K + w.HV * w.V
+    qkv = W.normal((w.B, T, C), 1.0, w.act, g)
+    a = W.normal((w.B, T, w.HV), 0.5, w.act, g)
+    b = W.normal((w.B, T, w.HV), 1.0, w.act, g)
+    st = W.gdn_state(w)
+    st_d = st.to(DEV)
+    out = torch.full((w.B, T, w.HV, w.V), float("nan"), dtype=TD[w.out], device=DEV)
+    S.gdn_fused_recurrent(qkv.to(DEV), a.to(DEV), b.to(DEV), P["A_log"].to(DEV), P["dt_bias"].to(DEV), st_d,
+                          idx.to(DEV), out, lengths=lengths.to(DEV))
+    ref = st.double().numpy().copy()
+    ro = O.gdn_multi(qkv, a, b, P["A_log"], P["dt_bias"], ref, idx, H=w.H, HV=w.HV, K=w.K, V=w.V, lengths=lengths)
+    torch.cuda.synchronize()
+    for bi in range(w.B):
+        n = int(lengths[bi])
+        if not (0 <= int(idx[bi]) < w.num_slots) or n == 0:
+            continue
+        o, r = out[bi, :n], ro[bi, :n]
+        if o.dtype == torch.float32:
+            assert_mixed(o, r, CHAIN_TOL_T(n), f"case {i} ({w.name}, T {T}) row {bi} outputs")
+        else:
+            assert_16bit(o, r, CHAIN_TOL_T(n), f"case {i} ({w.name}, T {T}) row {bi} outputs")
+        assert torch.isnan(out[bi, n:].float()).all(), f"case {i}: outputs past row {bi}'s length written"
+    got = st_d.cpu()
+    for s in range(w.num_slots):
+        rows = [bi for bi in range(w.B) if int(idx[bi]) == s and int(lengths[bi]) > 0]
+        if rows:
+            assert_mixed(got[s], ref[s], CHAIN_TOL_T(int(lengths[rows[0]])), f"case {i} slot {s}")
+        else:
+            assert torch.equal(got[s], st[s]), f"case {i}: slot {s} changed"
+
+
+def CHAIN_TOL_T(n):
+    """Bar for outputs and states after n chained tokens: the single-step bar
+    for one token, the chained bar beyond."""
+    return FP32_TOL if n <= 1 else 2e-3
+
+
+@pytest.mark.parametrize("i", CASES[:12])
+def test_random_mamba_decode(i):
+    need_gpu()
+    rng = np.random.default_rng(7000 + i)
+    N = int(rng.choice([16, 32, 64, 128, 256]))
+    Dm = int(rng.choice([1, 7, 64, 100, 300, 1536]))
+    B = int(rng.integers(1, 9))
+    act = str(rng.choice(["f32", "bf16", "f16"]))
+    w = W.MambaWorkload(f"mamba_rand{i}_n{N}_d{Dm}_b{B}", B=B, Dm=Dm, N=N, num_slots=B + 2)
+    d = W.mamba_inputs(w, act=act)
+    use_D, use_z = bool(rng.random() < 0.5), bool(rng.random() < 0.5)
+    idx = d["idx"].clone() if "idx" in d else torch.arange(B, dtype=torch.int32)
+    for bi in range(B):
+        if rng.random() < 0.2:
+            idx[bi] = -1
+    h_d = d["h"].to(DEV)
+    out = torch.full((B, Dm), float("nan"), dtype=torch.float32, device=DEV)
+    S.mamba_decode_step(d["x"].to(DEV), d["dt"].to(DEV), d["A"].to(DEV), d["Bm"].to(DEV), d["Cm"].to(DEV),
+                        d["Dv"].to(DEV) if use_D else None, d["z"].to(DEV) if use_z else None, h_d, idx.to(DEV), out)
+    ref = d["h"].double().numpy().copy()
+    ro = O.mamba_step(d["x"], d["dt"], d["A"], d["Bm"], d["Cm"], d["Dv"] if use_D else None,
+                      d["z"] if use_z else None, ref, idx)
+    torch.cuda.synchronize()
+    live = [bi for bi in range(B) if 0 <= int(idx[bi]) < w.num_slots]
+    if live:
+        assert_mixed(out[live], ro[live], FP32_TOL, f"case {i} ({w.name}, {act}, D {use_D}, z {use_z}) output")
+    got = h_d.cpu()
+    named = {int(idx[bi]) for bi in live}
+    for s in range(w.num_slots):
+        if s in named:
+            assert_mixed(got[s], ref[s], FP32_TOL, f"case {i} slot {s}")
+        else:
+            assert torch.equal(got[s], d["h"][s]), f"case {i}: slot {s} changed"
