@@ -340,3 +340,105 @@ def test_random_mamba_decode(i):
             assert_mixed(got[s], ref[s], FP32_TOL, f"case {i} slot {s}")
         else:
             assert torch.equal(got[s], d["h"][s]), f"case {i}: slot {s} changed"
+
+
+def _tokens(w, T, seed_tag):
+    g = W.generator(0, w.name, seed_tag, T)
+    C = 2 * w.H * w.K + w.HV * w.V
+    return (W.normal((w.B, T, C), 1.0, w.act, g), W.normal((w.B, T, w.HV), 0.5, w.act, g),
+            W.normal((w.B, T, w.HV), 1.0, w.act, g), W.normal((w.B, T, w.HV, w.V), 1.0, w.act, g))
+
+
+@pytest.mark.parametrize("i", CASES[:12])
+def test_random_gdn_chunk_prefill(i):
+    need_gpu()
+    rng = np.random.default_rng(8000 + i)
+    K = int(rng.choice([64, 128]))
+    V = int(rng.choice([16, 48, 64, 128, 256]))
+    H, G = int(rng.integers(1, 3)), int(rng.choice([1, 2, 4]))
+    B = int(rng.integers(1, 5))
+    T = int(rng.choice([1, 7, 63, 64, 65, 130, 200]))
+    act, outd = str(rng.choice(["f32", "bf16", "f16"])), str(rng.choice(["f32", "bf16"]))
+    norm = str(rng.choice(["none", "silu", "sigmoid"]))
+    w = W.GDNWorkload(f"chunk_rand{i}_k{K}_v{V}_h{H}_g{G}_b{B}_t{T}_{act}", B=B, H=H, HV=G * H, K=K, V=V,
+                      num_slots=B + 2, act=act, out=outd, idx="perm")
+    idx = W.slot_indices(w).clone()
+    if B > 1 and rng.random() < 0.5:
+        idx[int(rng.integers(0, B))] = -1
+    lengths = torch.tensor([int(rng.choice([T, int(rng.integers(0, T + 1))])) for _ in range(B)], dtype=torch.int32)
+    P, st = W.gdn_params(w), W.gdn_state(w)
+    qkv, a, b, z = _tokens(w, T, "rand_chunk")
+    nw = torch.ones(V, dtype=torch.float32) * 0.75
+    st_d = st.to(DEV)
+    out = torch.full((B, T, w.HV, V), 7.0, dtype=TD[outd], device=DEV)
+    kw = dict(norm_gate=z.to(DEV), norm_weight=nw.to(DEV), norm_act=norm) if norm != "none" else {}
+    S.gdn_chunk_prefill(qkv.to(DEV), a.to(DEV), b.to(DEV), P["A_log"].to(DEV), P["dt_bias"].to(DEV), st_d,
+                        idx.to(DEV), out, lengths=lengths.to(DEV), **kw)
+    ref = st.double().numpy().copy()
+    okw = dict(norm_gate=z, norm_weight=nw, norm_act=O.ACT_SIGMOID if norm == "sigmoid" else O.ACT_SILU) \
+        if norm != "none" else {}
+    ro = O.gdn_multi(qkv, a, b, P["A_log"], P["dt_bias"], ref, idx, H=H, HV=w.HV, K=K, V=V, lengths=lengths, **okw)
+    torch.cuda.synchronize()
+    o = out.cpu()
+    for bi in range(B):
+        n = int(lengths[bi])
+        live = 0 <= int(idx[bi]) < w.num_slots
+        if live and n:
+            if o.dtype == torch.float32:
+                assert_mixed(o[bi, :n], ro[bi, :n], CHAIN_TOL_T(n), f"case {i} ({w.name}, norm {norm}) row {bi}")
+            else:
+                assert_16bit(o[bi, :n], ro[bi, :n], CHAIN_TOL_T(n), f"case {i} ({w.name}, norm {norm}) row {bi}")
+        assert (o[bi, n if live else 0:].float() == 7.0).all(), f"case {i}: row {bi} wrote past its length"
+    got = st_d.cpu()
+    for s in range(w.num_slots):
+        rows = [bi for bi in range(B) if int(idx[bi]) == s and int(lengths[bi]) > 0]
+        if rows:
+            assert_mixed(got[s], ref[s], CHAIN_TOL_T(int(lengths[rows[0]])), f"case {i} slot {s}")
+        else:
+            assert torch.equal(got[s], st[s]), f"case {i}: slot {s} changed"
+
+
+@pytest.mark.parametrize("i", CASES[:12])
+def test_random_mamba_scan(i):
+    need_gpu()
+    rng = np.random.default_rng(9000 + i)
+    N = int(rng.choice([16, 32, 64, 128, 256]))
+    Dm = int(rng.choice([7, 64, 100, 300, 1536]))
+    B = int(rng.integers(1, 5))
+    T = int(rng.choice([1, 5, 31, 64, 100, 257]))
+    act = str(rng.choice(["f32", "bf16", "f16"]))
+    w = W.MambaScanWorkload(f"scan_rand{i}_n{N}_d{Dm}_b{B}_t{T}_{act}", B=B, T=T, Dm=Dm, N=N, num_slots=B + 2)
+    d = W.mamba_scan_inputs(w, act=act)
+    lengths = torch.tensor([int(rng.choice([T, int(rng.integers(0, T + 1))])) for _ in range(B)], dtype=torch.int32)
+    idx = d["idx"].clone()
+    if B > 1 and rng.random() < 0.5:
+        idx[int(rng.integers(0, B))] = -1
+    use_D, use_z, zero = bool(rng.random() < 0.5), bool(rng.random() < 0.5), bool(rng.random() < 0.3)
+    ws_mode = str(rng.choice(["full", "none", "small"]))
+    nws = S.mamba_scan_workspace_bytes(B, T, Dm, N)
+    ws = None if ws_mode == "none" else torch.empty(max((nws if ws_mode == "full" else nws // 3) // 4, 1),
+                                                      device=DEV)
+    h_d = d["h"].to(DEV)
+    out = torch.full((B, T, Dm), 7.0, dtype=torch.float32, device=DEV)
+    S.mamba_scan(d["x"].to(DEV), d["dt"].to(DEV), d["A"].to(DEV), d["Bm"].to(DEV), d["Cm"].to(DEV),
+                 d["Dv"].to(DEV) if use_D else None, d["z"].to(DEV) if use_z else None, h_d, idx.to(DEV), out,
+                 lengths=lengths.to(DEV), zero_init=zero, workspace=ws)
+    ref = d["h"].double().numpy().copy()
+    ro = O.mamba_scan(d["x"], d["dt"], d["A"], d["Bm"], d["Cm"], d["Dv"] if use_D else None,
+                      d["z"] if use_z else None, ref, idx, lengths=lengths, zero_init=zero)
+    torch.cuda.synchronize()
+    o = out.cpu()
+    what = f"case {i} ({w.name}, ws {ws_mode}, D {use_D}, z {use_z}, zero {zero})"
+    for bi in range(B):
+        n = int(lengths[bi])
+        live = 0 <= int(idx[bi]) < w.num_slots
+        if live and n:
+            assert_mixed(o[bi, :n], ro[bi, :n], CHAIN_TOL_T(n), f"{what} row {bi}")
+        assert (o[bi, n if live else 0:] == 7.0).all(), f"{what}: row {bi} wrote past its length"
+    got = h_d.cpu()
+    for s in range(w.num_slots):
+        rows = [bi for bi in range(B) if int(idx[bi]) == s]
+        if rows:  # whatever the row's length, the pool must hold what the oracle's does
+            assert_mixed(got[s], ref[s], CHAIN_TOL_T(max(int(lengths[rows[0]]), 1)), f"{what} slot {s}")
+        else:
+            assert torch.equal(got[s], d["h"][s]), f"{what}: slot {s} changed"
