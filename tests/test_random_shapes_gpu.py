@@ -49,7 +49,7 @@ def _check(out, ref, live, what):
         assert_16bit(o, ref[live], FP32_TOL, what)
 
 
-CASES = list(range(24))
+CASES = list(range(48))
 
 
 @pytest.mark.parametrize("i", CASES)
@@ -142,7 +142,7 @@ def test_random_gdn_buffered(i):
         assert torch.equal(got_st[s], st[s]), f"case {i}: slot {s} changed"
 
 
-@pytest.mark.parametrize("i", CASES[:12])
+@pytest.mark.parametrize("i", CASES[:24])
 def test_random_kda(i):
     need_gpu()
     rng = np.random.default_rng(3000 + i)
@@ -196,7 +196,7 @@ def _norm_kw(x, norm):
                  norm_act=O.ACT_SIGMOID if norm == "sigmoid" else O.ACT_SILU))
 
 
-@pytest.mark.parametrize("i", CASES[:12])
+@pytest.mark.parametrize("i", CASES[:24])
 def test_random_gdn_conv(i):
     need_gpu()
     rng = np.random.default_rng(4000 + i)
@@ -229,7 +229,7 @@ def test_random_gdn_conv(i):
     assert np.array_equal(to_np64(got_cs), ref_cs), f"case {i}: conv state differs"
 
 
-@pytest.mark.parametrize("i", CASES[:12])
+@pytest.mark.parametrize("i", CASES[:24])
 def test_random_gdn_state16(i):
     need_gpu()
     rng = np.random.default_rng(5000 + i)
@@ -261,7 +261,7 @@ def test_random_gdn_state16(i):
             assert torch.equal(got[s], st[s]), f"case {i}: slot {s} changed"
 
 
-@pytest.mark.parametrize("i", CASES[:12])
+@pytest.mark.parametrize("i", CASES[:24])
 def test_random_gdn_multi(i):
     need_gpu()
     rng = np.random.default_rng(6000 + i)
@@ -307,7 +307,7 @@ def CHAIN_TOL_T(n):
     return FP32_TOL if n <= 1 else 2e-3
 
 
-@pytest.mark.parametrize("i", CASES[:12])
+@pytest.mark.parametrize("i", CASES[:24])
 def test_random_mamba_decode(i):
     need_gpu()
     rng = np.random.default_rng(7000 + i)
@@ -349,7 +349,7 @@ def _tokens(w, T, seed_tag):
             W.normal((w.B, T, w.HV), 1.0, w.act, g), W.normal((w.B, T, w.HV, w.V), 1.0, w.act, g))
 
 
-@pytest.mark.parametrize("i", CASES[:12])
+@pytest.mark.parametrize("i", CASES[:24])
 def test_random_gdn_chunk_prefill(i):
     need_gpu()
     rng = np.random.default_rng(8000 + i)
@@ -398,7 +398,7 @@ def test_random_gdn_chunk_prefill(i):
             assert torch.equal(got[s], st[s]), f"case {i}: slot {s} changed"
 
 
-@pytest.mark.parametrize("i", CASES[:12])
+@pytest.mark.parametrize("i", CASES[:24])
 def test_random_mamba_scan(i):
     need_gpu()
     rng = np.random.default_rng(9000 + i)
