@@ -1,7 +1,9 @@
 """GPU tests of the two helper entry points: ssmd_check_slot_indices, the
 debug check that no two active rows of a call name one slot (the decode
 steps' precondition; expected counts come from a plain host count over the
-same vector), and the stream copy behind the benchmark's copy ceiling."""
+same vector), and the stream copy behind the benchmark's copy ceiling; and
+calls on two streams at once (the library keeps no device state between
+calls)."""
 import numpy as np
 import pytest
 import torch
@@ -75,3 +77,44 @@ def test_stream_copy_is_bit_exact():
     S.ssmd_stream_copy(src, dst)
     torch.cuda.synchronize()
     assert torch.equal(src.view(torch.int32), dst.view(torch.int32))
+
+
+def test_two_streams_interleaved_calls():
+    """Two independent workloads enqueued alternately on two streams (default
+    priority) for several steps: each matches its own oracle run, so calls
+    share no device state and take the stream they are given."""
+    import oracle as O
+    from tests._helpers import CHAIN_TOL, assert_mixed
+    need_gpu()
+    ws = [W.GDNWorkload(f"two_streams_{j}", B=6 + 4 * j, H=2, HV=4, K=128, V=64 + 64 * j, num_slots=12 + 4 * j,
+                        out="f32", idx="perm") for j in range(2)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    setups = []
+    for w in ws:
+        P, idx, st = W.gdn_params(w), W.slot_indices(w), W.gdn_state(w)
+        setups.append({"w": w, "P": P, "Pd": {k: v.to(DEV) for k, v in P.items()}, "idx": idx, "idx_d": idx.to(DEV),
+                       "st_d": st.to(DEV), "ref": st.double().numpy().copy(),
+                       "out": torch.empty(w.B, 1, w.HV, w.V, device=DEV)})
+    torch.cuda.synchronize()
+    steps = 6
+    xs = [[W.gdn_step_inputs(s["w"], 100 + t) for t in range(steps)] for s in setups]
+    xd = [[{k: v.to(DEV) for k, v in x.items()} for x in xl] for xl in xs]
+    torch.cuda.synchronize()
+    for t in range(steps):
+        for j, s in enumerate(setups):
+            with torch.cuda.stream(streams[j]):
+                x = xd[j][t]
+                S.gdn_decode_step(x["qkv"], x["a"], x["b"], s["Pd"]["A_log"], s["Pd"]["dt_bias"], s["st_d"],
+                                  s["idx_d"], s["out"], stream=streams[j])
+    torch.cuda.synchronize()
+    for j, s in enumerate(setups):
+        w = s["w"]
+        for t in range(steps):
+            x = xs[j][t]
+            ro = O.gdn_step(x["qkv"], x["a"], x["b"], s["P"]["A_log"], s["P"]["dt_bias"], s["ref"], s["idx"],
+                            H=w.H, HV=w.HV, K=w.K, V=w.V)
+        assert_mixed(s["out"].reshape(w.B, w.HV, w.V), ro, CHAIN_TOL, f"workload {j}: last output")
+        named = set(s["idx"].tolist())
+        got = s["st_d"].cpu()
+        for sl in named:
+            assert_mixed(got[sl], s["ref"][sl], CHAIN_TOL, f"workload {j}: slot {sl}")
