@@ -281,3 +281,28 @@ def test_binding_rejects_tensors_on_several_devices():
     with pytest.raises(ValueError, match="several devices"):
         S.ssmd_check_slot_indices(torch.zeros(4, dtype=torch.int32), 4,
                                   dup_count=torch.empty(1, dtype=torch.int32, device="meta"))
+
+
+def test_product_path_is_independent_of_the_oracle():
+    """The package imports nothing from oracle/ (in a fresh interpreter, after
+    importing it and loading the library, no oracle module is loaded), none of
+    its sources names it, and a missing library fails loudly instead of
+    falling back to anything."""
+    import subprocess
+    import sys
+    code = ("import sys, ssm_recurrent_decode_gated_amd as S; S.load_library(); "
+            "print(sorted(m for m in sys.modules if m == 'oracle' or m.startswith('oracle.')))")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip().splitlines()[-1] == "[]", r.stdout
+    pkg = os.path.join(ROOT, "ssm_recurrent_decode_gated_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "liboracle" not in text, f
+    code = ("import ssm_recurrent_decode_gated_amd._binding as B; B.LIB_PATH = '/nonexistent/libssmdec.so'; "
+            "B._LIB = None\ntry:\n    B.load_library()\nexcept RuntimeError as e:\n    print('raised', e)")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert "raised" in r.stdout and "no non-HIP fallback" in r.stdout, r.stdout + r.stderr
