@@ -668,7 +668,7 @@ def summarize_counters(fetch_dir, write_dir, out, command, which="gdn"):
                + 2 * T * wl.B * wl.HV * 2 + T * wl.B * wl.HV * wl.V * 2 + 2 * wl.HV * 4 + wl.B * 4)
         title = f"# rocprofv3 HBM counters, {kernel} at B=256 of 264 slots x {T} tokens (H=16 HV=32 K=V=128, bf16)"
     elif which == "conv":
-        kernel, wl = "gdn_conv_decode_kernel", W.GDN_B256
+        kernel, wl = "gdn_conv_pf_kernel", W.GDN_B256
         alg = gdn_conv_alg_bytes(wl, 4)
         title = f"# rocprofv3 HBM counters, {kernel} at B=256 of 264 slots (H=16 HV=32 K=V=128, bf16 act, conv width 4)"
     elif which == "buffered":

@@ -284,8 +284,17 @@ hipError_t launch_gc_norm(const GdnConvParams& cp, hipStream_t st) {
 
 // One block of GCONV_THREADS threads per (batch row, q/k head). The host has
 // checked G <= GCONV_GMAX and G V <= GCONV_OMAX (so 2K + G V <= GCONV_YMAX).
-hipError_t launch_gdn_conv(const GdnConvParams& cp, const Launch& l, hipStream_t st) {
-  (void)l;
+// Shapes the persistent kernel covers (width 4, no output norm, G V = 256 at
+// K = 64 or 128) take it, one block per CU or per group if there are fewer
+// (measured at H = 16, HV = 32, K = V = 128: B = 8 / 16 / 64 / 256 in 9.0 /
+// 13.2 / 53.3 / 202.4 us against 10.7 / 14.1 / 56.3 / 207.1 with this
+// kernel); a fixed launch shape with a grid cap forces it with that many
+// blocks, one without forces this kernel.
+hipError_t launch_gdn_conv(const GdnConvParams& cp, const Launch& l, int n_cu, hipStream_t st) {
+  if (gdn_conv_pf_fits(cp)) {
+    if (l.fixed && l.grid_cap > 0) return launch_gdn_conv_pf(cp, l.grid_cap, st);
+    if (!l.fixed) return launch_gdn_conv_pf(cp, n_cu, st);
+  }
   switch (cp.g.K) {
     case 16: return launch_gc_norm<16>(cp, st);
     case 32: return launch_gc_norm<32>(cp, st);

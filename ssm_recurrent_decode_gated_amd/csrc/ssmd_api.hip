@@ -307,7 +307,9 @@ int gdn_decode_step_conv(const void* x, int64_t x_row_stride, const float* conv_
   cp.cs_chan = cs_chan_stride;
   cp.cs_tap = cs_tap_stride;
   cp.W = W;
-  return launch_status(ssmd::launch_gdn_conv(cp, launch_for(), stream), fn);
+  int n_cu = 0;
+  if (int rc2 = cu_count(&n_cu)) return rc2;
+  return launch_status(ssmd::launch_gdn_conv(cp, launch_for(), n_cu, stream), fn);
 }
 
 int gdn_fused_recurrent(const void* mixed_qkv, int64_t qkv_row_stride, const void* a, const void* b,

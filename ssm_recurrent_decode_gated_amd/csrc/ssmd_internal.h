@@ -154,7 +154,11 @@ hipError_t launch_kda(const KdaParams& p, const Launch& l, hipStream_t s);
 // and dt_bias); kda_pf_supported says whether a call qualifies.
 bool kda_pf_supported(const KdaParams& p);
 hipError_t launch_kda_pf(const KdaParams& p, const Launch& l, int n_cu, hipStream_t s);
-hipError_t launch_gdn_conv(const GdnConvParams& p, const Launch& l, hipStream_t s);
+hipError_t launch_gdn_conv(const GdnConvParams& p, const Launch& l, int n_cu, hipStream_t s);
+// Persistent conv-fused step: whether it covers the shape, and its launch with
+// the given number of blocks (each walking groups with a grid stride).
+bool gdn_conv_pf_fits(const GdnConvParams& p);
+hipError_t launch_gdn_conv_pf(const GdnConvParams& p, int64_t blocks, hipStream_t s);
 hipError_t launch_gdn_multi(const GdnMultiParams& p, const Launch& l, int n_cu, hipStream_t s);
 hipError_t launch_gdn_chunk(const GdnChunkParams& p, int n_cu, hipStream_t s);
 int64_t gdn_chunk_workspace_floats(int B, int T, int HV, int K, int V, bool norm);

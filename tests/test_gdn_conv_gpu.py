@@ -181,3 +181,66 @@ def test_gdn_conv_equals_conv_then_packed_step():
     np.testing.assert_array_equal(cs_d.cpu().double().numpy(), cs_ref)
     assert_mixed(out_f.cpu(), out_u.cpu().double().numpy(), FP32_TOL, "fused vs unfused output")
     assert_mixed(st_a.cpu(), st_b.cpu().double().numpy(), FP32_TOL, "fused vs unfused state")
+
+
+# Shapes the persistent kernel takes (conv width 4, no output norm, G V = 256 at
+# K = 64 or 128, at least two (row, q/k head) groups per CU): the grid walks the
+# groups with a stride, so these counts leave a ragged last walk, and padded
+# rows, which the walk must skip while keeping its barriers, sit among them.
+PF_CASES = [
+    # name, B, H, HV, K, V, slots, act, out, layout, bias, pad every, row pad
+    ("k128_b264_h2_bf16_pad7", 264, 2, 4, 128, 128, 270, "bf16", "bf16", "DS", True, 7, 0),
+    ("k128_b300_h2_f32_sd", 300, 2, 4, 128, 128, 301, "f32", "f32", "SD", False, 0, 16),
+    ("k64_b280_h2_gqa4_v64_f16", 280, 2, 8, 64, 64, 290, "f16", "f32", "DS", True, 5, 0),
+    ("k128_b520_h1_pad3_f16_out", 520, 1, 2, 128, 128, 530, "bf16", "f16", "SD", True, 3, 0),
+]
+
+
+@pytest.mark.parametrize("case", PF_CASES, ids=[c[0] for c in PF_CASES])
+def test_gdn_conv_persistent_walk(case):
+    """The persistent conv-fused kernel against the oracle element by element:
+    outputs, states, the rolled conv state bit for bit, and padded rows and
+    unnamed slots left untouched."""
+    need_gpu()
+    name, B, H, HV, K, V, slots, act, outd, layout, bias, pad_every, row_pad = case
+    w = W.GDNWorkload("gdn_conv_pf_" + name, B=B, H=H, HV=HV, K=K, V=V, num_slots=slots, act=act, out=outd,
+                      idx="perm")
+    P, idx, cv, st, cs_d = _setup(w, 4, layout, bias)
+    if pad_every:
+        idx[::pad_every] = -1
+    x = W.gdn_step_inputs(w)
+    st_d = st.to(DEV)
+    out = _gpu(w, st_d, cs_d, idx, x, P, cv, outd, sentinel=7.0, row_pad=row_pad)
+    ref, ref_cs = st.double().numpy().copy(), cv["conv_state"].double().numpy().copy()
+    ro = _oracle(w, ref, ref_cs, idx, x, P, cv)
+    act_rows = [b for b in range(B) if idx[b] >= 0]
+    pad_rows = [b for b in range(B) if idx[b] < 0]
+    _check_out(out[act_rows], ro[act_rows], "output")
+    if pad_rows:
+        assert (out[pad_rows].float().cpu() == 7.0).all(), "padded row output written"
+    got, got_cs = st_d.cpu(), cs_d.cpu()
+    np.testing.assert_array_equal(got_cs.double().numpy(), ref_cs)
+    named = set(idx[idx >= 0].tolist())
+    assert_mixed(got[sorted(named)], ref[sorted(named)], FP32_TOL, "state")
+    for s in range(slots):
+        if s not in named:
+            assert torch.equal(got[s], st[s]), f"unnamed slot {s} changed"
+            assert torch.equal(got_cs[s], cv["conv_state"][s]), f"unnamed slot {s}: conv state changed"
+
+
+def test_gdn_conv_persistent_chain_8_steps():
+    """Eight chained steps on the persistent kernel (512 groups): conv window
+    and state carry over from step to step."""
+    need_gpu()
+    w = W.GDNWorkload("gdn_conv_pf_chain", B=256, H=2, HV=4, K=128, V=128, num_slots=260, idx="perm", out="f32")
+    P, idx, cv, st, cs_d = _setup(w)
+    st_d = st.to(DEV)
+    ref, ref_cs = st.double().numpy().copy(), cv["conv_state"].double().numpy().copy()
+    for t in range(8):
+        x = W.gdn_step_inputs(w, t)
+        out = _gpu(w, st_d, cs_d, idx, x, P, cv, "f32")
+        ro = _oracle(w, ref, ref_cs, idx, x, P, cv)
+        assert_mixed(out.reshape(w.B, w.HV, w.V), ro, CHAIN_TOL, f"step {t} output")
+    np.testing.assert_array_equal(cs_d.cpu().double().numpy(), ref_cs)
+    named = idx.tolist()
+    assert_mixed(st_d.cpu()[named], ref[named], CHAIN_TOL, "state after 8 steps")
