@@ -284,16 +284,22 @@ hipError_t launch_gc_norm(const GdnConvParams& cp, hipStream_t st) {
 
 // One block of GCONV_THREADS threads per (batch row, q/k head). The host has
 // checked G <= GCONV_GMAX and G V <= GCONV_OMAX (so 2K + G V <= GCONV_YMAX).
-// Shapes the persistent kernel covers (width 4, no output norm, G V = 256 at
-// K = 64 or 128) take it, one block per CU or per group if there are fewer
-// (measured at H = 16, HV = 32, K = V = 128: B = 8 / 16 / 64 / 256 in 9.0 /
-// 13.2 / 53.3 / 202.4 us against 10.7 / 14.1 / 56.3 / 207.1 with this
-// kernel); a fixed launch shape with a grid cap forces it with that many
-// blocks, one without forces this kernel.
+// Shapes the 8-wave kernel of gdn_conv_decode_pf.hip covers (width 4, no
+// output norm, G V = 256 at K = 64 or 128) take it: with fewer than four
+// groups per CU one block per CU walks them (or one per group if there are
+// fewer groups than CUs), from four up one block per group. Measured at
+// H = 16, HV = 32, K = V = 128: B = 8 / 16 / 32 / 64 / 256 in 9.0 / 13.2 /
+// 25.6 / 52.3 / 200.1 us, against 10.7 / 14.1 / 27.1 / 56.3 / 207.1 with this
+// kernel; walking at B = 64 / 256 took 53.3 / 202.7 us, one block per group
+// at B = 32 (two per CU) 27.4. A fixed launch shape with a grid cap forces
+// the 8-wave kernel with that many blocks, one without forces this kernel.
 hipError_t launch_gdn_conv(const GdnConvParams& cp, const Launch& l, int n_cu, hipStream_t st) {
   if (gdn_conv_pf_fits(cp)) {
     if (l.fixed && l.grid_cap > 0) return launch_gdn_conv_pf(cp, l.grid_cap, st);
-    if (!l.fixed) return launch_gdn_conv_pf(cp, n_cu, st);
+    if (!l.fixed) {
+      const int64_t groups = (int64_t)cp.g.B * cp.g.H;
+      return launch_gdn_conv_pf(cp, groups >= 4LL * n_cu ? groups : (int64_t)n_cu, st);
+    }
   }
   switch (cp.g.K) {
     case 16: return launch_gc_norm<16>(cp, st);

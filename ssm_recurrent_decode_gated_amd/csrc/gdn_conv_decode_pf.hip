@@ -1,8 +1,8 @@
 // gdn_conv_decode_pf.hip -- conv-fused GDN decode step, persistent form:
-// one 8-wave block per CU walks the (batch row, q/k head) groups with a grid
-// stride and, while one group's conv and state rows are computed and stored,
-// holds the next group's state rows, conv windows, conv weights and gates in
-// flight. Same arithmetic, row layout and conv-state roll as
+// 8-wave blocks walk the (batch row, q/k head) groups with a grid stride and,
+// while one group's conv and state rows are computed and stored, hold the
+// next group's state rows, conv windows, conv weights and gates in flight
+// (the launcher picks one block per CU or, for many groups, one per group). Same arithmetic, row layout and conv-state roll as
 // gdn_conv_decode.hip, which handles every shape this kernel does not.
 //
 // The group is still the unit of work (its conv state is rolled in place by

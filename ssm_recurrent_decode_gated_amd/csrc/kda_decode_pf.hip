@@ -1,14 +1,15 @@
 // kda_decode_pf.hip -- the fused KDA decode op (conv1d update + SiLU, KDA
-// delta rule, sigmoid-gated RMSNorm) as persistent blocks that prefetch the
-// next (token, head) unit while computing the current one: the structure of
-// gdn_decode_pf.hip applied to kda_decode.hip, for the common shapes (head
+// delta rule, sigmoid-gated RMSNorm) as blocks that, when they walk several
+// (token, head) units, prefetch the next one while computing the current
+// one: the structure of gdn_decode_pf.hip applied to kda_decode.hip, for the common shapes (head
 // size 64 or 128, conv width 4).
 //
 // Same computation as kda_decode_kernel ("Microbenchmark for the fused
 // Kimi-K3 KDA decode kernel on ROCm": module docstring, `triton_chain`,
 // `_gated_rmsnorm`, `Inputs`; "Optimization Log: Qwen3.5-27B Dense on B200",
-// "Kernel 4: Fused DeltaNet Recurrent", Math). One block of 4 waves per CU
-// walks (token, head) units with a grid stride: each wave holds D/4 state
+// "Kernel 4: Fused DeltaNet Recurrent", Math). Blocks of 4 waves walk
+// (token, head) units with a grid stride (by default the grid has one block
+// per unit, which measured faster; see the launcher): each wave holds D/4 state
 // rows, each thread up to two conv channels (window, weights, bias) and one
 // gate column and output row. Everything a unit needs from HBM is fetched
 // one unit ahead (activation values kept raw until used), so the compute of
@@ -257,31 +258,38 @@ __global__ __launch_bounds__(64 * KPF_WAVES) void kda_decode_pf_kernel(KdaParams
 
 namespace {
 
+// One block per (token, head) unit unless a grid cap is given (launch-shape
+// sweeps; the blocks then walk the units with a grid stride). Measured at
+// T = 64, D = 128, conv width 4, gated norm: 12 / 24 / 48 / 96 heads in
+// 20.5 / 37.4 / 71.6 / 143.6 us, against 22.1 / 41.5 / 77.4 / 151.4 with one
+// block per CU walking the units: several resident blocks per CU, each with
+// all its loads issued at once, keep more bytes in flight than one walking
+// block's one-unit-ahead prefetch.
 template <int D, bool NORM, int ACT, bool GP>
-hipError_t launch_kpf(const KdaParams& p, int n_cu, hipStream_t st) {
+hipError_t launch_kpf(const KdaParams& p, int cap, hipStream_t st) {
   const int64_t units = (int64_t)p.T * p.H;
-  const int64_t blocks = units < n_cu ? units : n_cu;  // one 4-wave block per CU
+  const int64_t blocks = cap > 0 && units > cap ? cap : units;
   kda_decode_pf_kernel<D, NORM, ACT, GP><<<dim3((unsigned)blocks), dim3(64 * KPF_WAVES), 0, st>>>(p, (int)units);
   return hipGetLastError();
 }
 
 template <int D, bool NORM, int ACT>
-hipError_t launch_kpf_gp(const KdaParams& p, int n_cu, hipStream_t st) {
-  return p.A_log || p.dt_bias ? launch_kpf<D, NORM, ACT, true>(p, n_cu, st) : launch_kpf<D, NORM, ACT, false>(p, n_cu, st);
+hipError_t launch_kpf_gp(const KdaParams& p, int cap, hipStream_t st) {
+  return p.A_log || p.dt_bias ? launch_kpf<D, NORM, ACT, true>(p, cap, st) : launch_kpf<D, NORM, ACT, false>(p, cap, st);
 }
 
 template <int D, bool NORM>
-hipError_t launch_kpf_act(const KdaParams& p, int n_cu, hipStream_t st) {
+hipError_t launch_kpf_act(const KdaParams& p, int cap, hipStream_t st) {
   switch (p.act_dt) {
-    case SSMD_F32: return launch_kpf_gp<D, NORM, SSMD_F32>(p, n_cu, st);
-    case SSMD_BF16: return launch_kpf_gp<D, NORM, SSMD_BF16>(p, n_cu, st);
-    default: return launch_kpf_gp<D, NORM, SSMD_F16>(p, n_cu, st);
+    case SSMD_F32: return launch_kpf_gp<D, NORM, SSMD_F32>(p, cap, st);
+    case SSMD_BF16: return launch_kpf_gp<D, NORM, SSMD_BF16>(p, cap, st);
+    default: return launch_kpf_gp<D, NORM, SSMD_F16>(p, cap, st);
   }
 }
 
 template <int D>
-hipError_t launch_kpf_norm(const KdaParams& p, int n_cu, hipStream_t st) {
-  return p.gate ? launch_kpf_act<D, true>(p, n_cu, st) : launch_kpf_act<D, false>(p, n_cu, st);
+hipError_t launch_kpf_norm(const KdaParams& p, int cap, hipStream_t st) {
+  return p.gate ? launch_kpf_act<D, true>(p, cap, st) : launch_kpf_act<D, false>(p, cap, st);
 }
 
 }  // namespace
@@ -290,11 +298,11 @@ bool kda_pf_supported(const KdaParams& p) {
   return (p.D == 64 || p.D == 128) && p.W == 4 && (p.A_log != nullptr) == (p.dt_bias != nullptr);
 }
 
-hipError_t launch_kda_pf(const KdaParams& p, const Launch& l, int n_cu, hipStream_t st) {
-  if (l.grid_cap > 0) n_cu = l.grid_cap;  // launch-shape sweeps
+hipError_t launch_kda_pf(const KdaParams& p, const Launch& l, hipStream_t st) {
+  const int cap = l.grid_cap;  // > 0 only for launch-shape sweeps
   switch (p.D) {
-    case 64: return launch_kpf_norm<64>(p, n_cu, st);
-    case 128: return launch_kpf_norm<128>(p, n_cu, st);
+    case 64: return launch_kpf_norm<64>(p, cap, st);
+    case 128: return launch_kpf_norm<128>(p, cap, st);
     default: return hipErrorInvalidValue;
   }
 }

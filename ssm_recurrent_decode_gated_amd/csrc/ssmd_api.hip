@@ -440,11 +440,8 @@ int kda_decode_step(const void* x, const float* conv_weight, const float* conv_b
   p.scale = scale;
   p.use_l2 = use_qk_l2norm ? 1 : 0;
   p.l2eps = l2norm_eps;
-  if (ssmd::kda_pf_supported(p) && aligned(conv_weight, 16) && (!dt_bias || aligned(dt_bias, 16))) {
-    int n_cu = 0;
-    if (int rc = cu_count(&n_cu)) return rc;
-    return launch_status(ssmd::launch_kda_pf(p, launch_for(), n_cu, stream), fn);
-  }
+  if (ssmd::kda_pf_supported(p) && aligned(conv_weight, 16) && (!dt_bias || aligned(dt_bias, 16)))
+    return launch_status(ssmd::launch_kda_pf(p, launch_for(), stream), fn);
   return launch_status(ssmd::launch_kda(p, launch_for(), stream), fn);
 }
 

@@ -153,7 +153,7 @@ hipError_t launch_kda(const KdaParams& p, const Launch& l, hipStream_t s);
 // 4, A_log and dt_bias both given or both NULL (16-byte aligned conv weights
 // and dt_bias); kda_pf_supported says whether a call qualifies.
 bool kda_pf_supported(const KdaParams& p);
-hipError_t launch_kda_pf(const KdaParams& p, const Launch& l, int n_cu, hipStream_t s);
+hipError_t launch_kda_pf(const KdaParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_gdn_conv(const GdnConvParams& p, const Launch& l, int n_cu, hipStream_t s);
 // Persistent conv-fused step: whether it covers the shape, and its launch with
 // the given number of blocks (each walking groups with a grid stride).
