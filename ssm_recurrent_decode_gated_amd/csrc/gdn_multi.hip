@@ -306,7 +306,7 @@ hipError_t launch_gm_k(GdnMultiParams mp, int wpb, hipStream_t st) {
 // to 8. Without the norm, row groups drop to one per wave when the plain
 // depth would give fewer than two blocks per CU.
 template <int K, bool NORM, int ACT>
-hipError_t launch_gm_shape(const GdnMultiParams& mp, int n_cu, hipStream_t st) {
+hipError_t launch_gm_shape(const GdnMultiParams& mp, const Launch& l, int n_cu, hipStream_t st) {
   const GdnParams& p = mp.g;
   if constexpr (NORM) {
     constexpr int RG = gmulti_rg_norm<K>();
@@ -317,23 +317,24 @@ hipError_t launch_gm_shape(const GdnMultiParams& mp, int n_cu, hipStream_t st) {
     constexpr int RG = gmulti_rg_plain<K>();
     const int rows = 4 * RG * RowLayout<K>::RPI;
     const int64_t blocks = (int64_t)p.B * p.HV * ((p.V + rows - 1) / rows);
+    if (l.fixed) return launch_gm_k<K, false, ACT, RG>(mp, l.wpb, st);  // launch-shape sweeps
     if (RG == 1 || blocks >= 2LL * n_cu) return launch_gm_k<K, false, ACT, RG>(mp, 4, st);
     return launch_gm_k<K, false, ACT, 1>(mp, 4, st);
   }
 }
 
 template <int K, bool NORM>
-hipError_t launch_gm_act(const GdnMultiParams& mp, int n_cu, hipStream_t st) {
+hipError_t launch_gm_act(const GdnMultiParams& mp, const Launch& l, int n_cu, hipStream_t st) {
   switch (mp.g.act_dt) {
-    case SSMD_F32: return launch_gm_shape<K, NORM, SSMD_F32>(mp, n_cu, st);
-    case SSMD_BF16: return launch_gm_shape<K, NORM, SSMD_BF16>(mp, n_cu, st);
-    default: return launch_gm_shape<K, NORM, SSMD_F16>(mp, n_cu, st);
+    case SSMD_F32: return launch_gm_shape<K, NORM, SSMD_F32>(mp, l, n_cu, st);
+    case SSMD_BF16: return launch_gm_shape<K, NORM, SSMD_BF16>(mp, l, n_cu, st);
+    default: return launch_gm_shape<K, NORM, SSMD_F16>(mp, l, n_cu, st);
   }
 }
 
 template <int K>
-hipError_t launch_gm_norm(const GdnMultiParams& mp, int n_cu, hipStream_t st) {
-  return mp.g.norm_gate ? launch_gm_act<K, true>(mp, n_cu, st) : launch_gm_act<K, false>(mp, n_cu, st);
+hipError_t launch_gm_norm(const GdnMultiParams& mp, const Launch& l, int n_cu, hipStream_t st) {
+  return mp.g.norm_gate ? launch_gm_act<K, true>(mp, l, n_cu, st) : launch_gm_act<K, false>(mp, l, n_cu, st);
 }
 
 }  // namespace
@@ -349,13 +350,12 @@ int gdn_multi_max_norm_rows(int K) {
 }
 
 hipError_t launch_gdn_multi(const GdnMultiParams& mp, const Launch& l, int n_cu, hipStream_t st) {
-  (void)l;
   switch (mp.g.K) {
-    case 16: return launch_gm_norm<16>(mp, n_cu, st);
-    case 32: return launch_gm_norm<32>(mp, n_cu, st);
-    case 64: return launch_gm_norm<64>(mp, n_cu, st);
-    case 128: return launch_gm_norm<128>(mp, n_cu, st);
-    case 256: return launch_gm_norm<256>(mp, n_cu, st);
+    case 16: return launch_gm_norm<16>(mp, l, n_cu, st);
+    case 32: return launch_gm_norm<32>(mp, l, n_cu, st);
+    case 64: return launch_gm_norm<64>(mp, l, n_cu, st);
+    case 128: return launch_gm_norm<128>(mp, l, n_cu, st);
+    case 256: return launch_gm_norm<256>(mp, l, n_cu, st);
     default: return hipErrorInvalidValue;
   }
 }
