@@ -90,6 +90,8 @@ __global__ __launch_bounds__(512) void gdn_multi_kernel(GdnMultiParams mp) {
   // Each region is read from a block-uniform base with 32-bit element
   // offsets, so a pending load holds one offset register, not a 64-bit
   // address (the host keeps T * row stride below 2^31 elements).
+  // Counts per thread for a block of 256 threads: every launch of this
+  // kernel uses 4 to 8 waves, so one pass of these covers the chunk.
   constexpr int SQK = (TC * 2 * K + 255) / 256;  // q and k values per thread
   constexpr int SV = (TC * R4 + 255) / 256;      // v (and norm gate) values per thread
   E rq[SQK], rv[SV], rz[NORM ? SV : 1], rab;
@@ -317,7 +319,9 @@ hipError_t launch_gm_shape(const GdnMultiParams& mp, const Launch& l, int n_cu, 
     constexpr int RG = gmulti_rg_plain<K>();
     const int rows = 4 * RG * RowLayout<K>::RPI;
     const int64_t blocks = (int64_t)p.B * p.HV * ((p.V + rows - 1) / rows);
-    if (l.fixed) return launch_gm_k<K, false, ACT, RG>(mp, l.wpb, st);  // launch-shape sweeps
+    // launch-shape sweeps: the staging above spreads a chunk's q, k and v
+    // over at least 256 threads, so a fixed shape takes 4 to 8 waves
+    if (l.fixed) return launch_gm_k<K, false, ACT, RG>(mp, min(max(l.wpb, 4), 8), st);
     if (RG == 1 || blocks >= 2LL * n_cu) return launch_gm_k<K, false, ACT, RG>(mp, 4, st);
     return launch_gm_k<K, false, ACT, 1>(mp, 4, st);
   }

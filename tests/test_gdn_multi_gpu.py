@@ -1,16 +1,19 @@
 """GPU parity of gdn_fused_recurrent (the GDN step over T tokens per row,
 state held in registers) against the fp64 oracle's token-by-token steps:
 outputs and final states to the fp32 tolerance (chained tolerance over long
-token runs), 16-bit outputs to one ulp, ragged lengths and padding touching
+token runs), 16-bit outputs to the RNE of the exact value, ragged lengths and padding touching
 nothing, and T = 1 equal to the packed step."""
-import numpy as np
+import os
+import subprocess
+import sys
+
 import pytest
 import torch
 
 import oracle as O
 import ssm_recurrent_decode_gated_amd as S
 import workloads as W
-from tests._helpers import CHAIN_TOL, FP32_TOL, assert_16bit, assert_mixed, need_gpu
+from tests._helpers import CHAIN_TOL, FP32_TOL, assert_out16, assert_mixed, need_gpu
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -51,7 +54,7 @@ def _check_out(out, ro, tol, what):
     if out.dtype == torch.float32:
         assert_mixed(out.cpu(), ro, tol, what)
     else:
-        assert_16bit(out, ro, tol, what)
+        assert_out16(out, ro, tol, what)
 
 
 def test_gdn_multi_b256_of_264_four_tokens():
@@ -163,3 +166,32 @@ def test_gdn_multi_256_tokens_and_split():
     torch.cuda.synchronize()
     assert_mixed(torch.cat(halves, dim=1).cpu(), out.cpu().double().numpy(), FP32_TOL, "two calls vs one")
     assert_mixed(st2.cpu(), got.double().numpy(), FP32_TOL, "state, two calls vs one")
+
+
+def _fixed_shape_child():
+    """Body of the test below, run in a child process whose SSMD_TUNE asks
+    for a fixed 2-wave launch shape: T = 8 and T = 20 tokens (one and three
+    staging chunks, the last one partial) against the oracle."""
+    w = W.GDNWorkload("multi_fixed_shape", B=3, H=2, HV=4, K=128, V=128, num_slots=5, idx="perm")
+    P, idx, st = W.gdn_params(w), W.slot_indices(w), W.gdn_state(w)
+    named = sorted(set(idx.tolist()))
+    for T in (8, 20):
+        d = _inputs(w, T, seed=T)
+        out, got, ro, ref = _run(w, T, d, P, st, idx, out_dtype="f32")
+        _check_out(out, ro, CHAIN_TOL, f"T={T} outputs")
+        assert_mixed(got[named], ref[named], CHAIN_TOL, f"T={T} states")
+    print("FIXED_SHAPE_OK", flush=True)
+
+
+def test_gdn_multi_fixed_narrow_launch_shape():
+    """The launch-shape override (SSMD_TUNE, read once per process) asking
+    for blocks narrower than the kernel's chunk staging covers must still
+    give oracle-exact results over several token chunks: the library widens
+    such a shape to 4 waves. Runs in a fresh process so the override is read
+    before any other call."""
+    need_gpu()
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, SSMD_TUNE="2")
+    r = subprocess.run([sys.executable, "-c", "import tests.test_gdn_multi_gpu as t; t._fixed_shape_child()"],
+                       cwd=root, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "FIXED_SHAPE_OK" in r.stdout, (r.stdout[-3000:], r.stderr[-3000:])
