@@ -47,7 +47,7 @@ extern "C" {
 #define SSMD_ERR_NULL_ARG (-1)    /* a required pointer is NULL */
 #define SSMD_ERR_BAD_SHAPE (-2)   /* sizes, strides or alignment are inconsistent */
 #define SSMD_ERR_BAD_DTYPE (-3)   /* unknown dtype or activation code */
-#define SSMD_ERR_UNSUPPORTED (-4) /* head size not compiled in */
+#define SSMD_ERR_UNSUPPORTED (-4) /* head size not compiled in, or an input with no defined meaning */
 #define SSMD_ERR_LAUNCH (-5)      /* the HIP runtime refused the launch */
 
 /* element types */
@@ -285,8 +285,8 @@ int gdn_decode_step_conv(const void* x, int64_t x_row_stride,
  *   conv_state[s, c, :] <- window[1..W-1]
  * y = [q | k | v], each [H, D]. Per head h:
  *   if use_qk_l2norm: q, k L2-normalised (eps l2norm_eps); q <- scale * q;
- *   g[i]  = lower_bound * sigmoid(exp(A_log[h]) * (raw_g[t,h,i] + dt_bias[h*D+i]))
- *           (A_log / dt_bias NULL = 0, giving lower_bound * sigmoid(raw_g));
+ *   g[i]  = lower_bound * sigmoid(raw_g[t,h,i])   (per key channel i; the
+ *           workload's gate, lower_bound = -5);
  *   beta  = sigmoid(raw_beta[t, h]);
  *   S = state[s, h] (D x D, row = value index):
  *   S <- S diag(exp(g)); delta = beta (v - S k); S <- S + delta k^T; o = S q;
@@ -300,7 +300,11 @@ int gdn_decode_step_conv(const void* x, int64_t x_row_stride,
  *                layout [num_slots, W-1, C] has strides ((W-1)*C, 1, C),
  *                the DS layout [num_slots, C, W-1] has (C*(W-1), W-1, 1)
  *   raw_g        [T, H, D] act_dtype; raw_beta [T, H] act_dtype
- *   A_log [H] fp32 or NULL; dt_bias [H*D] fp32 or NULL
+ *   A_log, dt_bias: must be NULL. [KDA] `Inputs` and `fused` pass an A_log
+ *                [H] and a dt_bias [H*D] to the op without stating how they
+ *                enter the gate; rather than give them a meaning no page
+ *                fixes, a call with either non-NULL returns
+ *                SSMD_ERR_UNSUPPORTED and launches nothing.
  *   state        [num_slots, H, D, D] fp32, in place
  *   out          [T, H, D] out_dtype
  *   output_gate  [T, H, D] act_dtype or NULL (no norm); norm_weight [D] fp32 or NULL

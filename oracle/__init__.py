@@ -33,7 +33,7 @@ def configure(L: ctypes.CDLL) -> ctypes.CDLL:
     L.orc_sigmoid.argtypes = [_d]
     L.orc_silu.argtypes = [_d]
     L.orc_round_fmt.argtypes = [_d, _i]
-    L.orc_kda_gate.argtypes = [_d, _d, _d, _d]
+    L.orc_kda_gate.argtypes = [_d, _d]
     for f in ("orc_softplus", "orc_sigmoid", "orc_silu", "orc_round_fmt", "orc_kda_gate"):
         getattr(L, f).restype = _d
     L.orc_gdn_gates.argtypes = [_d, _d, _d, _d, _dp, _dp]
@@ -42,15 +42,19 @@ def configure(L: ctypes.CDLL) -> ctypes.CDLL:
     L.orc_gdn_step.argtypes = gdn + [_i]
     L.orc_gdn_step_buffered.argtypes = gdn + [_dp, _dp, _dp, _ip, _i, _i]
     L.orc_conv1d_update.argtypes = [_i] * 4 + [_dp, _dp, _dp, _dp, _ip, _i, _dp, _i]
-    L.orc_kda_step.argtypes = [_i] * 4 + [_dp, _dp, _dp, _dp, _dp, _d, _dp, _ip, _dp,
+    L.orc_kda_step.argtypes = [_i] * 4 + [_dp, _dp, _dp, _d, _dp, _ip, _dp,
                                           _dp, _dp, _d, _d, _i, _d]
-    L.orc_kda_decode.argtypes = [_i] * 5 + [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _d,
+    L.orc_kda_decode.argtypes = [_i] * 5 + [_dp, _dp, _dp, _dp, _dp, _dp, _d,
                                             _dp, _ip, _dp, _dp, _dp, _d, _d, _i, _d, _dp]
     L.orc_mamba_step.argtypes = [_i] * 4 + [_dp] * 8 + [_ip, _dp]
     L.orc_gdn_multi.argtypes = [_i] * 7 + [_dp, ctypes.c_long] + [_dp] * 5 + [_ip, _ip, _dp, _d, _i, _d, _dp, _dp,
                                                                         _d, _i]
     L.orc_mamba_scan.argtypes = [_i] * 5 + [_dp] * 8 + [_ip, _ip, _i, _dp]
     L.orc_gdn_step_conv.argtypes = [_i] * 7 + [_dp] * 9 + [_ip, _dp, _d, _i, _d, _dp, _dp, _d, _i, _dp]
+    _fp = ctypes.POINTER(ctypes.c_float)
+    L.orc_gdn_step_f32.argtypes = [_i] * 6 + [_fp, _l, _fp, _fp, _fp, _fp, _fp, _ip, _fp, ctypes.c_float, _i,
+                                              ctypes.c_float]
+    L.orc_gdn_step_f32.restype = _i
     L.orc_set_threads.argtypes = [_i]
     L.orc_set_threads.restype = None
     for f in ("orc_gdn_step", "orc_gdn_step_buffered", "orc_conv1d_update", "orc_gdn_step_conv",
@@ -130,8 +134,8 @@ def gdn_gates(a, b, A_log, dt_bias):
     return g.value, beta.value
 
 
-def kda_gate(raw_g, A_log, dt_bias, lower_bound):
-    return lib().orc_kda_gate(float(raw_g), float(A_log), float(dt_bias), float(lower_bound))
+def kda_gate(raw_g, lower_bound):
+    return lib().orc_kda_gate(float(raw_g), float(lower_bound))
 
 
 def num_threads() -> int:
@@ -163,6 +167,23 @@ def gdn_step(qkv, a, b, A_log, dt_bias, state, idx, *, H, HV, K, V, scale=None,
     _chk(lib().orc_gdn_step(B, H, HV, K, V, num_slots, _p(qkv), qkv.shape[1], _p(a), _p(b),
                             _p(A_log), _p(dt_bias), _p(state), _p(idx), _p(out), scale,
                             int(use_l2), l2eps, _p(ng), _p(nw), norm_eps, norm_act, int(state_fmt)))
+    return out
+
+
+def gdn_step_f32(qkv, a, b, A_log, dt_bias, state, idx, *, H, HV, K, V, scale=None, use_l2=True, l2eps=1e-6):
+    """The packed GDN step computed entirely in fp32 (the oracle's float
+    build, no output norm). `state` is a float32 [num_slots, HV, V, K] array
+    updated in place. Returns out float32 [B, HV, V] (NaN for padded rows)."""
+    f32 = lambda x: np.ascontiguousarray(f64(x).astype(np.float32))  # noqa: E731
+    qkv, a, b, A_log, dt_bias, idx = f32(qkv), f32(a), f32(b), f32(A_log), f32(dt_bias), i32(idx)
+    assert state.dtype == np.float32 and state.flags["C_CONTIGUOUS"]
+    assert state.shape[1:] == (HV, V, K)
+    B = idx.shape[0]
+    out = np.full((B, HV, V), np.nan, dtype=np.float32)
+    fp = lambda x: x.ctypes.data_as(ctypes.POINTER(ctypes.c_float))  # noqa: E731
+    scale = K ** -0.5 if scale is None else scale
+    _chk(lib().orc_gdn_step_f32(B, H, HV, K, V, state.shape[0], fp(qkv), qkv.shape[1], fp(a), fp(b), fp(A_log),
+                                fp(dt_bias), fp(state), _p(idx), fp(out), scale, int(use_l2), l2eps))
     return out
 
 
@@ -254,27 +275,23 @@ def conv1d_update(x, w, bias, conv_state, idx, *, skip_slot0=True, silu_act=True
     return y
 
 
-def kda_step(y, raw_g, raw_beta, state, idx, *, H, D, A_log=None, dt_bias=None,
-             lower_bound=-5.0, gate=None, norm_weight=None, norm_eps=1e-5, scale=None,
+def kda_step(y, raw_g, raw_beta, state, idx, *, H, D, lower_bound=-5.0, gate=None, norm_weight=None, norm_eps=1e-5, scale=None,
              use_l2=True, l2eps=1e-6):
     """KDA recurrent step on post-conv activations y [T, 3*H*D]; state float64
     [num_slots, H, D, D] in place. Returns out [T, H, D]."""
     y, raw_g, raw_beta, idx = f64(y), f64(raw_g), f64(raw_beta), i32(idx)
     T = idx.shape[0]
     out = np.full((T, H, D), np.nan)
-    A = None if A_log is None else f64(A_log)
-    dtb = None if dt_bias is None else f64(dt_bias)
     gt = None if gate is None else f64(gate)
     nw = None if norm_weight is None else f64(norm_weight)
     scale = D ** -0.5 if scale is None else scale
-    _chk(lib().orc_kda_step(T, H, D, state.shape[0], _p(y), _p(raw_g), _p(raw_beta), _p(A),
-                            _p(dtb), lower_bound, _p(state), _p(idx), _p(out), _p(gt), _p(nw),
+    _chk(lib().orc_kda_step(T, H, D, state.shape[0], _p(y), _p(raw_g), _p(raw_beta), lower_bound, _p(state), _p(idx), _p(out), _p(gt), _p(nw),
                             norm_eps, scale, int(use_l2), l2eps))
     return out
 
 
 def kda_decode(x, conv_w, conv_bias, conv_state, raw_g, raw_beta, state, idx, *, H, D,
-               A_log=None, dt_bias=None, lower_bound=-5.0, gate=None, norm_weight=None,
+               lower_bound=-5.0, gate=None, norm_weight=None,
                norm_eps=1e-5, scale=None, use_l2=True, l2eps=1e-6):
     """Fused KDA decode: conv1d update (+SiLU) -> KDA step -> sigmoid-gated
     RMSNorm. conv_state float64 logical [num_slots, 3HD, W-1] and state float64
@@ -285,14 +302,11 @@ def kda_decode(x, conv_w, conv_bias, conv_state, raw_g, raw_beta, state, idx, *,
     W = conv_w.shape[1]
     out = np.full((T, H, D), np.nan)
     ysc = np.zeros((T, 3 * H * D))
-    A = None if A_log is None else f64(A_log)
-    dtb = None if dt_bias is None else f64(dt_bias)
     gt = None if gate is None else f64(gate)
     nw = None if norm_weight is None else f64(norm_weight)
     scale = D ** -0.5 if scale is None else scale
     _chk(lib().orc_kda_decode(T, H, D, W, state.shape[0], _p(x), _p(conv_w), _p(cb),
-                              _p(conv_state), _p(raw_g), _p(raw_beta), _p(A), _p(dtb),
-                              lower_bound, _p(state), _p(idx), _p(out), _p(gt), _p(nw),
+                              _p(conv_state), _p(raw_g), _p(raw_beta), lower_bound, _p(state), _p(idx), _p(out), _p(gt), _p(nw),
                               norm_eps, scale, int(use_l2), l2eps, _p(ysc)))
     return out
 

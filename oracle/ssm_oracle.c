@@ -24,10 +24,10 @@
  * not change any arithmetic.
  *
  * Parity pins (closed forms, invariants, a hand-worked 4x4 case) live in
- * tests/test_oracle_pins.py. Parity unpinned: the KDA gate when A_log or
- * dt_bias is given (only the A_log = dt_bias = 0 special case is pinned), and
- * the choice to L2-normalise q/k in the KDA step (a reading, not a formula the
- * pages print).
+ * tests/test_oracle_pins.py; every function here is pinned by at least one
+ * of them. One choice is a reading rather than a formula the pages print:
+ * L2-normalising q/k in the KDA step (optional, as in the GDN step, whose
+ * arithmetic it shares and whose pins cover it).
  */
 #include <math.h>
 #include <stdint.h>
@@ -104,14 +104,14 @@ void orc_gdn_gates(double a, double b, double A_log, double dt_bias,
     *beta = orc_sigmoid(b);
 }
 
-/* KDA per-channel gate. The fused-op workload fixes g = lb * sigmoid(raw_g)
- * with lb = -5 [KDA, constants and `fused` call: lower_bound]. The pages also
- * pass A_log[H] and dt_bias[H*D] without saying how they enter; the reading
- * used here is g = lb * sigmoid(exp(A_log) * (raw_g + dt_bias)), which reduces
- * to the stated formula when A_log = dt_bias = 0 (parity unpinned otherwise). */
-double orc_kda_gate(double raw_g, double A_log, double dt_bias, double lb)
+/* KDA per-channel gate, as the fused-op workload fixes it: g = lb *
+ * sigmoid(raw_g) with lb = -5 [KDA, constants and the `fused` call:
+ * lower_bound]. The pages also pass A_log[H] and dt_bias[H*D] to the op
+ * without saying how they enter the gate, so no form using them is computed
+ * here (the library refuses them). */
+double orc_kda_gate(double raw_g, double lb)
 {
-    return lb * orc_sigmoid(exp(A_log) * (raw_g + dt_bias));
+    return lb * orc_sigmoid(raw_g);
 }
 
 /* ------------------------------------------------------------------ */
@@ -247,6 +247,80 @@ int orc_gdn_step(int B, int H, int HV, int K, int V, int num_slots,
             free(q);
         }
     }
+    return ORC_OK;
+}
+
+/* The packed GDN step once more, every value in IEEE fp32 (float, no
+ * wider intermediates: each operation rounds to float). A sanity build of
+ * the oracle, not a second oracle: it runs the same method in the same order
+ * (gates, optional q/k L2 norm and scale, decay, S k, delta, rank-1 update,
+ * S q) without the output norm, so the fp64 oracle can be held against a
+ * float computation of the same recurrence (the fp32 tolerance of [MBU]
+ * "Correctness" is the bar). state is fp32 [num_slots][HV][V][K], updated in
+ * place; out is fp32 [B][HV][V]. */
+int orc_gdn_step_f32(int B, int H, int HV, int K, int V, int num_slots,
+                     const float *qkv, long qkv_stride, const float *a_in,
+                     const float *b_in, const float *A_log, const float *dt_bias,
+                     float *state, const int32_t *idx, float *out, float scale,
+                     int use_l2, float l2eps)
+{
+    if (B < 0 || H < 1 || HV < 1 || HV % H || K < 1 || V < 1 || num_slots < 1)
+        return ORC_BAD;
+    const int grp = HV / H;
+    float *qs = malloc(sizeof(float) * (2 * (size_t)K + 2 * (size_t)V));
+    float *ks = qs + K, *sk = ks + K, *dl = sk + V;
+    for (int bi = 0; bi < B; ++bi) {
+        const int slot = idx[bi];
+        if (slot < 0 || slot >= num_slots)
+            continue;
+        const float *x = qkv + (size_t)bi * qkv_stride;
+        for (int hv = 0; hv < HV; ++hv) {
+            const float *xq = x + (size_t)(hv / grp) * K;
+            const float *xk = x + (size_t)H * K + (size_t)(hv / grp) * K;
+            const float *xv = x + 2 * (size_t)H * K + (size_t)hv * V;
+            float nq = 1.0f, nk = 1.0f;
+            if (use_l2) {
+                float s2q = 0.0f, s2k = 0.0f;
+                for (int i = 0; i < K; ++i) {
+                    s2q += xq[i] * xq[i];
+                    s2k += xk[i] * xk[i];
+                }
+                nq = 1.0f / sqrtf(s2q + l2eps);
+                nk = 1.0f / sqrtf(s2k + l2eps);
+            }
+            for (int i = 0; i < K; ++i) {
+                qs[i] = xq[i] * nq * scale;
+                ks[i] = xk[i] * nk;
+            }
+            const float z = a_in[(size_t)bi * HV + hv] + dt_bias[hv];
+            const float sp = z > 20.0f ? z : log1pf(expf(z));
+            const float gl = -expf(A_log[hv]) * sp;
+            const float bt = 1.0f / (1.0f + expf(-b_in[(size_t)bi * HV + hv]));
+            const float ed = expf(gl);
+            float *M = state + ((size_t)slot * HV + hv) * (size_t)V * K;
+            for (size_t e = 0; e < (size_t)V * K; ++e)
+                M[e] = M[e] * ed;
+            for (int r = 0; r < V; ++r) {
+                float dot = 0.0f;
+                for (int i = 0; i < K; ++i)
+                    dot += M[(size_t)r * K + i] * ks[i];
+                sk[r] = dot;
+            }
+            for (int r = 0; r < V; ++r)
+                dl[r] = bt * (xv[r] - sk[r]);
+            for (int r = 0; r < V; ++r)
+                for (int i = 0; i < K; ++i)
+                    M[(size_t)r * K + i] = M[(size_t)r * K + i] + dl[r] * ks[i];
+            float *o = out + ((size_t)bi * HV + hv) * V;
+            for (int r = 0; r < V; ++r) {
+                float dot = 0.0f;
+                for (int i = 0; i < K; ++i)
+                    dot += M[(size_t)r * K + i] * qs[i];
+                o[r] = dot;
+            }
+        }
+    }
+    free(qs);
     return ORC_OK;
 }
 
@@ -438,16 +512,16 @@ int orc_conv1d_update(int T, int C, int W, int num_slots, const double *x,
 /* KDA recurrent step on the post-conv activations y [T][3*H*D] = [q | k | v]
  * ([KDA] `triton_chain`: the conv output feeds fused_recurrent_kda_packed_decode
  * as mixed_qkv). Per token t and head h:
- *   q, k <- L2-normalised, q *= scale          (reading; parity unpinned)
- *   g[c] <- orc_kda_gate(raw_g[t,h,c], ...)    (per key channel)
+ *   q, k <- L2-normalised, q *= scale          (optional; a reading: the
+ *                                               pages' chain shows no norm)
+ *   g[c] <- orc_kda_gate(raw_g[t,h,c], lb)     (per key channel)
  *   beta <- sigmoid(raw_beta[t,h])
  *   delta rule with decay[c] = exp(g[c])
  *   o <- gated RMSNorm with a sigmoid gate ([KDA] `_gated_rmsnorm`) if gate
  * A token is skipped when its slot is <= 0 or >= num_slots (slot 0 is the
- * NULL block, [KDA] `Inputs`). A_log [H] / dt_bias [H*D] may be NULL (= 0). */
+ * NULL block, [KDA] `Inputs`). */
 int orc_kda_step(int T, int H, int D, int num_slots, const double *y,
-                 const double *raw_g, const double *raw_beta,
-                 const double *A_log, const double *dt_bias, double lower_bound,
+                 const double *raw_g, const double *raw_beta, double lower_bound,
                  double *state, const int32_t *idx, double *out,
                  const double *gate, const double *norm_w, double norm_eps,
                  double scale, int use_l2, double l2eps)
@@ -467,10 +541,7 @@ int orc_kda_step(int T, int H, int D, int num_slots, const double *y,
             prep_qk(row + (size_t)h * D, row + (size_t)H * D + (size_t)h * D, D,
                     scale, use_l2, l2eps, q, k);
             for (int c = 0; c < D; ++c) {
-                double gc = orc_kda_gate(raw_g[((size_t)t * H + h) * D + c],
-                                         A_log ? A_log[h] : 0.0,
-                                         dt_bias ? dt_bias[(size_t)h * D + c] : 0.0,
-                                         lower_bound);
+                double gc = orc_kda_gate(raw_g[((size_t)t * H + h) * D + c], lower_bound);
                 decay[c] = exp(gc);
             }
             const double beta = orc_sigmoid(raw_beta[(size_t)t * H + h]);
@@ -495,8 +566,7 @@ int orc_kda_step(int T, int H, int D, int num_slots, const double *y,
 int orc_kda_decode(int T, int H, int D, int W, int num_slots, const double *x,
                    const double *conv_w, const double *conv_bias,
                    double *conv_state, const double *raw_g,
-                   const double *raw_beta, const double *A_log,
-                   const double *dt_bias, double lower_bound, double *state,
+                   const double *raw_beta, double lower_bound, double *state,
                    const int32_t *idx, double *out, const double *gate,
                    const double *norm_w, double norm_eps, double scale,
                    int use_l2, double l2eps, double *y_scratch)
@@ -505,8 +575,8 @@ int orc_kda_decode(int T, int H, int D, int W, int num_slots, const double *x,
                                conv_state, idx, 1, y_scratch, 1);
     if (rc)
         return rc;
-    return orc_kda_step(T, H, D, num_slots, y_scratch, raw_g, raw_beta, A_log,
-                        dt_bias, lower_bound, state, idx, out, gate, norm_w,
+    return orc_kda_step(T, H, D, num_slots, y_scratch, raw_g, raw_beta,
+                        lower_bound, state, idx, out, gate, norm_w,
                         norm_eps, scale, use_l2, l2eps);
 }
 

@@ -367,7 +367,9 @@ def kda_decode_step(x, conv_weight, conv_bias, conv_state, raw_g, raw_beta, A_lo
                     norm_eps=1e-5, scale=None, use_qk_l2norm=True, l2norm_eps=1e-6, stream=None):
     """The fused KDA decode op (conv1d update + SiLU, KDA delta rule, sigmoid
     gated RMSNorm); see kda_decode_step in include/ssmdec.h. conv_state is the
-    logical [num_slots, 3*H*D, W-1] view of either physical layout."""
+    logical [num_slots, 3*H*D, W-1] view of either physical layout. A_log and
+    dt_bias are passed through as the ABI takes them; the library refuses
+    anything but None for them (no formula for them is defined)."""
     _dev(state, "state", torch.float32)
     if state.dim() != 4 or state.shape[2] != state.shape[3]:
         raise ValueError("state must be [num_slots, H, D, D]")

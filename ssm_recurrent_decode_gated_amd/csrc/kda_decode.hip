@@ -157,15 +157,8 @@ __global__ __launch_bounds__(512) void kda_decode_kernel(KdaParams p) {
     kq += kf[e] * qf[e];
   }
   kq = group_sum<LPR>(kq);
-  const float ea = p.A_log ? expf(p.A_log[h]) : 1.f;
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float db = p.dt_bias ? p.dt_bias[h * D + RL::col(c, j) + e] : 0.f;
-      dec[4 * j + e] = expf(p.lower_bound * sigmoid_f(ea * (rg[4 * j + e] + db)));
-    }
-  }
+  for (int e = 0; e < NV * 4; ++e) dec[e] = expf(p.lower_bound * sigmoid_f(rg[e]));
   const float beta = sigmoid_f(rbeta);
 
   // ---- stream the state rows

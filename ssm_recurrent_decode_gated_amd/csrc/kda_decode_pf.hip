@@ -29,7 +29,7 @@ namespace ssmd {
 
 constexpr int KPF_WAVES = 4;
 
-template <int D, bool NORM, int ACT, bool GP>
+template <int D, bool NORM, int ACT>
 __global__ __launch_bounds__(64 * KPF_WAVES) void kda_decode_pf_kernel(KdaParams p, int n_units) {
   using RL = RowLayout<D>;
   constexpr int LPR = RL::LPR, NV = RL::NV, RPI = RL::RPI;
@@ -67,7 +67,6 @@ __global__ __launch_bounds__(64 * KPF_WAVES) void kda_decode_pf_kernel(KdaParams
     T win[CPT][W];  // conv windows: state taps 0..W-2 (oldest first), then x
     float wv[CPT][W], bias[CPT];
     T graw, rbeta, z;  // raw activation values, converted when used
-    float dbv, alog;
     f4 s[RG][NV];
   };
   auto valid = [&](const Unit& U) { return U.slot > 0 && U.slot < p.num_slots; };  // slot 0: NULL block
@@ -89,10 +88,6 @@ __global__ __launch_bounds__(64 * KPF_WAVES) void kda_decode_pf_kernel(KdaParams
     }
     const int64_t hoff = ((int64_t)U.t * p.H + U.h) * D;
     U.graw = static_cast<const T*>(p.raw_g)[hoff + col];
-    if constexpr (GP) {
-      U.dbv = p.dt_bias[(int64_t)U.h * D + col];
-      U.alog = p.A_log[U.h];
-    }
     U.rbeta = static_cast<const T*>(p.raw_beta)[(int64_t)U.t * p.H + U.h];
     if constexpr (NORM) U.z = static_cast<const T*>(p.gate)[hoff + col];
     const float* S = p.state + ((int64_t)U.slot * p.H + U.h) * (int64_t)D * D;
@@ -149,10 +144,7 @@ __global__ __launch_bounds__(64 * KPF_WAVES) void kda_decode_pf_kernel(KdaParams
       }
     }
     // ---- per-column decay, one column per thread
-    if (tid < D) {
-      const float ea = GP ? expf(U.alog) : 1.f;
-      dl[tid] = expf(p.lower_bound * sigmoid_f(ea * (to_f(U.graw) + (GP ? U.dbv : 0.f))));
-    }
+    if (tid < D) dl[tid] = expf(p.lower_bound * sigmoid_f(to_f(U.graw)));
     __syncthreads();
     epilogue();  // the previous unit's outputs (its o and sums are complete)
     // ---- q, k fragments, norms, the decay of this lane's columns
@@ -265,25 +257,20 @@ namespace {
 // block per CU walking the units: several resident blocks per CU, each with
 // all its loads issued at once, keep more bytes in flight than one walking
 // block's one-unit-ahead prefetch.
-template <int D, bool NORM, int ACT, bool GP>
+template <int D, bool NORM, int ACT>
 hipError_t launch_kpf(const KdaParams& p, int cap, hipStream_t st) {
   const int64_t units = (int64_t)p.T * p.H;
   const int64_t blocks = cap > 0 && units > cap ? cap : units;
-  kda_decode_pf_kernel<D, NORM, ACT, GP><<<dim3((unsigned)blocks), dim3(64 * KPF_WAVES), 0, st>>>(p, (int)units);
+  kda_decode_pf_kernel<D, NORM, ACT><<<dim3((unsigned)blocks), dim3(64 * KPF_WAVES), 0, st>>>(p, (int)units);
   return hipGetLastError();
-}
-
-template <int D, bool NORM, int ACT>
-hipError_t launch_kpf_gp(const KdaParams& p, int cap, hipStream_t st) {
-  return p.A_log || p.dt_bias ? launch_kpf<D, NORM, ACT, true>(p, cap, st) : launch_kpf<D, NORM, ACT, false>(p, cap, st);
 }
 
 template <int D, bool NORM>
 hipError_t launch_kpf_act(const KdaParams& p, int cap, hipStream_t st) {
   switch (p.act_dt) {
-    case SSMD_F32: return launch_kpf_gp<D, NORM, SSMD_F32>(p, cap, st);
-    case SSMD_BF16: return launch_kpf_gp<D, NORM, SSMD_BF16>(p, cap, st);
-    default: return launch_kpf_gp<D, NORM, SSMD_F16>(p, cap, st);
+    case SSMD_F32: return launch_kpf<D, NORM, SSMD_F32>(p, cap, st);
+    case SSMD_BF16: return launch_kpf<D, NORM, SSMD_BF16>(p, cap, st);
+    default: return launch_kpf<D, NORM, SSMD_F16>(p, cap, st);
   }
 }
 
@@ -295,7 +282,7 @@ hipError_t launch_kpf_norm(const KdaParams& p, int cap, hipStream_t st) {
 }  // namespace
 
 bool kda_pf_supported(const KdaParams& p) {
-  return (p.D == 64 || p.D == 128) && p.W == 4 && (p.A_log != nullptr) == (p.dt_bias != nullptr);
+  return (p.D == 64 || p.D == 128) && p.W == 4;
 }
 
 hipError_t launch_kda_pf(const KdaParams& p, const Launch& l, hipStream_t st) {

@@ -406,6 +406,14 @@ int kda_decode_step(const void* x, const float* conv_weight, const float* conv_b
   if (cs_slot_stride < 1 || cs_chan_stride < 1 || cs_tap_stride < 1)
     return fail(SSMD_ERR_BAD_SHAPE, "%s: conv-state strides must be positive", fn);
   if ((int64_t)T * H >= (1LL << 31)) return fail(SSMD_ERR_BAD_SHAPE, "%s: T*H too large", fn);
+  // The pages pass A_log and dt_bias to the fused op but state no formula for
+  // them; the gate computed here is the workload's lower_bound *
+  // sigmoid(raw_g), and a call that supplies either tensor is refused rather
+  // than given a meaning no page fixes.
+  if (A_log || dt_bias)
+    return fail(SSMD_ERR_UNSUPPORTED,
+                "%s: A_log / dt_bias must be NULL (no formula for them is defined; the gate is "
+                "lower_bound * sigmoid(raw_g))", fn);
   if (T == 0) return ok();
   if (!x || !conv_weight || !conv_state || !raw_g || !raw_beta || !state || !state_indices || !out)
     return fail(SSMD_ERR_NULL_ARG, "%s: a required pointer is NULL", fn);
@@ -421,8 +429,6 @@ int kda_decode_step(const void* x, const float* conv_weight, const float* conv_b
   p.raw_g = raw_g;
   p.raw_g_vec = aligned(raw_g, 4 * dtype_bytes(act_dtype));
   p.raw_beta = raw_beta;
-  p.A_log = A_log;
-  p.dt_bias = dt_bias;
   p.lower_bound = lower_bound;
   p.state = state;
   p.num_slots = num_slots;
@@ -440,7 +446,7 @@ int kda_decode_step(const void* x, const float* conv_weight, const float* conv_b
   p.scale = scale;
   p.use_l2 = use_qk_l2norm ? 1 : 0;
   p.l2eps = l2norm_eps;
-  if (ssmd::kda_pf_supported(p) && aligned(conv_weight, 16) && (!dt_bias || aligned(dt_bias, 16)))
+  if (ssmd::kda_pf_supported(p) && aligned(conv_weight, 16))
     return launch_status(ssmd::launch_kda_pf(p, launch_for(), stream), fn);
   return launch_status(ssmd::launch_kda(p, launch_for(), stream), fn);
 }

@@ -78,8 +78,6 @@ struct KdaParams {
   const void* raw_g;
   bool raw_g_vec;  // raw_g is 4-element aligned: vector loads
   const void* raw_beta;
-  const float* A_log;
-  const float* dt_bias;
   float lower_bound;
   float* state;
   int32_t num_slots;
@@ -149,9 +147,9 @@ hipError_t launch_gdn_pf(const GdnParams& p, const Launch& l, int n_cu, hipStrea
 hipError_t launch_gdn_s16(const GdnParams& p, const Launch& l, int n_cu, hipStream_t s);
 hipError_t launch_gdn_buffered(const GdnParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_kda(const KdaParams& p, const Launch& l, hipStream_t s);
-// Persistent prefetching form of the KDA op for head size 64/128, conv width
-// 4, A_log and dt_bias both given or both NULL (16-byte aligned conv weights
-// and dt_bias); kda_pf_supported says whether a call qualifies.
+// Persistent prefetching form of the KDA op for head size 64/128 and conv
+// width 4 (16-byte aligned conv weights); kda_pf_supported says whether a
+// call qualifies.
 bool kda_pf_supported(const KdaParams& p);
 hipError_t launch_kda_pf(const KdaParams& p, const Launch& l, hipStream_t s);
 hipError_t launch_gdn_conv(const GdnConvParams& p, const Launch& l, int n_cu, hipStream_t s);

@@ -101,10 +101,11 @@ def test_buffered_host_validation():
 def test_kda_host_validation():
     L = S.load_library()
 
-    def call(T=64, H=96, D=128, W=4, x=0x10000, cs=(216 * 128 * 3, 1, 36864), act=1, state=0x60000):
-        return L.kda_decode_step(x, 0x20000, None, 0x30000, cs[0], cs[1], cs[2], 0x40000, 0x50000, None, None,
-                                 -5.0, state, 72, 0x70000, 0x80000, 0x90000, None, 1e-5, T, H, D, W, act, 1,
-                                 0.088, 1, 1e-6, None)
+    def call(T=64, H=96, D=128, W=4, x=0x10000, cs=(216 * 128 * 3, 1, 36864), act=1, state=0x60000,
+             A_log=None, dt_bias=None):
+        return L.kda_decode_step(x, 0x20000, None, 0x30000, cs[0], cs[1], cs[2], 0x40000, 0x50000, A_log,
+                                 dt_bias, -5.0, state, 72, 0x70000, 0x80000, 0x90000, None, 1e-5, T, H, D, W,
+                                 act, 1, 0.088, 1, 1e-6, None)
     assert call(D=96) == UNSUPPORTED
     assert call(W=1) == BAD_SHAPE
     assert call(W=9) == BAD_SHAPE
@@ -115,6 +116,11 @@ def test_kda_host_validation():
     assert call(cs=(0, 1, 1)) == BAD_SHAPE
     assert call(state=0x60008) == BAD_SHAPE
     assert call(T=0, x=None) == OK
+    # A_log / dt_bias have no formula on the pages: refused, also for an empty call
+    assert call(A_log=0xA0000) == UNSUPPORTED
+    assert "A_log" in S.ssmd_last_error()
+    assert call(dt_bias=0xB0000) == UNSUPPORTED
+    assert call(A_log=0xA0000, dt_bias=0xB0000, T=0) == UNSUPPORTED
 
 
 def test_stream_copy_host_validation():

@@ -33,8 +33,7 @@ MUTANTS = [
      "act == ORC_ACT_SIGMOID ? orc_silu(gate[r]) : orc_sigmoid(gate[r])"),
     ("conv no roll", "cs[j] = win[j + 1];", "cs[j] = win[j];"),
     ("conv taps reversed", "acc += w[(size_t)c * W + j] * win[j];", "acc += w[(size_t)c * W + j] * win[W - 1 - j];"),
-    ("kda gate sign", "return lb * orc_sigmoid(exp(A_log) * (raw_g + dt_bias));",
-     "return lb * orc_sigmoid(-exp(A_log) * (raw_g + dt_bias));"),
+    ("kda gate sign", "return lb * orc_sigmoid(raw_g);", "return lb * orc_sigmoid(-raw_g);"),
     ("kda keeps slot 0", "if (s <= 0 || s >= num_slots)\n                continue;\n            const size_t C",
      "if (s < 0 || s >= num_slots)\n                continue;\n            const size_t C"),
     ("replay without decay", "S[(size_t)r * K + c] = dj * S[(size_t)r * K + c] +",

@@ -91,12 +91,13 @@ def test_gdn_gates_closed_forms():
     assert g == -30.0
 
 
-def test_kda_gate_reduces_to_lower_bound_sigmoid():
-    # with A_log = dt_bias = 0 the gate is lb * sigmoid(raw_g)
-    assert O.kda_gate(0.0, 0.0, 0.0, -5.0) == -2.5
-    assert O.kda_gate(math.log(3.0), 0.0, 0.0, -5.0) == pytest.approx(-3.75, rel=1e-15)
-    assert O.kda_gate(-BIG, 0.0, 0.0, -5.0) == pytest.approx(0.0, abs=1e-80)
-    assert O.kda_gate(BIG, 0.0, 0.0, -5.0) == -5.0
+def test_kda_gate_is_lower_bound_sigmoid():
+    # the workload's gate lb * sigmoid(raw_g): sigmoid(0) = 1/2, sigmoid(ln 3) = 3/4
+    assert O.kda_gate(0.0, -5.0) == -2.5
+    assert O.kda_gate(math.log(3.0), -5.0) == pytest.approx(-3.75, rel=1e-15)
+    assert O.kda_gate(-math.log(3.0), -4.0) == pytest.approx(-1.0, rel=1e-15)
+    assert O.kda_gate(-BIG, -5.0) == pytest.approx(0.0, abs=1e-80)
+    assert O.kda_gate(BIG, -5.0) == -5.0
 
 
 # ------------------------------------------------------------ GDN step
@@ -443,7 +444,7 @@ def test_pin_kda_decay_is_per_key_column():
     s0 = st.copy()
     O.kda_step(y, raw_g, np.full((1, H), -BIG), st, [1], H=H, D=D)
     for h in range(H):
-        dec = np.exp([O.kda_gate(r, 0.0, 0.0, -5.0) for r in raw_g[0, h]])
+        dec = np.exp(-5.0 / (1.0 + np.exp(-raw_g[0, h])))  # e^{lb sigmoid(raw_g)}, lb = -5
         np.testing.assert_allclose(st[1, h], s0[1, h] * dec[None, :], rtol=1e-15)
     np.testing.assert_array_equal(st[0], s0[0])
 
@@ -652,3 +653,30 @@ def test_pin_gdn_multi_lengths_padding_split():
                       H=H, HV=HV, K=K, V=V)
     np.testing.assert_array_equal(np.concatenate([o3a, o3b], axis=1)[0], o[0])
     np.testing.assert_array_equal(st3[4], st[4])
+
+
+# ------------------------------------------------------- fp32 build (Pin-14)
+def test_fp32_build_matches_fp64_on_tiny_chain():
+    """The oracle's fp32 build of the packed step against its fp64 one on the
+    tiny workload (B = 2, H = HV = 2, K = V = 16, fp32 inputs, q/k L2-normed,
+    a ~ N(0,1), S0 ~ N(0, 0.1^2)), 64 chained steps from the same fp32
+    state, each side on its own trajectory: every output and the final state
+    within 1e-5 (the fp32 tolerance of [MBU] "Correctness"). A mistake in
+    either build (they share no code) separates them by far more."""
+    import workloads as W
+    from tests._helpers import mixed_err
+    w = W.GDN_TINY
+    P, idx = W.gdn_params(w), W.slot_indices(w)
+    s0 = W.gdn_state(w)
+    s64, s32 = s0.double().numpy().copy(), s0.numpy().copy()
+    worst = 0.0
+    for t in range(w.steps):
+        x = W.gdn_step_inputs(w, t)
+        o64 = O.gdn_step(x["qkv"], x["a"], x["b"], P["A_log"], P["dt_bias"], s64, idx, H=w.H, HV=w.HV, K=w.K,
+                         V=w.V)
+        o32 = O.gdn_step_f32(x["qkv"], x["a"], x["b"], P["A_log"], P["dt_bias"], s32, idx, H=w.H, HV=w.HV,
+                             K=w.K, V=w.V)
+        worst = max(worst, float(mixed_err(o32, o64).max()))
+    worst = max(worst, float(mixed_err(s32, s64).max()))
+    assert worst <= 1e-5, worst
+    assert worst > 0.0  # the float build really rounds to fp32
