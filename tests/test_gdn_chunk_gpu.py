@@ -9,7 +9,7 @@ import torch
 import oracle as O
 import ssm_recurrent_decode_gated_amd as S
 import workloads as W
-from tests._helpers import CHAIN_TOL, FP32_TOL, assert_16bit, assert_mixed, need_gpu
+from tests._helpers import CHAIN_TOL, FP32_TOL, assert_out16, assert_mixed, need_gpu
 from tests.test_gdn_multi_gpu import _inputs
 
 pytestmark = pytest.mark.gpu
@@ -41,7 +41,7 @@ def _check(out, ro, tol, what):
     if out.dtype == torch.float32:
         assert_mixed(out.cpu(), ro, tol, what)
     else:
-        assert_16bit(out, ro, tol, what)
+        assert_out16(out, ro, tol, what)
 
 
 def test_gdn_chunk_prompt_2048():

@@ -1,6 +1,6 @@
 """GPU parity of gdn_decode_step_conv (causal conv1d update + SiLU fused in
 front of the GDN step) against the fp64 oracle: outputs and states to the
-fp32 tolerance (16-bit outputs to one ulp of the exact value), the rolled conv
+fp32 tolerance (16-bit outputs: the RNE of the exact value), the rolled conv
 state bit for bit (it holds raw inputs), and padded rows touching nothing."""
 import numpy as np
 import pytest
@@ -9,7 +9,7 @@ import torch
 import oracle as O
 import ssm_recurrent_decode_gated_amd as S
 import workloads as W
-from tests._helpers import CHAIN_TOL, FP32_TOL, assert_16bit, assert_mixed, need_gpu
+from tests._helpers import CHAIN_TOL, FP32_TOL, assert_out16, assert_mixed, need_gpu
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -48,7 +48,7 @@ def _check_out(out, ref, what):
     if out.dtype == torch.float32:
         assert_mixed(out.reshape(B, HV, V), ref, FP32_TOL, what)
     else:
-        assert_16bit(out.reshape(B, HV, V), ref, FP32_TOL, what)
+        assert_out16(out.reshape(B, HV, V), ref, FP32_TOL, what)
 
 
 def _setup(w, Wd=4, layout="DS", bias=True):

@@ -3,17 +3,17 @@
 Every case runs the same seeded inputs (workloads/) through the HIP kernel and
 through oracle/, and compares element by element: fp32 outputs and states to
 the mixed relative error 1e-4 (single step) or 2e-3 (chained), 16-bit outputs
-to one ulp of the exact value, and slot placement / untouched memory bit for
-bit.
+to the RNE of the exact value (the other neighbour only where a rounding
+midpoint lies within the fp32 bar), and slot placement / untouched memory bit
+for bit.
 """
-import numpy as np
 import pytest
 import torch
 
 import oracle as O
 import ssm_recurrent_decode_gated_amd as S
 import workloads as W
-from tests._helpers import CHAIN_TOL, FP32_TOL, assert_16bit, assert_mixed, need_gpu, to_np64
+from tests._helpers import CHAIN_TOL, FP32_TOL, assert_out16, assert_mixed, need_gpu, to_np64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -46,7 +46,7 @@ def _check_out(out, ref, what):
     if out.dtype == torch.float32:
         assert_mixed(out.reshape(B, HV, V), ref, FP32_TOL, what)
     else:
-        assert_16bit(out.reshape(B, HV, V), ref, FP32_TOL, what)
+        assert_out16(out.reshape(B, HV, V), ref, FP32_TOL, what)
 
 
 def test_gdn_tiny_fp32_chain_64_steps():
@@ -206,17 +206,15 @@ def test_gdn_strided_qkv_rows():
 @pytest.mark.slow
 def test_gdn_b64_1000_step_drift():
     """1000 chained steps at B=64, H=16, HV=32, K=V=128 with fresh inputs per
-    step. The GPU runs every row; the oracle follows 3 rows (96 heads) in
-    fp64; outputs at steps 1, 10, 100, 1000 and the final states of those
-    rows must stay within 2e-3 of the exact trajectory."""
+    step. The oracle follows all 64 rows (2048 heads) on its own fp64
+    trajectory; outputs at steps 1, 10, 100, 1000 and the final state of
+    every row must stay within 2e-3 of it."""
     need_gpu()
     w = W.GDN_B64_CHAIN
     P, idx = W.gdn_params(w), W.slot_indices(w)
     st = W.gdn_state(w)
     st_d = st.to(DEV)
-    rows = [0, 29, 63]
-    ref = st[rows].double().numpy().copy()
-    sub_idx = np.arange(len(rows), dtype=np.int32)
+    ref = st.double().numpy().copy()
     Pd = {k: v.to(DEV) for k, v in P.items()}
     idx_d = idx.to(DEV)
     out = torch.empty(w.B, 1, w.HV, w.V, dtype=torch.bfloat16, device=DEV)
@@ -227,8 +225,8 @@ def test_gdn_b64_1000_step_drift():
         o = out32 if t in checks else out
         S.gdn_decode_step(x["qkv"].to(DEV), x["a"].to(DEV), x["b"].to(DEV), Pd["A_log"], Pd["dt_bias"],
                           st_d, idx_d, o)
-        ro = O.gdn_step(x["qkv"][rows], x["a"][rows], x["b"][rows], P["A_log"], P["dt_bias"], ref,
-                        sub_idx, H=w.H, HV=w.HV, K=w.K, V=w.V)
+        ro = O.gdn_step(x["qkv"], x["a"], x["b"], P["A_log"], P["dt_bias"], ref, idx, H=w.H, HV=w.HV, K=w.K,
+                        V=w.V)
         if t in checks:
-            assert_mixed(out32[rows].reshape(len(rows), w.HV, w.V), ro, CHAIN_TOL, f"output at step {t}")
-    assert_mixed(st_d[rows], ref, CHAIN_TOL, "state after 1000 steps")
+            assert_mixed(out32.reshape(w.B, w.HV, w.V), ro, CHAIN_TOL, f"output at step {t}")
+    assert_mixed(st_d, ref, CHAIN_TOL, "state after 1000 steps")

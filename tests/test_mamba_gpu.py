@@ -9,7 +9,7 @@ import torch
 import oracle as O
 import ssm_recurrent_decode_gated_amd as S
 import workloads as W
-from tests._helpers import CHAIN_TOL, FP32_TOL, assert_16bit, assert_mixed, need_gpu, to_np64
+from tests._helpers import CHAIN_TOL, FP32_TOL, assert_out16, assert_mixed, need_gpu, to_np64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -48,7 +48,7 @@ def test_mamba_decode_step(case, with_D, with_z):
     if outd == torch.float32:
         assert_mixed(out.cpu(), ro, FP32_TOL, "y")
     else:
-        assert_16bit(out, ro, FP32_TOL, "y")
+        assert_out16(out, ro, FP32_TOL, "y")
     slots = d["idx"].tolist()
     assert_mixed(st[slots], ref[slots], FP32_TOL, "state")
     for s in set(range(w.num_slots)) - set(slots):

@@ -10,7 +10,7 @@ import torch
 import oracle as O
 import ssm_recurrent_decode_gated_amd as S
 import workloads as W
-from tests._helpers import FP32_TOL, assert_16bit, assert_mixed, need_gpu
+from tests._helpers import FP32_TOL, assert_out16, assert_mixed, need_gpu
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -41,7 +41,7 @@ def _check_out(out, ro, what="y"):
     if out.dtype == torch.float32:
         assert_mixed(out.cpu(), ro, FP32_TOL, what)
     else:
-        assert_16bit(out, ro, FP32_TOL, what)
+        assert_out16(out, ro, FP32_TOL, what)
 
 
 @pytest.mark.parametrize("path", ["chunked", "single_pass", "three_chunks"])

@@ -76,3 +76,60 @@ def test_ring16_f16_subnormal_neighbour_accepted():
     got = ref.copy()
     got[0, 2] = ref[0, 2] + 2.0 ** -24 if ref[0, 2] < ex[0, 2] else ref[0, 2] - 2.0 ** -24
     assert_rounded16(got, ref, "f16 subnormal", ex, 10)
+
+
+# ------------------------------------------------ 16-bit outputs (assert_out16)
+def test_rne16_matches_library_conversions():
+    """The test-side RNE against torch's float32 -> bf16 / f16 conversions
+    (each a single rounding): normal values, exact ties, tiny and subnormal
+    values, overflow."""
+    from tests._helpers import rne16
+    rng = np.random.default_rng(7)
+    x = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-8, 5, 20000),
+        (rng.integers(0, 1 << 16, 4000).astype(np.uint32) << 16 | 0x8000).view(np.float32),  # bf16 ties
+        [0.0, -0.0, 65504.0, 65519.0, 65520.0, 1e5, 6.0e-8, 3.0e-8, 2.0 ** -25, 3.4e38],
+    ]).astype(np.float32)
+    x = x[np.isfinite(x)]
+    t = torch.from_numpy(x)
+    np.testing.assert_array_equal(rne16(x.astype(np.float64), 7), t.to(torch.bfloat16).double().numpy())
+    np.testing.assert_array_equal(rne16(x.astype(np.float64), 10), t.to(torch.float16).double().numpy())
+
+
+def _out16_case(seed=0, dtype=torch.bfloat16):
+    ex = np.random.default_rng(seed).standard_normal((32, 128))
+    return ex, torch.from_numpy(ex).to(torch.float32).to(dtype)  # fp64 -> fp32 (exact to 1e-8) -> RNE
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_out16_accepts_a_correct_rounding(dtype):
+    from tests._helpers import assert_out16
+    ex, got = _out16_case(0, dtype)
+    assert_out16(got, ex, 1e-4, "rne")
+
+
+def test_out16_accepts_the_other_neighbour_only_near_a_midpoint():
+    from tests._helpers import assert_out16, rne16
+    lo = rne16(np.random.default_rng(1).standard_normal((16, 64)), 7)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(lo))[1] - 1 - 7)
+    up = lo + ulp * np.sign(lo)
+    near = 0.5 * (lo + up) + 1e-7 * np.sign(lo) * np.abs(lo)  # just past the midpoint: RNE gives `up`
+    assert_out16(torch.from_numpy(lo).to(torch.bfloat16), near, 1e-4, "other neighbour at a midpoint")
+    far = lo + 0.8 * (up - lo)  # well past the midpoint: only `up` is a correct rounding
+    with pytest.raises(AssertionError):
+        assert_out16(torch.from_numpy(lo).to(torch.bfloat16), far, 1e-4, "one ulp off")
+
+
+def test_out16_rejects_truncation():
+    from tests._helpers import assert_out16
+    ex, _ = _out16_case(2)
+    with pytest.raises(AssertionError):
+        assert_out16(torch.from_numpy(_bf16_trunc(ex)).to(torch.bfloat16), ex, 1e-4, "truncated")
+
+
+def test_out16_rejects_an_error_above_the_fp32_bar():
+    from tests._helpers import assert_out16
+    ex, _ = _out16_case(3)
+    bad = ex * (1 + 3e-3)  # a kernel 3e-3 off, rounded correctly
+    with pytest.raises(AssertionError):
+        assert_out16(torch.from_numpy(bad).to(torch.float32).to(torch.bfloat16), ex, 1e-4, "3e-3 off")

@@ -11,7 +11,7 @@ import torch
 import oracle as O
 import ssm_recurrent_decode_gated_amd as S
 import workloads as W
-from tests._helpers import FP32_TOL, assert_16bit, assert_mixed, assert_rounded16, need_gpu, to_np64
+from tests._helpers import FP32_TOL, assert_out16, assert_mixed, assert_rounded16, need_gpu, to_np64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -46,7 +46,7 @@ def _check(out, ref, live, what):
     if o.dtype == torch.float32:
         assert_mixed(o, ref[live], FP32_TOL, what)
     else:
-        assert_16bit(o, ref[live], FP32_TOL, what)
+        assert_out16(o, ref[live], FP32_TOL, what)
 
 
 CASES = list(range(48))
@@ -290,7 +290,7 @@ def test_random_gdn_multi(i):
         if o.dtype == torch.float32:
             assert_mixed(o, r, CHAIN_TOL_T(n), f"case {i} ({w.name}, T {T}) row {bi} outputs")
         else:
-            assert_16bit(o, r, CHAIN_TOL_T(n), f"case {i} ({w.name}, T {T}) row {bi} outputs")
+            assert_out16(o, r, CHAIN_TOL_T(n), f"case {i} ({w.name}, T {T}) row {bi} outputs")
         assert torch.isnan(out[bi, n:].float()).all(), f"case {i}: outputs past row {bi}'s length written"
     got = st_d.cpu()
     for s in range(w.num_slots):
@@ -387,7 +387,7 @@ def test_random_gdn_chunk_prefill(i):
             if o.dtype == torch.float32:
                 assert_mixed(o[bi, :n], ro[bi, :n], CHAIN_TOL_T(n), f"case {i} ({w.name}, norm {norm}) row {bi}")
             else:
-                assert_16bit(o[bi, :n], ro[bi, :n], CHAIN_TOL_T(n), f"case {i} ({w.name}, norm {norm}) row {bi}")
+                assert_out16(o[bi, :n], ro[bi, :n], CHAIN_TOL_T(n), f"case {i} ({w.name}, norm {norm}) row {bi}")
         assert (o[bi, n if live else 0:].float() == 7.0).all(), f"case {i}: row {bi} wrote past its length"
     got = st_d.cpu()
     for s in range(w.num_slots):
