@@ -232,6 +232,39 @@ int gdn_chunk_prefill(const void* mixed_qkv, int64_t qkv_row_stride,
                       hipStream_t stream);
 
 /*
+ * gdn_chunk_prefill_noalloc -- gdn_chunk_prefill for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same computation, arguments,
+ * layouts and conventions, without the workspace arguments. The workspace is
+ * instead a fixed array of SSMD_CHUNK_SCRATCH_BYTES in device memory that the
+ * library holds on each device it runs on until the process ends; the call
+ * allocates and frees nothing. Limits and behaviour:
+ *   - a call needing more than SSMD_CHUNK_SCRATCH_BYTES of workspace
+ *     (gdn_chunk_workspace_bytes of its sizes) returns SSMD_ERR_BAD_SHAPE
+ *     and launches nothing; 128 MiB holds the records of, e.g., one
+ *     4096-token row at HV = 32, or one 2048-token row with the gated norm;
+ *   - every call on a device shares that device's array: calls that can run
+ *     at the same time on one device (other streams, other threads) race on
+ *     it and must be ordered by the caller; the array's contents are
+ *     don't-care on entry and exit, so nothing needs clearing;
+ *   - the first call on a device looks up the array's device address
+ *     (hipGetSymbolAddress); make that first call outside stream capture.
+ */
+#define SSMD_CHUNK_SCRATCH_BYTES (128LL << 20)
+int gdn_chunk_prefill_noalloc(const void* mixed_qkv, int64_t qkv_row_stride,
+                              const void* a, const void* b,
+                              const float* A_log, const float* dt_bias,
+                              float* state, int32_t num_slots,
+                              const int32_t* ssm_state_indices, const int32_t* lengths,
+                              void* out,
+                              int32_t B, int32_t T, int32_t H, int32_t HV, int32_t K, int32_t V,
+                              int32_t act_dtype, int32_t out_dtype,
+                              float scale, int32_t use_qk_l2norm, float l2norm_eps,
+                              const void* norm_gate, const float* norm_weight,
+                              float norm_eps, int32_t norm_act,
+                              hipStream_t stream);
+
+/*
  * gdn_decode_step_conv -- gdn_decode_step with the causal conv1d update + SiLU
  * of its q, k and v channels fused in front, in one launch (the fused op of
  * [KDA] module docstring and `triton_chain` applied to the GDN step; [LOG]

@@ -11,11 +11,13 @@ from ._binding import (  # noqa: F401
     DTYPE_CODE,
     EXPORTS,
     LIB_PATH,
+    SSMD_CHUNK_SCRATCH_BYTES,
     SsmdError,
     gdn_decode_step,
     gdn_decode_step_buffered,
     gdn_decode_step_conv,
     gdn_chunk_prefill,
+    gdn_chunk_prefill_noalloc,
     gdn_chunk_workspace_bytes,
     gdn_fused_recurrent,
     gdn_decode_step_state16,
@@ -30,6 +32,6 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = ["gdn_decode_step", "gdn_decode_step_state16", "gdn_decode_step_buffered", "gdn_decode_step_conv",
-           "gdn_fused_recurrent", "gdn_chunk_prefill", "gdn_chunk_workspace_bytes",
+           "gdn_fused_recurrent", "gdn_chunk_prefill", "gdn_chunk_prefill_noalloc", "gdn_chunk_workspace_bytes",
            "kda_decode_step", "mamba_decode_step", "mamba_scan", "mamba_scan_workspace_bytes", "ssmd_last_error",
            "ssmd_stream_copy", "SsmdError", "load_library"]

@@ -22,7 +22,7 @@ SSMD_ACT_SILU, SSMD_ACT_SIGMOID = 0, 1
 DTYPE_CODE = {torch.float32: SSMD_F32, torch.bfloat16: SSMD_BF16, torch.float16: SSMD_F16}
 ACT_CODE = {"silu": SSMD_ACT_SILU, "sigmoid": SSMD_ACT_SIGMOID}
 EXPORTS = ("gdn_decode_step", "gdn_decode_step_state16", "gdn_decode_step_buffered", "gdn_decode_step_conv",
-           "gdn_fused_recurrent", "gdn_chunk_prefill", "gdn_chunk_workspace_bytes",
+           "gdn_fused_recurrent", "gdn_chunk_prefill", "gdn_chunk_prefill_noalloc", "gdn_chunk_workspace_bytes",
            "kda_decode_step", "mamba_decode_step", "mamba_scan", "mamba_scan_workspace_bytes", "ssmd_last_error",
            "ssmd_stream_copy", "ssmd_check_slot_indices")
 
@@ -54,6 +54,7 @@ def load_library() -> ctypes.CDLL:
         L.gdn_decode_step_state16.argtypes = _GDN_ARGS[:7] + [_i32] + _GDN_ARGS[7:] + [_p]
         L.gdn_fused_recurrent.argtypes = _GDN_ARGS[:9] + [_p] + _GDN_ARGS[9:11] + [_i32] + _GDN_ARGS[11:] + [_p]
         L.gdn_chunk_prefill.argtypes = L.gdn_fused_recurrent.argtypes[:-1] + [_p, _i64, _p]
+        L.gdn_chunk_prefill_noalloc.argtypes = L.gdn_fused_recurrent.argtypes
         L.gdn_chunk_workspace_bytes.argtypes = [_i32] * 6
         L.gdn_decode_step_conv.argtypes = [_p, _i64, _p, _p, _p, _i64, _i64, _i64, _i32] + _GDN_ARGS[2:] + [_p]
         L.kda_decode_step.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _f, _p, _i32,
@@ -328,6 +329,30 @@ def gdn_chunk_prefill(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices,
         norm_eps, ACT_CODE[norm_act], _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(state, stream))
     _check(rc, "gdn_chunk_prefill")
+    return out
+
+
+# size of the library's static workspace behind gdn_chunk_prefill_noalloc (include/ssmdec.h)
+SSMD_CHUNK_SCRATCH_BYTES = 128 << 20
+
+
+@_one_device
+def gdn_chunk_prefill_noalloc(mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices, out, *, lengths=None,
+                              H=None, scale=None, use_qk_l2norm=True, l2norm_eps=1e-6, norm_gate=None,
+                              norm_weight=None, norm_eps=1e-5, norm_act="silu", stream=None):
+    """gdn_chunk_prefill with the library's static workspace instead of a
+    caller's (for callers that cannot allocate); see
+    gdn_chunk_prefill_noalloc in include/ssmdec.h. Nothing is allocated,
+    here or in the library."""
+    B, T, H, HV, K, V, num_slots, row_stride, act = _gdn_multi_args(
+        mixed_qkv, a, b, A_log, dt_bias, state, ssm_state_indices, out, lengths, H, norm_gate, norm_weight)
+    scale = K ** -0.5 if scale is None else scale
+    rc = load_library().gdn_chunk_prefill_noalloc(
+        _ptr(mixed_qkv), row_stride, _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(state), num_slots,
+        _ptr(ssm_state_indices), _ptr(lengths), _ptr(out), B, T, H, HV, K, V, DTYPE_CODE[act],
+        DTYPE_CODE[out.dtype], scale, int(bool(use_qk_l2norm)), l2norm_eps, _ptr(norm_gate), _ptr(norm_weight),
+        norm_eps, ACT_CODE[norm_act], _stream(state, stream))
+    _check(rc, "gdn_chunk_prefill_noalloc")
     return out
 
 

@@ -28,12 +28,20 @@
 // All arithmetic is fp32 (16-bit inputs enter products exactly); the dense
 // products run on the matrix cores, the diagonal blocks of the inverse on
 // the VALU.
+#include <atomic>
 #include <type_traits>
 
 #include "ssmd_device.h"
 #include "ssmd_internal.h"
 
 namespace ssmd {
+
+// Workspace of gdn_chunk_prefill_noalloc, for callers that cannot allocate:
+// a fixed array in device memory, one per device (each device that loads
+// this code holds its own copy until the process ends), shared by every
+// call on that device. In host code `scratch` only names the symbol; its
+// device address comes from hipGetSymbolAddress (gdn_chunk_scratch below).
+static __device__ __align__(256) unsigned char scratch[SSMD_CHUNK_SCRATCH_BYTES];
 
 constexpr int GCH = 64;  // tokens per chunk
 
@@ -862,6 +870,29 @@ __global__ __launch_bounds__(256) void gdn_chunk_norm_kernel(GdnChunkParams cp) 
     const float w = p.norm_w ? p.norm_w[r] : 1.f;
     store_act1(p.out, base + r, p.out_dt, cp.obuf[base + r] * inv * w * gz);
   }
+}
+
+hipError_t gdn_chunk_scratch(void** ptr) {
+  // device address of `scratch`, looked up once per device with that device
+  // current (concurrent first calls store the same value)
+  static std::atomic<void*> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64) {
+    void* c = cache[dev].load(std::memory_order_acquire);
+    if (c) {
+      *ptr = c;
+      return hipSuccess;
+    }
+  }
+  void* a = nullptr;
+  e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (!a) return hipErrorInvalidSymbol;
+  if (dev >= 0 && dev < 64) cache[dev].store(a, std::memory_order_release);
+  *ptr = a;
+  return hipSuccess;
 }
 
 int64_t gdn_chunk_workspace_floats(int B, int T, int HV, int K, int V, bool norm) {

@@ -350,14 +350,17 @@ int64_t gdn_chunk_workspace_bytes(int32_t B, int32_t T, int32_t HV, int32_t K, i
   return 4 * ssmd::gdn_chunk_workspace_floats(B, T, HV, K, V, with_norm != 0);
 }
 
-int gdn_chunk_prefill(const void* mixed_qkv, int64_t qkv_row_stride, const void* a, const void* b,
-                      const float* A_log, const float* dt_bias, float* state, int32_t num_slots,
-                      const int32_t* ssm_state_indices, const int32_t* lengths, void* out, int32_t B,
-                      int32_t T, int32_t H, int32_t HV, int32_t K, int32_t V, int32_t act_dtype,
-                      int32_t out_dtype, float scale, int32_t use_qk_l2norm, float l2norm_eps,
-                      const void* norm_gate, const float* norm_weight, float norm_eps, int32_t norm_act,
-                      void* workspace, int64_t workspace_bytes, hipStream_t stream) {
-  const char* fn = "gdn_chunk_prefill";
+namespace {
+
+// Body of the two chunked-prefill entry points: `workspace` is the caller's
+// buffer, or (static_ws) NULL, meaning the library's static array.
+int chunk_prefill(const char* fn, const void* mixed_qkv, int64_t qkv_row_stride, const void* a, const void* b,
+                  const float* A_log, const float* dt_bias, float* state, int32_t num_slots,
+                  const int32_t* ssm_state_indices, const int32_t* lengths, void* out, int32_t B, int32_t T,
+                  int32_t H, int32_t HV, int32_t K, int32_t V, int32_t act_dtype, int32_t out_dtype, float scale,
+                  int32_t use_qk_l2norm, float l2norm_eps, const void* norm_gate, const float* norm_weight,
+                  float norm_eps, int32_t norm_act, void* workspace, int64_t workspace_bytes, bool static_ws,
+                  hipStream_t stream) {
   if (T < 0) return fail(SSMD_ERR_BAD_SHAPE, "%s: T = %d < 0", fn, T);
   if (B < 0) return fail(SSMD_ERR_BAD_SHAPE, "%s: B = %d < 0", fn, B);
   const int64_t rows = (int64_t)B * T;
@@ -368,12 +371,27 @@ int gdn_chunk_prefill(const void* mixed_qkv, int64_t qkv_row_stride, const void*
   if (K != 64 && K != 128) return fail(SSMD_ERR_UNSUPPORTED, "%s: K = %d not in {64, 128}", fn, K);
   if (V % 16 || V > 256) return fail(SSMD_ERR_UNSUPPORTED, "%s: V = %d must be a multiple of 16, <= 256", fn, V);
   if (rows == 0) return ok();
-  const int64_t need = 4 * ssmd::gdn_chunk_workspace_floats(B, T, HV, K, V, norm_gate != nullptr);
-  if (!workspace || workspace_bytes < need)
-    return fail(SSMD_ERR_BAD_SHAPE, "%s: workspace of %lld bytes needed (got %lld)", fn, (long long)need,
-                (long long)workspace_bytes);
-  if (!aligned(workspace, 16)) return fail(SSMD_ERR_BAD_SHAPE, "%s: workspace must be 16-byte aligned", fn);
   if ((int64_t)B * HV * ((T + 63) / 64) >= (1LL << 31)) return fail(SSMD_ERR_BAD_SHAPE, "%s: too many chunks", fn);
+  const int64_t need = 4 * ssmd::gdn_chunk_workspace_floats(B, T, HV, K, V, norm_gate != nullptr);
+  if (static_ws) {
+    if (need > (int64_t)SSMD_CHUNK_SCRATCH_BYTES)
+      return fail(SSMD_ERR_BAD_SHAPE,
+                  "%s: this call needs %lld bytes of workspace, more than the library's static %lld "
+                  "(B * HV * ceil(T / 64) too large; use gdn_chunk_prefill with a workspace)",
+                  fn, (long long)need, (long long)SSMD_CHUNK_SCRATCH_BYTES);
+  } else {
+    if (!workspace || workspace_bytes < need)
+      return fail(SSMD_ERR_BAD_SHAPE, "%s: workspace of %lld bytes needed (got %lld)", fn, (long long)need,
+                  (long long)workspace_bytes);
+    if (!aligned(workspace, 16)) return fail(SSMD_ERR_BAD_SHAPE, "%s: workspace must be 16-byte aligned", fn);
+  }
+  int n_cu = 0;
+  if (int rc2 = cu_count(&n_cu)) return rc2;
+  if (static_ws) {
+    const hipError_t e = ssmd::gdn_chunk_scratch(&workspace);
+    if (e != hipSuccess)
+      return fail(SSMD_ERR_LAUNCH, "%s: cannot find the static workspace on this device: %s", fn, hipGetErrorString(e));
+  }
   ssmd::GdnChunkParams cp{};
   cp.g = gdn_params(mixed_qkv, qkv_row_stride, a, b, A_log, dt_bias, state, num_slots, ssm_state_indices, out, B,
                     H, HV, K, V, act_dtype, out_dtype, scale, use_qk_l2norm, l2norm_eps, norm_gate, norm_weight,
@@ -383,9 +401,35 @@ int gdn_chunk_prefill(const void* mixed_qkv, int64_t qkv_row_stride, const void*
   cp.nck = (T + 63) / 64;
   cp.ws = static_cast<float*>(workspace);
   cp.obuf = norm_gate ? cp.ws + (ssmd::gdn_chunk_workspace_floats(B, T, HV, K, V, false)) : nullptr;
-  int n_cu = 0;
-  if (int rc2 = cu_count(&n_cu)) return rc2;
   return launch_status(ssmd::launch_gdn_chunk(cp, n_cu, stream), fn);
+}
+
+}  // namespace
+
+int gdn_chunk_prefill(const void* mixed_qkv, int64_t qkv_row_stride, const void* a, const void* b,
+                      const float* A_log, const float* dt_bias, float* state, int32_t num_slots,
+                      const int32_t* ssm_state_indices, const int32_t* lengths, void* out, int32_t B,
+                      int32_t T, int32_t H, int32_t HV, int32_t K, int32_t V, int32_t act_dtype,
+                      int32_t out_dtype, float scale, int32_t use_qk_l2norm, float l2norm_eps,
+                      const void* norm_gate, const float* norm_weight, float norm_eps, int32_t norm_act,
+                      void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  return chunk_prefill("gdn_chunk_prefill", mixed_qkv, qkv_row_stride, a, b, A_log, dt_bias, state, num_slots,
+                       ssm_state_indices, lengths, out, B, T, H, HV, K, V, act_dtype, out_dtype, scale,
+                       use_qk_l2norm, l2norm_eps, norm_gate, norm_weight, norm_eps, norm_act, workspace,
+                       workspace_bytes, false, stream);
+}
+
+int gdn_chunk_prefill_noalloc(const void* mixed_qkv, int64_t qkv_row_stride, const void* a, const void* b,
+                              const float* A_log, const float* dt_bias, float* state, int32_t num_slots,
+                              const int32_t* ssm_state_indices, const int32_t* lengths, void* out, int32_t B,
+                              int32_t T, int32_t H, int32_t HV, int32_t K, int32_t V, int32_t act_dtype,
+                              int32_t out_dtype, float scale, int32_t use_qk_l2norm, float l2norm_eps,
+                              const void* norm_gate, const float* norm_weight, float norm_eps, int32_t norm_act,
+                              hipStream_t stream) {
+  return chunk_prefill("gdn_chunk_prefill_noalloc", mixed_qkv, qkv_row_stride, a, b, A_log, dt_bias, state,
+                       num_slots, ssm_state_indices, lengths, out, B, T, H, HV, K, V, act_dtype, out_dtype, scale,
+                       use_qk_l2norm, l2norm_eps, norm_gate, norm_weight, norm_eps, norm_act, nullptr, 0, true,
+                       stream);
 }
 
 int kda_decode_step(const void* x, const float* conv_weight, const float* conv_bias, void* conv_state,

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ssmdec.h"
+
 namespace ssmd {
 
 struct GdnParams {
@@ -160,6 +162,9 @@ hipError_t launch_gdn_conv_pf(const GdnConvParams& p, int64_t blocks, hipStream_
 hipError_t launch_gdn_multi(const GdnMultiParams& p, const Launch& l, int n_cu, hipStream_t s);
 hipError_t launch_gdn_chunk(const GdnChunkParams& p, int n_cu, hipStream_t s);
 int64_t gdn_chunk_workspace_floats(int B, int T, int HV, int K, int V, bool norm);
+// Device address of the chunked prefill's static workspace on the current
+// device (SSMD_CHUNK_SCRATCH_BYTES bytes).
+hipError_t gdn_chunk_scratch(void** ptr);
 // Largest V the multi-token kernel takes with the gated RMSNorm (one block per head).
 int gdn_multi_max_norm_rows(int K);
 hipError_t launch_mamba(const MambaParams& p, const Launch& l, hipStream_t s);

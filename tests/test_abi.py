@@ -312,3 +312,20 @@ def test_product_path_is_independent_of_the_oracle():
             "B._LIB = None\ntry:\n    B.load_library()\nexcept RuntimeError as e:\n    print('raised', e)")
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120)
     assert "raised" in r.stdout and "no non-HIP fallback" in r.stdout, r.stdout + r.stderr
+
+
+def test_chunk_prefill_noalloc_host_validation():
+    """The static-workspace prefill refuses a call whose records would not fit
+    its SSMD_CHUNK_SCRATCH_BYTES array (checked before any HIP call), and
+    otherwise validates like gdn_chunk_prefill."""
+    L = S.load_library()
+
+    def call(B=1, T=8192, H=1, HV=32, K=64, V=64):
+        return L.gdn_chunk_prefill_noalloc(0x10000, 2 * H * K + HV * V, 0x20000, 0x30000, 0x40000, 0x50000,
+                                           0x60000, 4, 0x70000, None, 0x80000, B, T, H, HV, K, V, 1, 0, 0.125, 1,
+                                           1e-6, None, None, 1e-5, 0, None)
+    assert S.gdn_chunk_workspace_bytes(1, 8192, 32, 64, 64) > S.SSMD_CHUNK_SCRATCH_BYTES
+    assert call() == BAD_SHAPE
+    assert "static" in S.ssmd_last_error()
+    assert call(K=32) == UNSUPPORTED
+    assert call(T=0) == OK
