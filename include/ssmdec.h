@@ -144,12 +144,15 @@ int gdn_decode_step_state16(const void* mixed_qkv, int64_t qkv_row_stride,
  *   g_cache [num_slots, HV, L]    fp32       -- that step's log decay g
  * The call computes this step's output exactly as gdn_decode_step would from
  * the state S_{p-1} obtained by replaying records 0..p-1 on the checkpoint
- * (S <- exp(g_j) S + d_j k_j^T), appends this step's record at position p
- * (delta and k rounded RNE to act_dtype, g as fp32), and, only when
- * p == L-1, writes the folded state S_p back to `state`. write_pos is read
- * only: the caller advances it to (p + 1) % L between calls. With L == 1 the
- * call computes what gdn_decode_step computes. Ring entries past p are
- * don't-care; a zeroed ring with write_pos = 0 is a cold start.
+ * (S <- exp(g_j) S + d_j k_j^T). For p < L-1 it appends this step's record
+ * at position p (delta and k rounded RNE to act_dtype, g as fp32) and
+ * leaves `state` as it is; for p == L-1 it writes the folded state S_p back
+ * to `state` and appends no record (the next cycle starts at position 0, so
+ * a record at L-1 would never be read). write_pos is read only: the caller
+ * advances it to (p + 1) % L between calls. With L == 1 the call computes
+ * what gdn_decode_step computes. Ring entries past p, and the whole ring
+ * after a flush, are don't-care; a zeroed ring with write_pos = 0 is a cold
+ * start.
  * All other arguments are those of gdn_decode_step.
  */
 int gdn_decode_step_buffered(const void* mixed_qkv, int64_t qkv_row_stride,

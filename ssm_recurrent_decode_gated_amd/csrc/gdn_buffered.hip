@@ -77,7 +77,12 @@ __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tile
   float* cg = ca + pos;
   float* rk = cg + pos;
   float* rq = rk + rows_per_tile;
-  __shared__ float o_lds[NORM ? 1024 : 1];
+  // this tile's outputs and deltas, written out as contiguous runs at the end
+  // (scattered 2-byte stores inside a read-only stream cost far more than
+  // their bytes); a tile has at most 256 rows without the norm, V <= 1024
+  // with it
+  __shared__ float o_lds[NORM ? 1024 : 256];
+  __shared__ float d_lds[NORM ? 1024 : 256];
   __shared__ float red_lds[1];
 
   // ---- small loads first (activations, then this cycle's ring records
@@ -300,9 +305,11 @@ __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tile
       delta[i] = beta * (vv[i] - decay * sk);
       const float o = decay * sqv + delta[i] * kq;
       if (row < r1 && c == 0) {
-        st_act<ACT>(p.d_cache, dw + row, delta[i]);
-        if constexpr (NORM) o_lds[row] = o;
+        // a flush streams the state out anyway: its outputs go straight out
+        // (the norm epilogue needs them in LDS); non-flush steps stage theirs
+        if (NORM || !flush) o_lds[row - r0] = o;
         else store_act1(p.out, obase + row, p.out_dt, o);
+        d_lds[row - r0] = delta[i];
       }
     }
     if (flush) {
@@ -346,18 +353,26 @@ __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tile
     for (int i = 0; i < RG; ++i) load_group(pass, i);
   }
 
-  // ---- append this step's key (once per q/k head) and g
-  if (tile == 0 && hv % G == 0 && wave == 0 && rr == 0) {
-    const int64_t kw = kr_g + (int64_t)pos * K;
+  // ---- this step's record at position p: delta (this tile's rows), the key
+  // (once per q/k head) and g. A flush appends none: the next cycle starts at
+  // position 0, and a record at L-1 would never be read.
+  if (!flush) {  // uniform over the block
+    __syncthreads();
+    // outputs (without the norm: the norm epilogue writes them) and this
+    // step's delta record, in one pass
+    const StoreRun ro{p.out, obase + r0, p.out_dt, o_lds, NORM ? 0 : r1 - r0};
+    const StoreRun rd{p.d_cache, dw + r0, ACT, d_lds, r1 - r0};
+    store_runs(ro, rd, tid, bd);
+    if (tile == 0 && hv % G == 0 && wave == 0 && rr == 0) {
+      const int64_t kw = kr_g + (int64_t)pos * K;
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) st_act<ACT>(p.k_cache, kw + RL::col(c, j) + e, kf[4 * j + e]);
+      for (int j = 0; j < NV; ++j) store4(p.k_cache, kw + RL::col(c, j), ACT, &kf[4 * j]);
+    }
+    if (tile == 0 && tid == 0) p.g_cache[((int64_t)slot * p.HV + hv) * p.L + pos] = g;
   }
-  if (tile == 0 && tid == 0) p.g_cache[((int64_t)slot * p.HV + hv) * p.L + pos] = g;
 
   if constexpr (NORM) {
-    __syncthreads();
+    if (flush) __syncthreads();  // (non-flush steps passed one above)
     if (wave == 0) {
       float ss = 0.f;
       for (int r = lane; r < V; r += 64) ss += o_lds[r] * o_lds[r];
@@ -370,8 +385,10 @@ __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tile
       const float z = ld_act<ACT>(p.norm_gate, obase + r);
       const float gz = p.norm_act == SSMD_ACT_SIGMOID ? sigmoid_f(z) : silu_f(z);
       const float w = p.norm_w ? p.norm_w[r] : 1.f;
-      store_act1(p.out, obase + r, p.out_dt, o_lds[r] * inv * w * gz);
+      o_lds[r] = o_lds[r] * inv * w * gz;
     }
+    __syncthreads();
+    store_runs(StoreRun{p.out, obase, p.out_dt, o_lds, V}, StoreRun{p.out, obase, p.out_dt, o_lds, 0}, tid, bd);
   }
 }
 

@@ -11,6 +11,7 @@
 namespace ssmd {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------- conversions
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
@@ -118,6 +119,91 @@ __device__ __forceinline__ void st_act(void* base, int64_t off, float v) {
   else static_cast<uint16_t*>(base)[off] = f32_to_f16_bits(v);
 }
 
+// A run of n consecutive fp32 values src[0..n) (in LDS or registers) bound
+// for base[off .. off + n) in dtype dt.
+struct StoreRun {
+  void* base;
+  int64_t off;
+  int dt;
+  const float* src;
+  int n;
+};
+
+// One 16-byte piece of a run: `per` values from sv to q, converted to dt.
+__device__ __forceinline__ void store_piece16(void* q, int dt, const float* sv) {
+  if (dt == SSMD_F32) {
+    *reinterpret_cast<f4*>(q) = f4{sv[0], sv[1], sv[2], sv[3]};
+  } else {
+    u4 w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t lo = dt == SSMD_BF16 ? f32_to_bf16_bits(sv[2 * k]) : f32_to_f16_bits(sv[2 * k]);
+      const uint32_t hi = dt == SSMD_BF16 ? f32_to_bf16_bits(sv[2 * k + 1]) : f32_to_f16_bits(sv[2 * k + 1]);
+      w[k] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u4*>(q) = w;
+  }
+}
+
+// Unaligned head and tail of a run as element stores; returns the byte
+// address of its first 16-byte-aligned element and the number of 16-byte
+// pieces after it (head elements come first).
+__device__ __forceinline__ char* run_edges(const StoreRun& r, int tid, int bd, int* head, int* nvec) {
+  const int esz = r.dt == SSMD_F32 ? 4 : 2;
+  char* d = static_cast<char*>(r.base) + r.off * esz;
+  *head = min(r.n, (int)(((16 - ((uintptr_t)d & 15)) & 15) / esz));
+  *nvec = (r.n - *head) / (16 / esz);
+  const int tail0 = *head + *nvec * (16 / esz);
+  for (int e = tid; e < *head; e += bd) store_act1(r.base, r.off + e, r.dt, r.src[e]);
+  for (int e = tail0 + tid; e < r.n; e += bd) store_act1(r.base, r.off + e, r.dt, r.src[e]);
+  return d + (int64_t)*head * esz;
+}
+
+// Writes two runs, spread over a block's threads (tid of bd): their
+// 16-byte-aligned parts as 16-byte stores in one combined pass (both runs'
+// pieces issued together), the unaligned head and tail of each as element
+// stores. Runs written this way reach memory as whole lines instead of
+// scattered 2-byte pieces, which inside a read-only stream cost far more
+// than their bytes. A run with n = 0 writes nothing.
+__device__ __forceinline__ void store_runs(const StoreRun& a, const StoreRun& b, int tid, int bd) {
+  int ha, na, hb, nb;
+  char* const da = run_edges(a, tid, bd, &ha, &na);
+  char* const db = run_edges(b, tid, bd, &hb, &nb);
+  const int pa = a.dt == SSMD_F32 ? 4 : 8, pb = b.dt == SSMD_F32 ? 4 : 8;  // values per piece
+  for (int v = tid; v < na + nb; v += bd) {
+    const bool first = v < na;
+    const int i = first ? v : v - na;
+    const int per = first ? pa : pb;
+    char* const q = (first ? da : db) + (int64_t)i * 16;
+    const float* const sv = (first ? a.src + ha : b.src + hb) + i * per;
+    store_piece16(q, first ? a.dt : b.dt, sv);
+  }
+}
+
+// Stores 4 consecutive fp32 values to base[off .. off + 4) in dtype dt from
+// one lane: one 8-byte (16-bit types) or 16-byte (fp32) store where aligned,
+// element stores otherwise.
+__device__ __forceinline__ void store4(void* base, int64_t off, int dt, const float v[4]) {
+  if (dt == SSMD_F32) {
+    float* d = static_cast<float*>(base) + off;
+    if (((uintptr_t)d & 15) == 0) {
+      *reinterpret_cast<f4*>(d) = f4{v[0], v[1], v[2], v[3]};
+      return;
+    }
+  } else {
+    uint16_t* d = static_cast<uint16_t*>(base) + off;
+    if (((uintptr_t)d & 7) == 0) {
+      uint32_t h[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) h[k] = dt == SSMD_BF16 ? f32_to_bf16_bits(v[k]) : f32_to_f16_bits(v[k]);
+      *reinterpret_cast<uint2*>(d) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      return;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) store_act1(base, off + k, dt, v[k]);
+}
+
 // ------------------------------------------------------------- math
 __device__ __forceinline__ float softplus_f(float x) { return x > 20.f ? x : log1pf(expf(x)); }
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
@@ -182,8 +268,6 @@ struct RowLayout16 {
   static constexpr int RPI = 64 / LPR;                  // rows per wave-wide access
   __device__ static __forceinline__ int col(int c, int j) { return EV * (c + LPR * j); }
 };
-
-typedef unsigned int u4 __attribute__((ext_vector_type(4)));
 
 template <bool NT>
 __device__ __forceinline__ u4 ld16x8(const void* p) {

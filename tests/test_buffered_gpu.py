@@ -116,10 +116,12 @@ def _single_call_case(case, ring_offset=0, act="bf16"):
     G = HV // H
     for b in range(B):
         s, p = int(idx[b]), phases[b]
-        if p == L - 1:
+        if p == L - 1:  # a flush writes the folded state and appends no record
             assert_mixed(got_st[s], ref_st[s], FP32_TOL, f"flushed state row {b}")
-        else:
-            assert torch.equal(got_st[s], st[s]), f"non-flush row {b} wrote the checkpoint"
+            for k in ring0:
+                np.testing.assert_array_equal(got[k][s], ring0[k][s], err_msg=f"{k} row {b} (flush)")
+            continue
+        assert torch.equal(got_st[s], st[s]), f"non-flush row {b} wrote the checkpoint"
         assert_rounded16(got["d_cache"][s, :, p], ref_ring["d_cache"][s, :, p], f"delta record row {b}",
                        ex_ring["d_cache"][s, :, p], mant)
         assert_rounded16(got["k_cache"][s, :, p], ref_ring["k_cache"][s, :, p], f"key record row {b}",
@@ -253,10 +255,12 @@ def test_buffered_many_rows_with_padding(K, V, HV, L):
     ring0 = {k: v.double().numpy() for k, v in ring.items()}
     for b in live:
         s, p = int(idx[b]), phases[b]
-        if p == L - 1:
+        if p == L - 1:  # a flush writes the folded state and appends no record
             assert_mixed(got_st[s], ref_st[s], FP32_TOL, f"flushed state row {b}")
-        else:
-            assert torch.equal(got_st[s], st[s]), f"non-flush row {b} wrote the checkpoint"
+            for k in ring0:
+                np.testing.assert_array_equal(got[k][s], ring0[k][s], err_msg=f"{k} row {b} (flush)")
+            continue
+        assert torch.equal(got_st[s], st[s]), f"non-flush row {b} wrote the checkpoint"
         assert_rounded16(got["d_cache"][s, :, p], ref_ring["d_cache"][s, :, p], f"delta record row {b}",
                        ex_ring["d_cache"][s, :, p])
         assert_rounded16(got["k_cache"][s, :, p], ref_ring["k_cache"][s, :, p], f"key record row {b}",

@@ -124,12 +124,15 @@ def test_random_gdn_buffered(i):
     _check(o, ro, live, f"case {i} ({w.name}, L {L}, norm {norm}) output")
     got_st = st_d.cpu()
     got = {k: to_np64(v) for k, v in ring_d.items()}
+    ring0 = {k: to_np64(v) for k, v in ring.items()}
     for b in live:
         s, p = int(idx[b]), phases[b]
-        if p == L - 1:
+        if p == L - 1:  # a flush writes the folded state and appends no record
             assert_mixed(got_st[s], ref[s], FP32_TOL, f"case {i} flushed slot {s}")
-        else:
-            assert torch.equal(got_st[s], st[s]), f"case {i}: non-flush slot {s} written"
+            for k in ring0:
+                np.testing.assert_array_equal(got[k][s], ring0[k][s], err_msg=f"case {i} {k} slot {s} (flush)")
+            continue
+        assert torch.equal(got_st[s], st[s]), f"case {i}: non-flush slot {s} written"
         for k in ("d_cache", "k_cache"):
             if w.act == "f32":
                 assert_mixed(got[k][s][:, p], rr[k][s][:, p], FP32_TOL, f"case {i} {k} row {b}")
