@@ -8,13 +8,19 @@ the 256 MB Infinity Cache cannot hold the state between steps.
 
 The same JSON line also carries the latency-to-bandwidth sweep (B = 1, 16,
 64, 256 under HIP-graph replay of one call per pool), the buffered variant
-(B=64, L = 1/8/16, exact cycle mean), the fused KDA step (T=64, 96 heads),
+against the packed step (B = 16, 64, 256; L = 1/8/16, exact cycle mean), the
+fused KDA step (T=64, 96 heads, and one TP-8 rank's 12 heads),
 the conv-fused GDN step, the 16-bit-state step, Mamba-1 decode and prefill
 scan, the multi-token GDN call, the chunked and sequential GDN prefill, a
 same-size stream-copy ceiling, the roofline entry of the dominant kernel and
 the fp64 oracle's rate on the host cores.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle S] [--no-cpu-baseline]
+                  [--batch-sizes 16 64 256] [--ls 1 8 16]     # the buffered legs
+  python bench.py --replay-table [--batch-sizes 1 16 64 256] [--ls 1 8 16] [--hv 32] [--h 16] [--k 128]
+                  [--v 128] [--dtype bf16|fp16|fp32]          # the ReplaySSM page's packed-vs-buffered table
+  python bench.py --kda-table [--tokens 1 8 32 64 128] [--heads 12] [--layout SD|DS] [--graph]
+                  [--layers N]                                # the fused-KDA page's table
   python bench.py --profile-pass [gdn|kda|chunk|buffered|conv|state16|multi]   # rocprofv3 counter passes
   python bench.py --summarize-counters FETCH_DIR WRITE_DIR --kernel gdn|kda --out profiles/X.txt
   python bench.py --summarize-trace TRACE_DIR --title T --command C --out profiles/X.md
@@ -135,7 +141,15 @@ def graph_time_us(calls, reps, stream):
 
 
 # ------------------------------------------------------------ legs
-def headline(dev, steps, warmup):
+def headline(dev, steps, warmup, settle_s=0.3):
+    """The B=256-of-264 packed step, eager launches over rotated pools.
+
+    After any idle period (here: the host-side input generation) the first
+    ~60 launches run in a power-management transient: on MI355X launches
+    10-40 after idle read 192-201 us against 185-186 us at steady state. So
+    the W + K steps are first run straight after setup (reported as the cold
+    sample), then the step runs untimed for `settle_s` seconds, then W
+    warm-up steps and the K timed steps (the value)."""
     import torch
     import workloads as W
     w = W.GDN_B256
@@ -143,17 +157,29 @@ def headline(dev, steps, warmup):
     M = _pools_for(pool_bytes)
     su = GDNSetup(w, M, dev)
     stream = torch.cuda.current_stream()
-    for i in range(warmup):
-        su.call(i)
     torch.cuda.synchronize()
-    it = iter(range(10 ** 9))
-    ms = _events_ms(lambda: su.call(next(it)), steps, stream)
+
+    def sample():
+        for i in range(warmup):
+            su.call(i)
+        torch.cuda.synchronize()
+        it = iter(range(10 ** 9))
+        ms = _events_ms(lambda: su.call(next(it)), steps, stream)
+        torch.cuda.synchronize()
+        return ms * 1e3 / steps
+    cold = sample()
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:
+        su.call(n)
+        n += 1
+        if n % 64 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
-    us = ms * 1e3 / steps
+    us = sample()
     sb = gdn_state_bytes(w.B, w.HV, w.V, w.K)
     ab = gdn_alg_bytes(w.B, w.H, w.HV, w.K, w.V)
     return {"w": w, "pools": M, "us": us, "state_gbs": sb / us / 1e3, "alg_gbs": ab / us / 1e3,
-            "alg_bytes": ab, "state_bytes": sb, "setup": su}
+            "alg_bytes": ab, "state_bytes": sb, "setup": su, "cold_us": cold, "settle_steps": n}
 
 
 def state16(dev, steps=200, warmup=10):
@@ -235,52 +261,66 @@ def copy_ceiling(dev, nbytes=2 * 2 ** 30, reps=20):
     return {"bytes_moved_per_copy": 2 * nbytes, "GBps": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
 
 
-def buffered(dev, Ls=(1, 8, 16), reps=30):
+def buffered(dev, batches=(16, 64, 256), Ls=(1, 8, 16), reps=30, H=16, HV=32, K=128, V=128, act="bf16"):
+    """The buffered step (gdn_decode_step_buffered) against the packed one at
+    each batch size, the ReplaySSM page's comparison: per L, the exact mean
+    of a full L-phase cycle (a graph holding phases 0..L-1 on every pool, so
+    no cycle-mean estimate is needed), the non-flush phases 0 and (L-1)/2 and
+    the flush phase L-1, the speed-up over the packed step (graph replay of
+    the same pools) and the page's state-traffic ratio (1 + 1/L) / 2."""
     import torch
     import ssm_recurrent_decode_gated_amd as S
     import workloads as W
-    w = W.GDN_B64_CHAIN
-    pool_bytes = w.num_slots * w.HV * w.V * w.K * 4
-    M = _pools_for(pool_bytes)
-    su = GDNSetup(w, M, dev)
+    tdt = W.DTYPES[act]
     out = {}
-    for L in Ls:
-        rings = [{"d": torch.zeros(w.num_slots, w.HV, L, w.V, dtype=torch.bfloat16, device=dev),
-                  "k": torch.zeros(w.num_slots, w.H, L, w.K, dtype=torch.bfloat16, device=dev),
-                  "g": torch.zeros(w.num_slots, w.HV, L, device=dev)} for _ in range(M)]
-        wps = [torch.full((w.B,), p, dtype=torch.int32, device=dev) for p in range(L)]
+    for B in batches:
+        w = W.GDNWorkload(f"gdn_b{B}_h{H}_hv{HV}_k{K}_v{V}_{act}", B=B, H=H, HV=HV, K=K, V=V, num_slots=B,
+                          act=act)
+        pool_bytes = w.num_slots * w.HV * w.V * w.K * 4
+        M = _pools_for(pool_bytes)
+        su = GDNSetup(w, M, dev)
+        packed = graph_time_us([lambda i=i: su.call(i) for i in range(M)], reps, torch.cuda.current_stream())
+        res = {"packed_us": round(packed, 3), "pools": M}
+        for L in Ls:
+            rings = [{"d": torch.zeros(w.num_slots, w.HV, L, w.V, dtype=tdt, device=dev),
+                      "k": torch.zeros(w.num_slots, w.H, L, w.K, dtype=tdt, device=dev),
+                      "g": torch.zeros(w.num_slots, w.HV, L, device=dev)} for _ in range(M)]
+            wps = [torch.full((w.B,), p, dtype=torch.int32, device=dev) for p in range(L)]
 
-        def call(i, p):
-            r = rings[i]
-            S.gdn_decode_step_buffered(su.qkv, su.a, su.b, su.A_log, su.dt_bias, su.pools[i], su.idx_d,
-                                       su.out, r["d"], r["k"], r["g"], wps[p])
-        # one cycle on every pool: L launches per pool, phases 0..L-1 in order
-        calls = [lambda i=i, p=p: call(i, p) for p in range(L) for i in range(M)]
-        us = graph_time_us(calls, reps, torch.cuda.current_stream())
-        per_phase = {}
-        for p in sorted({0, (L - 1) // 2, L - 1}):
-            per_phase[p] = round(graph_time_us([lambda i=i, p=p: call(i, p) for i in range(M)], reps,
-                                               torch.cuda.current_stream()), 3)
-        state_b = w.B * w.HV * w.V * w.K * 4 * (1 + 1.0 / L)
-        out[f"L{L}"] = {"cycle_mean_us": round(us, 3), "phase_us": per_phase,
-                        "state_GBps": round(state_b / us / 1e3, 1),
-                        "state_bytes_ratio_vs_packed": round((1 + 1.0 / L) / 2, 5)}
-        del rings
-    del su
-    torch.cuda.empty_cache()
+            def call(i, p):
+                r = rings[i]
+                S.gdn_decode_step_buffered(su.qkv, su.a, su.b, su.A_log, su.dt_bias, su.pools[i], su.idx_d,
+                                           su.out, r["d"], r["k"], r["g"], wps[p])
+            # one cycle on every pool: L launches per pool, phases 0..L-1 in order
+            calls = [lambda i=i, p=p: call(i, p) for p in range(L) for i in range(M)]
+            us = graph_time_us(calls, reps, torch.cuda.current_stream())
+            per_phase = {}
+            for p in sorted({0, (L - 1) // 2, L - 1}):
+                per_phase[p] = round(graph_time_us([lambda i=i, p=p: call(i, p) for i in range(M)], reps,
+                                                   torch.cuda.current_stream()), 3)
+            state_b = w.B * w.HV * w.V * w.K * 4 * (1 + 1.0 / L)
+            res[f"L{L}"] = {"cycle_mean_us": round(us, 3), "phase_us": per_phase,
+                            "speedup_vs_packed": round(packed / us, 3),
+                            "state_GBps": round(state_b / us / 1e3, 1),
+                            "state_bytes_ratio_vs_packed": round((1 + 1.0 / L) / 2, 5)}
+            del rings
+        out[f"B{B}"] = res
+        del su
+        torch.cuda.empty_cache()
     return out
 
 
-def kda(dev, reps=30, w=None):
-    """The fused KDA op at T = 64 tokens x 96 heads; with `w`, another shape
-    (one tensor-parallel rank's 12 heads)."""
+def kda_time(dev, w, layout="SD", graph=True, layers=None, reps=30):
+    """One fused KDA decode call (kda_decode_step) at workload w: graph replay
+    of one call per layer (each layer its own state and conv-state buffers,
+    `layers` of them, by default enough to exceed the Infinity Cache), or,
+    without `graph`, the same calls launched one by one."""
     import torch
     import ssm_recurrent_decode_gated_amd as S
     import workloads as W
-    w = w or W.KDA_T64
-    d = W.kda_inputs(w)
+    d = W.kda_inputs(w, layout=layout)
     pool_bytes = w.num_slots * w.H * w.D * w.D * 4
-    M = _pools_for(pool_bytes)
+    M = layers or _pools_for(pool_bytes)
     first = d["state"].to(dev)
     pools = [first] + [first.clone() for _ in range(M - 1)]
     cs = [d["conv_state"].to(dev) for _ in range(M)]
@@ -290,18 +330,29 @@ def kda(dev, reps=30, w=None):
     def call(i):
         S.kda_decode_step(dd["x"], dd["conv_weight"], None, cs[i], dd["raw_g"], dd["raw_beta"], None, None,
                           pools[i], dd["idx"], out, output_gate=dd["gate"], norm_weight=dd["norm_weight"])
-    us = graph_time_us([lambda i=i: call(i) for i in range(M)], reps, torch.cuda.current_stream())
+    if graph:
+        us = graph_time_us([lambda i=i: call(i) for i in range(M)], reps, torch.cuda.current_stream())
+    else:
+        for i in range(M):
+            call(i)
+        it = iter(range(10 ** 9))
+        us = _events_ms(lambda: call(next(it) % M), M * reps, torch.cuda.current_stream()) * 1e3 / (M * reps)
     sb = w.T * w.H * w.D * w.D * 4 * 2
     ab = kda_alg_bytes(w)
     del pools, cs
     torch.cuda.empty_cache()
-    res = {"workload": w.name, "us_per_step": round(us, 3), "state_GBps": round(sb / us / 1e3, 1),
-           "pct_hbm_peak": round(100 * sb / us / 1e3 / HBM_PEAK_GBS, 2), "alg_GBps": round(ab / us / 1e3, 1),
-           "pct_hbm_peak_alg": round(100 * ab / us / 1e3 / HBM_PEAK_GBS, 2), "pools": M}
-    if w is W.KDA_T64:
-        # one rank's share when the 96 heads are split over 8 GPUs: the same
-        # kernel at 12 heads (the step has no exchange between heads)
-        res["tp8_rank_h12"] = kda(dev, reps, W.KDAWorkload("kda_t64_h12_d128_w4", T=64, H=12, num_slots=72))
+    return {"workload": w.name, "us_per_step": round(us, 3), "state_GBps": round(sb / us / 1e3, 1),
+            "pct_hbm_peak": round(100 * sb / us / 1e3 / HBM_PEAK_GBS, 2), "alg_GBps": round(ab / us / 1e3, 1),
+            "pct_hbm_peak_alg": round(100 * ab / us / 1e3 / HBM_PEAK_GBS, 2), "layers": M,
+            "timing": "graph replay" if graph else "eager dispatch", "layout": layout}
+
+
+def kda(dev, reps=30):
+    """The fused KDA op at T = 64 tokens x 96 heads, and one tensor-parallel
+    rank's share (12 heads: the step has no exchange between heads)."""
+    import workloads as W
+    res = kda_time(dev, W.KDA_T64, reps=reps)
+    res["tp8_rank_h12"] = kda_time(dev, W.KDAWorkload("kda_t64_h12_d128_w4", T=64, H=12, num_slots=72), reps=reps)
     return res
 
 
@@ -505,6 +556,27 @@ def cpu_baseline(su, target_s=10.0, single_s=5.0):
                               "us_per_step": round(el1 / n1 * 1e6, 1), "steps": n1},
             "sample": f"full B=256-of-264 step (H=16, HV=32, K=V=128) repeated {n} times in {el:.1f} s on "
                       f"{cores} threads, then {n1} times in {el1:.1f} s on one; fp32-state byte model"}
+
+
+TRACE_FILE = os.path.join(ROOT, "profiles", "gdn_b256_of264_kernel_trace.md")
+
+
+def trace_kernel_avg_us():
+    """The headline kernel's average duration in the committed rocprofv3
+    kernel-trace summary, or None when the kernel source changed since."""
+    if not os.path.exists(TRACE_FILE):
+        return None
+    text = open(TRACE_FILE).read()
+    if f"kernel_source_sha256 = {kernel_source_hash()}" not in text:
+        return None
+    for line in text.splitlines():
+        if line.startswith("|") and KERNEL_NAME in line:
+            cells = [c.strip() for c in line.strip("|").split("|")]
+            try:
+                return round(float(cells[3]) / 1e3, 3)
+            except (IndexError, ValueError):
+                return None
+    return None
 
 
 def counters_traffic():
@@ -714,8 +786,11 @@ def summarize_trace(trace_dir, out, command, title):
     rows = list(csv.DictReader(open(files[0])))
     cols = ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"]
     lines = [f"# {title}", "", "Command (run from /tmp on the MI355X, `<repo>` = repository root):", "",
-             f"    {command}", "", "`run_kernel_stats.csv`:", "", "| " + " | ".join(cols) + " |",
-             "|" + "---|" * len(cols)]
+             f"    {command}", ""]
+    if any(KERNEL_NAME in r["Name"] for r in rows):
+        lines += [f"kernel_source_sha256 = {kernel_source_hash()} ({KERNEL_NAME} source at the time of the run)",
+                  ""]
+    lines += ["`run_kernel_stats.csv`:", "", "| " + " | ".join(cols) + " |", "|" + "---|" * len(cols)]
     for r in rows:
         name = r["Name"]
         if len(name) > 160:  # torch's generated template names; the head names the kernel
@@ -727,12 +802,69 @@ def summarize_trace(trace_dir, out, command, title):
     print("\n".join(lines))
 
 
+def replay_table(dev, args):
+    """The ReplaySSM page's table (its `main`): per batch size the packed
+    step, then per L the buffered cycle mean split into its non-flush and
+    flush steps, the speed-up and the state-traffic ratio. Times in ms, as
+    the page prints them."""
+    act = {"bf16": "bf16", "fp16": "f16", "fp32": "f32"}[args.dtype]
+    print(f"GDN buffered decode HV={args.hv} H={args.h} K={args.k} V={args.v} dtype={args.dtype}\n"
+          "replay = exact mean per-step latency over one L-phase cycle (ms; graph replay, pools rotated past "
+          "the Infinity Cache); speedup = packed/replay; state-traffic = replay/packed", flush=True)
+    for B in args.batch_sizes:
+        r = buffered(dev, batches=(B,), Ls=tuple(args.ls), H=args.h, HV=args.hv, K=args.k, V=args.v,
+                     act=act)[f"B{B}"]
+        print(f"\nB={B:<4d} packed={r['packed_us'] / 1e3:.4f} ms")
+        for L in args.ls:
+            x = r[f"L{L}"]
+            ph = x["phase_us"]
+            split = "(flush only)" if L == 1 else \
+                f"(non-flush {ph[(L - 1) // 2] / 1e3:.4f}, flush {ph[L - 1] / 1e3:.4f})"
+            print(f"  L={L:<3d} replay={x['cycle_mean_us'] / 1e3:.4f} ms speedup={x['speedup_vs_packed']:5.2f}x "
+                  f"state-traffic={x['state_bytes_ratio_vs_packed']:5.2f}x {split}", flush=True)
+
+
+def kda_table(dev, args):
+    """The fused-KDA page's table (its `main`): per head count and token
+    count, the fused op's time and its state TB/s."""
+    import workloads as W
+    mode = "graph replay" if args.graph else "eager dispatch"
+    print(f"device: {__import__('torch').cuda.get_device_name(0)} timing: {mode} layout: {args.layout}")
+    print(f"{'heads':>6} {'tokens':>7} {'fused us':>9} {'state TB/s':>11} {'all TB/s':>9} {'layers':>7}", flush=True)
+    for H in args.heads:
+        for T in args.tokens:
+            w = W.KDAWorkload(f"kda_t{T}_h{H}_d128_w4", T=T, H=H, num_slots=T + 8, layout=args.layout)
+            r = kda_time(dev, w, layout=args.layout, graph=args.graph, layers=args.layers)
+            print(f"{H:>6} {T:>7} {r['us_per_step']:>9.2f} {r['state_GBps'] / 1e3:>11.3f} "
+                  f"{r['alg_GBps'] / 1e3:>9.3f} {r['layers']:>7}", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds the headline step runs untimed before its warm-up (leaves the post-idle "
+                         "power-management transient)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--replay-table", action="store_true", help="print the ReplaySSM page's table and exit")
+    ap.add_argument("--kda-table", action="store_true", help="print the fused-KDA page's table and exit")
+    ap.add_argument("--batch-sizes", type=int, nargs="+", default=None,
+                    help="buffered legs (default 16 64 256) / --replay-table rows (default 1 16 64 256)")
+    ap.add_argument("--ls", type=int, nargs="+", default=[1, 8, 16], help="buffered ring lengths")
+    ap.add_argument("--hv", type=int, default=32)
+    ap.add_argument("--h", type=int, default=16)
+    ap.add_argument("--k", type=int, default=128)
+    ap.add_argument("--v", type=int, default=128)
+    ap.add_argument("--dtype", choices=("bf16", "fp16", "fp32"), default="bf16")
+    ap.add_argument("--tokens", type=int, nargs="+", default=[1, 8, 32, 64, 128])
+    ap.add_argument("--heads", type=int, nargs="+", default=[12])
+    ap.add_argument("--layout", choices=("SD", "DS"), default="SD")
+    ap.add_argument("--graph", action="store_true", help="--kda-table: graph replay instead of eager dispatch")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="--kda-table: layers (state buffers) per graph; default: enough to exceed the "
+                         "Infinity Cache")
     ap.add_argument("--no-extras", action="store_true", help="headline only (no sweep/buffered/KDA/conv/Mamba/copy)")
     ap.add_argument("--profile-pass", nargs="?", const="gdn",
                     choices=("gdn", "kda", "chunk", "buffered", "conv", "state16", "multi"))
@@ -765,12 +897,22 @@ def main():
     torch.cuda.set_device(dev)
     import ssm_recurrent_decode_gated_amd as S
     S.load_library()
+    if args.replay_table:
+        args.batch_sizes = args.batch_sizes or [1, 16, 64, 256]
+        replay_table(dev, args)
+        return
+    if args.kda_table:
+        kda_table(dev, args)
+        return
 
     torch.cuda.synchronize()
-    h = headline(dev, args.steps, args.warmup)
+    h = headline(dev, args.steps, args.warmup, args.settle)
     torch.cuda.synchronize()
-    print(f"[bench] headline done: {h['us']:.1f} us/step", file=sys.stderr, flush=True)
-    extra = {"eager_us_per_step": round(h["us"], 3)}
+    print(f"[bench] headline done: {h['us']:.1f} us/step (cold sample {h['cold_us']:.1f})", file=sys.stderr,
+          flush=True)
+    extra = {"eager_us_per_step": round(h["us"], 3),
+             "cold_start_us_per_step": round(h["cold_us"], 3),
+             "settle_steps_before_warmup": h["settle_steps"]}
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(h["setup"])
@@ -778,15 +920,19 @@ def main():
     del h["setup"]
     torch.cuda.empty_cache()
     if not args.no_extras:
-        for key, leg in (("graph_sweep", sweep), ("copy_ceiling", copy_ceiling), ("buffered_b64", buffered),
+        bsz = tuple(args.batch_sizes or (16, 64, 256))
+        for key, leg in (("graph_sweep", sweep), ("copy_ceiling", copy_ceiling),
+                         ("buffered", lambda d: buffered(d, batches=bsz, Ls=tuple(args.ls))),
                          ("kda_t64_h96", kda), ("gdn_conv_b256", gdn_conv), ("mamba1", mamba), ("mamba1_prefill", mamba_prefill), ("gdn_multi_token", gdn_multi), ("gdn_prefill", gdn_prefill),
                          ("state16_b256", state16)):
             extra[key] = leg(dev)
             print(f"[bench] {key} done", file=sys.stderr, flush=True)
         extra["state16_b256"]["speedup_vs_fp32_state"] = round(h["us"] / extra["state16_b256"]["us_per_step"], 3)
         extra["pct_of_copy_ceiling"] = round(100 * h["state_gbs"] / extra["copy_ceiling"]["GBps"], 2)
+        extra["graph_replay_us_per_step_B256"] = extra["graph_sweep"]["B256"]["us_per_step"]
     w = h["w"]
     traffic = counters_traffic()
+    trace_us = trace_kernel_avg_us()
     line = {
         "metric": METRIC,
         "value": round(h["state_gbs"], 2),
@@ -805,8 +951,15 @@ def main():
         "config": {"workload": w.name, "B": w.B, "num_slots": w.num_slots, "H": w.H, "HV": w.HV, "K": w.K,
                    "V": w.V, "act_dtype": w.act, "out_dtype": w.out, "state_dtype": "f32",
                    "state_pools_rotated": h["pools"], "parallelism": "single GPU"},
+        "timing": ("eager launches, one gdn_decode_step per step over rotated state pools; HIP events around "
+                   "the K timed steps after a settle period and W warm-up steps (extra.cold_start_us_per_step: "
+                   "the same K steps straight after setup); graph replay of the same calls in "
+                   "extra.graph_replay_us_per_step_B256"),
         "roofline": {"bound": "hbm", "achieved": round(h["alg_gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(h["alg_gbs"] / HBM_PEAK_GBS, 4),
+                     "kernel_avg_us_rocprofv3": trace_us,
+                     "frac_at_rocprofv3_kernel_avg": None if trace_us is None else
+                     round(h["alg_bytes"] / trace_us / 1e3 / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic),
                      "algorithmic_bytes_per_launch": h["alg_bytes"], "kernel": KERNEL_NAME},
         "cpu_baseline": cpu,
