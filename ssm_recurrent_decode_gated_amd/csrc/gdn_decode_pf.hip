@@ -1,16 +1,16 @@
-// gdn_decode_pf.hip -- packed GDN decode (no output norm): persistent blocks
-// that prefetch the next work unit's state while the current one is computed
-// and stored. Same arithmetic and row layout as gdn_decode.hip.
+// gdn_decode_pf.hip -- packed GDN decode (no output norm). Same arithmetic
+// and row layout as gdn_decode.hip. Blocks walk work units (batch row, value
+// head, row tile) with a grid stride, each wave holding the next unit's
+// state pass in registers while it computes and stores the current one.
 //
-// Launch shape (measured on MI355X, B = 256, HV = 32, K = V = 128): one
-// 4-wave block per CU, each wave holding the state pass of two work units
-// (this one and the next), streams at 5.68 TB/s, against 5.45 TB/s for one
-// block per unit with every pass in flight at once and 5.63 TB/s for the best
-// plain copy kernel. Fewer concurrent streams with continuous prefetch keep
-// the HBM busier than many short-lived blocks; the grid must match the CU
-// count exactly (a few blocks more or fewer leaves CUs with twice the work).
-// Small batches, with at most two units per CU, launch one block per unit
-// instead (see the launcher).
+// Launch shape (measured on MI355X, HV = 32, K = V = 128; see the
+// launcher): at large batches one 4-wave block per 32-row tile, one row
+// group per wave, so every block is a single short read-then-write burst
+// (B = 256: 177 us, 6.06 TB/s of state). In-place streams on this part run
+// faster the less each block and wave holds: many short bursts in flight at
+// once keep HBM busier than a few long ones (a plain in-place copy: 5.6 TB/s
+// with 64 KB per block, 6.3 with 8 KB, 6.6 with 4 KB). Small batches, with at
+// most two full-height units per CU, launch one block per 128-row unit.
 #include "ssmd_device.h"
 #include "ssmd_internal.h"
 
@@ -164,6 +164,21 @@ template <int K, int ACT, bool VEC>
 hipError_t launch_pf_k(const GdnParams& p, const Launch& l, int n_cu, hipStream_t st) {
   constexpr int RG = pf_rg<K>();
   if (l.fixed) return launch_pf_rg<K, ACT, VEC, RG>(p, l.wpb, l.grid_cap > 0 ? l.grid_cap : n_cu, st);
+  auto units_for = [&](int w, int rg) {
+    const int rpt = w * rg * RowLayout<K>::RPI;
+    return (int64_t)p.B * p.HV * ((p.V + rpt - 1) / rpt);
+  };
+  // Large batches (more than two full-height units per CU): one 4-wave block
+  // per tile of 4 x RPI rows, one row group (8 rows of K = 64/128) per wave,
+  // no walk. Many short read-then-write bursts in flight at once keep HBM
+  // busier than a few long streams: at B = 256 (HV = 32, K = V = 128) 177 us,
+  // against 185.5 us for the persistent walk below (32 rows per wave, one
+  // block per CU) and 190.6 us for 16-row waves; B = 64: 46.4 us against
+  // 49.9. The persistent walk at one row group per wave measured 197-272 us,
+  // so small tiles go with one block each.
+  if constexpr (RG > 1) {
+    if (units_for(4, RG) > 2LL * n_cu) return launch_pf_rg<K, ACT, VEC, 1>(p, 4, units_for(4, 1), st);
+  }
   // Small batches (measured at HV = 32, K = V = 128): narrower blocks until
   // every CU has a unit, then, if even 1-wave blocks leave CUs idle, half the
   // rows per wave (B = 1: 4.1 us against 4.7 with 32-row units and 5.5 with
@@ -171,10 +186,6 @@ hipError_t launch_pf_k(const GdnParams& p, const Launch& l, int n_cu, hipStream_
   // while that is at most two per CU (B = 16: 12.5 us against 13.9
   // persistent); beyond that one persistent block per CU (B = 64: 50.2 us
   // against 52.1 with one block per unit).
-  auto units_for = [&](int w, int rg) {
-    const int rpt = w * rg * RowLayout<K>::RPI;
-    return (int64_t)p.B * p.HV * ((p.V + rpt - 1) / rpt);
-  };
   auto grid_for = [&](int64_t u) { return u <= 2LL * n_cu ? u : (int64_t)n_cu; };
   if constexpr (RG >= 2) {
     if (units_for(1, RG) < n_cu) return launch_pf_rg<K, ACT, VEC, RG / 2>(p, 1, grid_for(units_for(1, RG / 2)), st);
