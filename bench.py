@@ -123,12 +123,21 @@ class GDNSetup:
                           self.idx_d, self.out)
 
 
-def graph_time_us(calls, reps, stream):
-    """us per call for a HIP graph holding `calls` (one launch each), replayed."""
+GRAPH_MIN_CALLS = 64
+
+
+def graph_time_us(calls, reps, stream, min_calls=GRAPH_MIN_CALLS):
+    """us per call for a HIP graph holding `calls` (one launch each), replayed.
+    The list is repeated in order until the graph holds at least `min_calls`
+    launches, as a model step captures all its layers in one graph: a graph
+    launch costs about 20 us on this runtime and does not overlap the previous
+    replay, so a 2-call graph would charge 10 us to every call. Repeating the
+    list keeps its pool rotation (and each pool's phase order)."""
     import torch
     for c in calls:  # warm (and first-touch) outside the capture
         c()
     torch.cuda.synchronize()
+    calls = list(calls) * max(1, -(-min_calls // len(calls)))
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for c in calls:
@@ -236,7 +245,7 @@ def sweep(dev, batches=(1, 16, 64, 256), reps=50):
             # a graph holding one call, replayed: what one graph launch costs
             # when nothing amortises it (the page's one-call KDA graph)
             res["B1"]["one_call_graph_us"] = round(
-                graph_time_us([lambda: su.call(0)], reps, torch.cuda.current_stream()), 3)
+                graph_time_us([lambda: su.call(0)], reps, torch.cuda.current_stream(), min_calls=1), 3)
         if pool_bytes <= MALL_BYTES // 2:
             # one pool stepped over and over: its state stays in the Infinity
             # Cache, so this is a cache rate, not an HBM one

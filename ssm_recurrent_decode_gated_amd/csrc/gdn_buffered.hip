@@ -30,11 +30,10 @@ constexpr int buf_rg() {
   return K == 16 ? 1 : (K == 32 ? 2 : (K == 256 ? 2 : 4));
 }
 
-template <int K, bool NORM, int ACT, bool VEC>
+template <int K, bool NORM, int ACT, bool VEC, int RG>
 __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tiles_per_head,
                                                            int rows_per_tile) {
   using RL = RowLayout<K>;
-  constexpr int RG = buf_rg<K>();
   constexpr int LPR = RL::LPR, NV = RL::NV, RPI = RL::RPI, ROWS = RG * RPI;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -43,11 +42,8 @@ __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tile
   const int c = lane % LPR;
   const int rr = lane / LPR;
 
-  int bid = blockIdx.x;
-  const int tile = bid % tiles_per_head;
-  bid /= tiles_per_head;
-  const int hv = bid % p.HV;
-  const int bi = bid / p.HV;
+  int bi, hv, tile;
+  xcd_unit(blockIdx.x, p.B, p.H, p.HV, tiles_per_head, bi, hv, tile);
   const int slot = p.idx[bi];
   const int pos = p.write_pos[bi];
   if (slot < 0 || slot >= p.num_slots || pos < 0 || pos >= p.L) return;  // padded row
@@ -394,10 +390,10 @@ __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tile
 
 namespace {
 
-template <int K, bool NORM, int ACT, bool VEC>
-hipError_t launch_bk(const GdnParams& p, const Launch& l, hipStream_t st) {
+template <int K, bool NORM, int ACT, bool VEC, int RG>
+hipError_t launch_bk_rg(const GdnParams& p, const Launch& l, hipStream_t st) {
   constexpr int RPI = RowLayout<K>::RPI;
-  const int wave_rows = buf_rg<K>() * RPI;
+  const int wave_rows = RG * RPI;
   int wpb = l.wpb;
   int tiles, rows_per_tile;
   if (NORM) {
@@ -411,8 +407,16 @@ hipError_t launch_bk(const GdnParams& p, const Launch& l, hipStream_t st) {
   if (wpb > need) wpb = need;
   const size_t lds = buffered_lds_bytes(K, rows_per_tile, p.L);
   const dim3 grid((unsigned)((int64_t)p.B * p.HV * tiles));
-  gdn_buffered_kernel<K, NORM, ACT, VEC><<<grid, dim3(64 * wpb), lds, st>>>(p, tiles, rows_per_tile);
+  gdn_buffered_kernel<K, NORM, ACT, VEC, RG><<<grid, dim3(64 * wpb), lds, st>>>(p, tiles, rows_per_tile);
   return hipGetLastError();
+}
+
+// Full-height tiles: smaller ones (64 rows) measured a faster flush phase
+// (B = 64, L = 8: 50.0 against 54.0 us) but slower non-flush phases (every
+// tile repeats the ring staging and record dots), a slower cycle overall.
+template <int K, bool NORM, int ACT, bool VEC>
+hipError_t launch_bk(const GdnParams& p, const Launch& l, hipStream_t st) {
+  return launch_bk_rg<K, NORM, ACT, VEC, buf_rg<K>()>(p, l, st);
 }
 
 template <int K, bool NORM>

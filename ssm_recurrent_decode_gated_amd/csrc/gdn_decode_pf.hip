@@ -39,31 +39,10 @@ __global__ __launch_bounds__(512) void gdn_decode_pf_kernel(GdnParams p, int til
     float qf[NV * 4], kf[NV * 4], vv[RG], av, bv, A_log, dt_bias;
     f4 s[RG][NV];
   };
-  // Unit -> (batch row, value head, row tile), XCD-aware: the G * tiles
-  // units that share one q/k head (its G value heads, all their tiles) get
-  // unit indices that are equal mod 8, and workgroups go to the 8 XCDs round
-  // robin, so they run on one XCD and read that head's q and k from its L2
-  // rather than from HBM once per XCD. Groups past the last whole set of 8
-  // map in order.
-  const int G = p.HV / p.H;
-  const int n_share = G * tiles_per_head;
-  const int n_groups = p.B * p.H;
-  const int64_t in_sets = (int64_t)(n_groups / 8) * 8 * n_share;
   auto fetch = [&](int unit, Unit& U) {
-    int gi, m;
-    if (unit < in_sets) {
-      const int sx = unit >> 3;
-      gi = (sx / n_share) * 8 + (unit & 7);
-      m = sx % n_share;
-    } else {
-      const int r = unit - (int)in_sets;
-      gi = (n_groups / 8) * 8 + r / n_share;
-      m = r % n_share;
-    }
-    const int tile = m % tiles_per_head;
-    U.bi = gi / p.H;
-    U.h = gi - U.bi * p.H;
-    U.hv = U.h * G + m / tiles_per_head;
+    int tile;
+    xcd_unit(unit, p.B, p.H, p.HV, tiles_per_head, U.bi, U.hv, tile);
+    U.h = U.hv / (p.HV / p.H);
     U.slot = p.idx[U.bi];
     if (U.slot < 0 || U.slot >= p.num_slots) return;
     U.r0 = tile * rows_per_tile;

@@ -9,9 +9,9 @@
 // e^g S + delta k is rounded (RNE) once, when it is stored. The step's own
 // output comes from the unrounded row.
 //
-// Launch structure of gdn_decode_pf.hip (persistent blocks, here two per CU
-// by default, each wave holding the next unit's state pass while it computes
-// the current one). A row of K 16-bit values is spread over LPR lanes with
+// Launch structure: persistent blocks, two per CU by default, each wave
+// holding the next unit's state pass while it computes the current one;
+// units in XCD-aware order (xcd_unit). A row of K 16-bit values is spread over LPR lanes with
 // 128-bit accesses of 8 elements. With the gated-RMSNorm epilogue on, a unit
 // is a whole head: the block walks all V rows (the first pass prefetched),
 // keeps o in LDS and reduces across waves.
@@ -25,11 +25,10 @@ constexpr int s16_rg() {  // row groups per wave pass: 32 rows at K = 64/128
   return K == 16 ? 1 : (K == 32 ? 2 : (K == 256 ? 2 : 4));
 }
 
-template <int K, int ST, int ACT, bool VEC, bool NORM>
+template <int K, int ST, int ACT, bool VEC, bool NORM, int RG>
 __global__ __launch_bounds__(512) void gdn_decode_s16_kernel(GdnParams p, int tiles_per_head,
                                                              int rows_per_tile, int n_units) {
   using RL = RowLayout16<K>;
-  constexpr int RG = s16_rg<K>();
   constexpr int EV = RL::EV, LPR = RL::LPR, NV = RL::NV, RPI = RL::RPI, ROWS = RG * RPI;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -47,11 +46,8 @@ __global__ __launch_bounds__(512) void gdn_decode_s16_kernel(GdnParams p, int ti
     u4 s[RG][NV];  // first pass of state rows, packed
   };
   auto fetch = [&](int unit, Unit& U) {
-    int bid = unit;
-    const int tile = bid % tiles_per_head;
-    bid /= tiles_per_head;
-    U.hv = bid % p.HV;
-    U.bi = bid / p.HV;
+    int tile;
+    xcd_unit(unit, p.B, p.H, p.HV, tiles_per_head, U.bi, U.hv, tile);
     U.slot = p.idx[U.bi];
     if (U.slot < 0 || U.slot >= p.num_slots) return;
     U.h = U.hv / (p.HV / p.H);
@@ -194,9 +190,9 @@ __global__ __launch_bounds__(512) void gdn_decode_s16_kernel(GdnParams p, int ti
 
 namespace {
 
-template <int K, int ST, int ACT, bool VEC, bool NORM>
-hipError_t launch_s16_k(const GdnParams& p, const Launch& l, int n_cu, hipStream_t st) {
-  const int wave_rows = s16_rg<K>() * RowLayout16<K>::RPI;
+template <int K, int ST, int ACT, bool VEC, bool NORM, int RG>
+hipError_t launch_s16_rg(const GdnParams& p, const Launch& l, int n_cu, hipStream_t st) {
+  const int wave_rows = RG * RowLayout16<K>::RPI;
   int wpb = l.wpb;
   int tiles, rows_per_tile;
   if (NORM) {
@@ -214,9 +210,18 @@ hipError_t launch_s16_k(const GdnParams& p, const Launch& l, int n_cu, hipStream
   // (measured at B = 256: 111 us with 2 blocks per CU, 139 us with 1)
   const int64_t cap = l.grid_cap > 0 ? l.grid_cap : 2 * (int64_t)n_cu;
   const int64_t blocks = units < cap ? units : cap;
-  gdn_decode_s16_kernel<K, ST, ACT, VEC, NORM><<<dim3((unsigned)blocks), dim3(64 * wpb), 0, st>>>(
+  gdn_decode_s16_kernel<K, ST, ACT, VEC, NORM, RG><<<dim3((unsigned)blocks), dim3(64 * wpb), 0, st>>>(
       p, tiles, rows_per_tile, (int)units);
   return hipGetLastError();
+}
+
+// Unlike the fp32 step, this one measured slower with one block per small
+// tile (B = 256: 158 us with 8 rows per wave, 110 us with 16, against 106 us
+// for the walk below): half the bytes per row leave the per-unit chain (slot
+// index, then state) less to hide behind.
+template <int K, int ST, int ACT, bool VEC, bool NORM>
+hipError_t launch_s16_k(const GdnParams& p, const Launch& l, int n_cu, hipStream_t st) {
+  return launch_s16_rg<K, ST, ACT, VEC, NORM, s16_rg<K>()>(p, l, n_cu, st);
 }
 
 template <int K, int ST, bool NORM>

@@ -240,6 +240,34 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// ------------------------------------------------------------- unit order
+// Work unit -> (batch row bi, value head hv, row tile), XCD-aware: the
+// G * tiles units that share one q/k head (its G = HV/H value heads, all
+// their tiles) get unit indices that are equal mod 8. Workgroups go to the 8
+// XCDs round robin, so with one block per unit they run on one XCD and read
+// that head's q and k from its L2 rather than from HBM once per XCD. Groups
+// past the last whole set of 8 map in order. A bijection for any B, H, HV,
+// tiles.
+__device__ __forceinline__ void xcd_unit(int unit, int B, int H, int HV, int tiles, int& bi, int& hv, int& tile) {
+  const int G = HV / H;
+  const int n_share = G * tiles;
+  const int n_groups = B * H;
+  const int in_sets = (n_groups / 8) * 8 * n_share;
+  int gi, m;
+  if (unit < in_sets) {
+    const int sx = unit >> 3;
+    gi = (sx / n_share) * 8 + (unit & 7);
+    m = sx % n_share;
+  } else {
+    const int r = unit - in_sets;
+    gi = (n_groups / 8) * 8 + r / n_share;
+    m = r % n_share;
+  }
+  tile = m % tiles;
+  bi = gi / H;
+  hv = (gi - bi * H) * G + m / tiles;
+}
+
 // ------------------------------------------------------------- row layout
 // A head's state is V rows of K fp32 (row = value index). A row is split
 // over LPR lanes; lane c of a row owns the float4 columns c, c+LPR, c+2*LPR,
