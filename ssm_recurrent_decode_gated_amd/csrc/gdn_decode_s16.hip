@@ -9,12 +9,13 @@
 // e^g S + delta k is rounded (RNE) once, when it is stored. The step's own
 // output comes from the unrounded row.
 //
-// Launch structure: persistent blocks, two per CU by default, each wave
-// holding the next unit's state pass while it computes the current one;
-// units in XCD-aware order (xcd_unit). A row of K 16-bit values is spread over LPR lanes with
-// 128-bit accesses of 8 elements. With the gated-RMSNorm epilogue on, a unit
-// is a whole head: the block walks all V rows (the first pass prefetched),
-// keeps o in LDS and reduces across waves.
+// Launch structure: at large batches one 4-wave block per row tile holding a
+// single unit (WALK = false); otherwise persistent blocks, two per CU, each
+// wave holding the next unit's state pass while it computes the current one.
+// Units go in XCD-aware order (xcd_unit). A row of K 16-bit values is spread
+// over LPR lanes with 128-bit accesses of 8 elements. With the gated-RMSNorm
+// epilogue on, a unit is a whole head: the block walks all V rows (the first
+// pass prefetched), keeps o in LDS and reduces across waves.
 #include "ssmd_device.h"
 #include "ssmd_internal.h"
 
@@ -25,7 +26,7 @@ constexpr int s16_rg() {  // row groups per wave pass: 32 rows at K = 64/128
   return K == 16 ? 1 : (K == 32 ? 2 : (K == 256 ? 2 : 4));
 }
 
-template <int K, int ST, int ACT, bool VEC, bool NORM, int RG>
+template <int K, int ST, int ACT, bool VEC, bool NORM, int RG, bool WALK>
 __global__ __launch_bounds__(512) void gdn_decode_s16_kernel(GdnParams p, int tiles_per_head,
                                                              int rows_per_tile, int n_units) {
   using RL = RowLayout16<K>;
@@ -174,17 +175,25 @@ __global__ __launch_bounds__(512) void gdn_decode_s16_kernel(GdnParams p, int ti
     }
   };
 
-  Unit A, B;
-  int u = blockIdx.x;
-  const int gs = gridDim.x;
-  if (u < n_units) fetch(u, A);
-  while (u < n_units) {
-    if (u + gs < n_units) fetch(u + gs, B);
-    process(A);
-    if (u + gs >= n_units) break;
-    if (u + 2 * gs < n_units) fetch(u + 2 * gs, A);
-    process(B);
-    u += 2 * gs;
+  if constexpr (!WALK) {
+    Unit A;
+    for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
+      fetch(u, A);
+      process(A);
+    }
+  } else {
+    Unit A, B;
+    int u = blockIdx.x;
+    const int gs = gridDim.x;
+    if (u < n_units) fetch(u, A);
+    while (u < n_units) {
+      if (u + gs < n_units) fetch(u + gs, B);
+      process(A);
+      if (u + gs >= n_units) break;
+      if (u + 2 * gs < n_units) fetch(u + 2 * gs, A);
+      process(B);
+      u += 2 * gs;
+    }
   }
 }
 
@@ -210,18 +219,44 @@ hipError_t launch_s16_rg(const GdnParams& p, const Launch& l, int n_cu, hipStrea
   // (measured at B = 256: 111 us with 2 blocks per CU, 139 us with 1)
   const int64_t cap = l.grid_cap > 0 ? l.grid_cap : 2 * (int64_t)n_cu;
   const int64_t blocks = units < cap ? units : cap;
-  gdn_decode_s16_kernel<K, ST, ACT, VEC, NORM, RG><<<dim3((unsigned)blocks), dim3(64 * wpb), 0, st>>>(
+  gdn_decode_s16_kernel<K, ST, ACT, VEC, NORM, RG, true><<<dim3((unsigned)blocks), dim3(64 * wpb), 0, st>>>(
       p, tiles, rows_per_tile, (int)units);
   return hipGetLastError();
 }
 
-// Unlike the fp32 step, this one measured slower with one block per small
-// tile (B = 256: 158 us with 8 rows per wave, 110 us with 16, against 106 us
-// for the walk below): half the bytes per row leave the per-unit chain (slot
-// index, then state) less to hide behind.
+// One block of 4 waves per tile of 4 x RG x RPI rows, no walk: the kernel
+// holds a single unit, so its registers admit five waves per SIMD, and the
+// hardware dispatcher refills each CU as its blocks finish.
+template <int K, int ST, int ACT, bool VEC, int RG>
+hipError_t launch_s16_tiles(const GdnParams& p, int64_t units, int rows_per_tile, int tiles, hipStream_t st) {
+  const int wave_rows = RG * RowLayout16<K>::RPI;
+  const int wpb = (min(p.V, rows_per_tile) + wave_rows - 1) / wave_rows;
+  gdn_decode_s16_kernel<K, ST, ACT, VEC, false, RG, false><<<dim3((unsigned)units), dim3(64 * wpb), 0, st>>>(
+      p, tiles, rows_per_tile, (int)units);
+  return hipGetLastError();
+}
+
+// Large batches (more than four 4-wave tiles per CU): one block per tile of
+// half the walk's rows per wave. Measured on MI355X at HV = 32, K = V = 128,
+// bf16 state, same session: B = 256 94.2 us against 103.9 us for the walk
+// (5.77 TB/s), B = 64 27.3 against 28.8. With no compute at all the walk's
+// loads and stores take 100 us at B = 256: its limit is how its two units per
+// wave issue, not the arithmetic. A third block per CU for the walk, or a
+// capped grid-stride loop over single units (102 us), measured slower. Small
+// batches keep the walk (B = 16: 8.3 against 9.2 us): with few tiles, its
+// register use, two blocks per CU, spreads them evenly over the CUs.
 template <int K, int ST, int ACT, bool VEC, bool NORM>
 hipError_t launch_s16_k(const GdnParams& p, const Launch& l, int n_cu, hipStream_t st) {
-  return launch_s16_rg<K, ST, ACT, VEC, NORM, s16_rg<K>()>(p, l, n_cu, st);
+  constexpr int RG = s16_rg<K>();
+  if constexpr (!NORM) {
+    constexpr int RG1 = RG / 2 > 1 ? RG / 2 : 1;
+    const int rows_per_tile = 4 * RG1 * RowLayout16<K>::RPI;
+    const int tiles = (p.V + rows_per_tile - 1) / rows_per_tile;
+    const int64_t units = (int64_t)p.B * p.HV * tiles;
+    if (!l.fixed && units > 4LL * n_cu)
+      return launch_s16_tiles<K, ST, ACT, VEC, RG1>(p, units, rows_per_tile, tiles, st);
+  }
+  return launch_s16_rg<K, ST, ACT, VEC, NORM, RG>(p, l, n_cu, st);
 }
 
 template <int K, int ST, bool NORM>

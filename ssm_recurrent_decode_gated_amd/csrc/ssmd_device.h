@@ -325,20 +325,20 @@ __device__ __forceinline__ void unpack8(u4 v, float out[8]) {
   }
 }
 
+// Eight fp32 values to eight 16-bit ones (RNE), two per 32-bit word, low
+// half first. Converting pairs as vectors lets gfx950 round both halves of a
+// word in one v_cvt_pk_bf16_f32 instead of two single conversions and a merge.
 template <int ST>
 __device__ __forceinline__ u4 pack8(const float in[8]) {
+  typedef float f2v __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2v __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2v __attribute__((ext_vector_type(2)));
   u4 v;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    uint32_t lo, hi;
-    if constexpr (ST == SSMD_BF16) {
-      lo = f32_to_bf16_bits(in[2 * w]);
-      hi = f32_to_bf16_bits(in[2 * w + 1]);
-    } else {
-      lo = f32_to_f16_bits(in[2 * w]);
-      hi = f32_to_f16_bits(in[2 * w + 1]);
-    }
-    v[w] = lo | (hi << 16);
+    const f2v x = {in[2 * w], in[2 * w + 1]};
+    if constexpr (ST == SSMD_BF16) v[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, b2v));
+    else v[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, h2v));
   }
   return v;
 }

@@ -101,6 +101,27 @@ def test_state16_shapes(case, sdt):
     _check(w, sdt, out, got, st0, ro, ref, idx, exact)
 
 
+# More row tiles than four per CU on a 256-CU part: these take the launch with
+# one block per tile (no walk), over every head size, ragged V and GQA groups.
+TILE_CASES = [
+    ("k256_v100_gqa4_f16act", 40, 2, 8, 256, 100, 41, "f16", torch.float32),
+    ("k128_v200_gqa2", 12, 4, 8, 128, 200, 13, "bf16", torch.bfloat16),
+    ("k64_v40_gqa16", 70, 1, 16, 64, 40, 72, "bf16", torch.float32),
+    ("k32_v200", 20, 16, 16, 32, 200, 21, "f32", torch.float16),
+    ("k16_v7_gqa8", 130, 1, 8, 16, 7, 131, "bf16", torch.float32),
+]
+
+
+@pytest.mark.parametrize("case", TILE_CASES, ids=[c[0] for c in TILE_CASES])
+@pytest.mark.parametrize("sdt", [torch.bfloat16, torch.float16])
+def test_state16_one_block_per_tile(case, sdt):
+    need_gpu()
+    name, B, H, HV, K, V, slots, act, outd = case
+    w = W.GDNWorkload("s16_tiles_" + name, B=B, H=H, HV=HV, K=K, V=V, num_slots=slots, act=act, idx="perm")
+    out, got, st0, ro, ref, idx, exact = _run(w, sdt, outd)
+    _check(w, sdt, out, got, st0, ro, ref, idx, exact)
+
+
 @pytest.mark.parametrize("V,act_fn", [(128, "silu"), (300, "sigmoid")])
 def test_state16_gated_norm(V, act_fn):
     need_gpu()
