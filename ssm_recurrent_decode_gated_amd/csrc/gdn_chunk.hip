@@ -116,26 +116,26 @@ __device__ __forceinline__ void stg_st4(stg_t<ACT>* p, raw4_t<ACT> v) {
   else *reinterpret_cast<uint2*>(p) = v;
 }
 
-// One 16-index step of a Gram tile from two staged rows (each pointer at
-// column k0 + 4 kk of its lane's row): fp32 storage takes four fp32 MFMAs,
-// 16-bit storage one v_mfma_f32_16x16x16 on the raw words (products of 16-bit
-// values are exact in fp32, so this matches the fp32 product up to summation
-// order).
-typedef short s4v __attribute__((ext_vector_type(4)));
-typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+// gfx950's v_mfma_f32_16x16x32 (bf16 / f16 in, fp32 out): twice the
+// contraction indices of the 16x16x16 form per instruction, at the part's full
+// 16-bit matrix rate. Lane x + 16 kk supplies A[x][k] and B[k][x] for the 8
+// indices k0 + 8 kk .. k0 + 8 kk + 7 (the same element order in A and B, so
+// the sum over them is the contraction) and holds D[4 kk + r][x] in register r,
+// as in the 16x16x16 form.
+typedef __bf16 b8v __attribute__((ext_vector_type(8)));
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 template <int ACT>
-__device__ __forceinline__ f4v gram16(const stg_t<ACT>* a, const stg_t<ACT>* b, f4v c) {
-  if constexpr (ACT == SSMD_F32) {
-    return mma16(ld4s(a), ld4s(b), c);
-  } else {
-    const uint2 ua = *reinterpret_cast<const uint2*>(a), ub = *reinterpret_cast<const uint2*>(b);
-    if constexpr (ACT == SSMD_BF16)
-      return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4v, ua), __builtin_bit_cast(s4v, ub), c,
-                                                        0, 0, 0);
-    else
-      return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4v, ua), __builtin_bit_cast(h4v, ub), c, 0,
-                                                    0, 0);
-  }
+__device__ __forceinline__ f4v mma32(uint4 a, uint4 b, f4v c) {
+  if constexpr (ACT == SSMD_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8v, a), __builtin_bit_cast(b8v, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8v, a), __builtin_bit_cast(h8v, b), c, 0, 0, 0);
+}
+// 8 consecutive 16-bit values from LDS rows whose stride keeps them 8-byte
+// (not 16-byte) aligned: two 64-bit reads.
+__device__ __forceinline__ uint4 ld8h(const uint16_t* p) {
+  const uint2 lo = *reinterpret_cast<const uint2*>(p), hi = *reinterpret_cast<const uint2*>(p + 4);
+  return uint4{lo.x, lo.y, hi.x, hi.y};
 }
 
 // Issues the loads of rows i < n of a [64][L] activation block (row i = element
@@ -274,11 +274,20 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(GdnChunkParams cp) 
     const int ti = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
     const int tj = t - ti * (ti + 1) / 2;
     f4v qk = {0.f, 0.f, 0.f, 0.f}, kkm = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (ACT == SSMD_F32) {
 #pragma unroll 4
-    for (int k0 = 0; k0 < K; k0 += 16) {
-      const ST* bk = Kr + (16 * tj + x) * KS + k0 + 4 * kk;
-      qk = gram16<ACT>(Qr + (16 * ti + x) * KS + k0 + 4 * kk, bk, qk);
-      kkm = gram16<ACT>(Kr + (16 * ti + x) * KS + k0 + 4 * kk, bk, kkm);
+      for (int k0 = 0; k0 < K; k0 += 16) {
+        const ST* bk = Kr + (16 * tj + x) * KS + k0 + 4 * kk;
+        qk = mma16(ld4s(Qr + (16 * ti + x) * KS + k0 + 4 * kk), ld4s(bk), qk);
+        kkm = mma16(ld4s(Kr + (16 * ti + x) * KS + k0 + 4 * kk), ld4s(bk), kkm);
+      }
+    } else {  // raw 16-bit words, 32 indices per instruction
+#pragma unroll
+      for (int k0 = 0; k0 < K; k0 += 32) {
+        const uint4 bk = ld8h(Kr + (16 * tj + x) * KS + k0 + 8 * kk);
+        qk = mma32<ACT>(ld8h(Qr + (16 * ti + x) * KS + k0 + 8 * kk), bk, qk);
+        kkm = mma32<ACT>(ld8h(Kr + (16 * ti + x) * KS + k0 + 8 * kk), bk, kkm);
+      }
     }
     const int j = 16 * tj + x;
     const float gj = gam[j], kj = ksc[j];
@@ -564,8 +573,8 @@ __global__ __launch_bounds__(256) void gdn_chunk_state_kernel(GdnChunkParams cp)
 // rounded to bf16, m the remainder rounded, l the rest (at most 8 significant
 // bits, so exact). A product of a bf16 operand with v is then the sum of three
 // exact bf16 x bf16 products, accumulated in fp32: fp32 accuracy at the bf16
-// matrix-core rate (v_mfma_f32_16x16x16_bf16 covers 16 contraction indices in
-// the time v_mfma_f32_16x16x4_f32 covers 4 at a quarter of the rate).
+// matrix-core rate (v_mfma_f32_16x16x32_bf16 covers 32 contraction indices;
+// v_mfma_f32_16x16x4_f32 covers 4, at a lower rate).
 __device__ __forceinline__ void split3(float v, uint32_t& h, uint32_t& m, uint32_t& l) {
   h = f32_to_bf16_bits(v);
   const float r1 = v - bf16_bits_to_f32(h);
@@ -573,13 +582,10 @@ __device__ __forceinline__ void split3(float v, uint32_t& h, uint32_t& m, uint32
   l = f32_to_bf16_bits(r1 - bf16_bits_to_f32(m));
 }
 
-__device__ __forceinline__ f4v mma_bf16(uint2 a, uint2 b, f4v c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4v, a), __builtin_bit_cast(s4v, b), c, 0, 0,
-                                                    0);
-}
+__device__ __forceinline__ f4v mma_bf16(uint4 a, uint4 b, f4v c) { return mma32<SSMD_BF16>(a, b, c); }
 
-// A (bf16, one lane's 4 values) times B given as three bf16 planes.
-__device__ __forceinline__ f4v mma_x3(uint2 a, uint2 bh, uint2 bm, uint2 bl, f4v c) {
+// A (bf16, one lane's 8 values) times B given as three bf16 planes.
+__device__ __forceinline__ f4v mma_x3(uint4 a, uint4 bh, uint4 bm, uint4 bl, f4v c) {
   c = mma_bf16(a, bl, c);
   c = mma_bf16(a, bm, c);
   return mma_bf16(a, bh, c);
@@ -673,8 +679,8 @@ __global__ __launch_bounds__(256) void gdn_chunk_state_x3_kernel(GdnChunkParams 
     // every global load of the chunk is issued here, before the first wait:
     // raw k (to LDS), the factors, this wave's rows of M and P, its q operands
     // and the v values of its R entries
-    const int64_t qoff = rbase + (int64_t)min(16 * ti + x, n - 1) * p.qkv_stride + (int64_t)h * K + 4 * kk;
-    uint2 qa[K / 16];
+    const int64_t qoff = rbase + (int64_t)min(16 * ti + x, n - 1) * p.qkv_stride + (int64_t)h * K + 8 * kk;
+    uint4 qa[K / 32];
     uint32_t vr[4][NRT];
     f4 mA[4], pA[4];
     {
@@ -690,8 +696,13 @@ __global__ __launch_bounds__(256) void gdn_chunk_state_x3_kernel(GdnChunkParams 
           pA[jb] = ld4s(rec + GCH_P + (16 * ti + x) * GCH + 16 * jb + 4 * kk);
         }
 #pragma unroll
-      for (int m = 0; m < K / 16; ++m)
-        qa[m] = vec ? ld_raw4<SSMD_BF16, true>(p.qkv, qoff + 16 * m) : ld_raw4<SSMD_BF16, false>(p.qkv, qoff + 16 * m);
+      for (int m = 0; m < K / 32; ++m) {
+        const uint2 lo = vec ? ld_raw4<SSMD_BF16, true>(p.qkv, qoff + 32 * m)
+                             : ld_raw4<SSMD_BF16, false>(p.qkv, qoff + 32 * m);
+        const uint2 hi = vec ? ld_raw4<SSMD_BF16, true>(p.qkv, qoff + 32 * m + 4)
+                             : ld_raw4<SSMD_BF16, false>(p.qkv, qoff + 32 * m + 4);
+        qa[m] = uint4{lo.x, lo.y, hi.x, hi.y};
+      }
       const uint16_t* const vq = static_cast<const uint16_t*>(p.qkv);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -714,17 +725,15 @@ __global__ __launch_bounds__(256) void gdn_chunk_state_x3_kernel(GdnChunkParams 
     f4v Y[NRT], Z[NRT];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) Y[rt] = Z[rt] = f4v{0.f, 0.f, 0.f, 0.f};
-    const uint16_t* const krow = Kst + (16 * ti + x) * KS + 4 * kk;
+    const uint16_t* const krow = Kst + (16 * ti + x) * KS + 8 * kk;
 #pragma unroll
-    for (int k0 = 0; k0 < K; k0 += 16) {
-      const uint2 aq = qa[k0 / 16];
-      const uint2 ak = *reinterpret_cast<const uint2*>(krow + k0);
+    for (int k0 = 0; k0 < K; k0 += 32) {
+      const uint4 aq = qa[k0 / 32];
+      const uint4 ak = ld8h(krow + k0);
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
-        const int o = (16 * rt + x) * SB + k0 + 4 * kk;
-        const uint2 bh = *reinterpret_cast<const uint2*>(&Sp[0][o]);
-        const uint2 bm = *reinterpret_cast<const uint2*>(&Sp[1][o]);
-        const uint2 bl = *reinterpret_cast<const uint2*>(&Sp[2][o]);
+        const int o = (16 * rt + x) * SB + k0 + 8 * kk;
+        const uint4 bh = ld8h(&Sp[0][o]), bm = ld8h(&Sp[1][o]), bl = ld8h(&Sp[2][o]);
         Y[rt] = mma_x3(aq, bh, bm, bl, Y[rt]);
         Z[rt] = mma_x3(ak, bh, bm, bl, Z[rt]);
       }
@@ -803,23 +812,22 @@ __global__ __launch_bounds__(256) void gdn_chunk_state_x3_kernel(GdnChunkParams 
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) Sn[q][rt] *= eg;
 #pragma unroll
-    for (int j0 = 0; j0 < GCH; j0 += 16) {
-      const int j = j0 + 4 * kk;
-      uint2 bk[CPW];
+    for (int j0 = 0; j0 < GCH; j0 += 32) {
+      const int j = j0 + 8 * kk;
+      uint4 bk[CPW];
 #pragma unroll
       for (int q = 0; q < CPW; ++q) {
         const int tc = wave + 4 * q;
         if (tc < NCT) {
           const uint16_t* kc = Kst + j * KS + 16 * tc + x;
-          bk[q] = uint2{kc[0] | ((uint32_t)kc[KS] << 16), kc[2 * KS] | ((uint32_t)kc[3 * KS] << 16)};
+          bk[q] = uint4{kc[0] | ((uint32_t)kc[KS] << 16), kc[2 * KS] | ((uint32_t)kc[3 * KS] << 16),
+                        kc[4 * KS] | ((uint32_t)kc[5 * KS] << 16), kc[6 * KS] | ((uint32_t)kc[7 * KS] << 16)};
         }
       }
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
         const int o = (16 * rt + x) * DB + j;
-        const uint2 ah = *reinterpret_cast<const uint2*>(&Dq[0][o]);
-        const uint2 am = *reinterpret_cast<const uint2*>(&Dq[1][o]);
-        const uint2 al = *reinterpret_cast<const uint2*>(&Dq[2][o]);
+        const uint4 ah = ld8h(&Dq[0][o]), am = ld8h(&Dq[1][o]), al = ld8h(&Dq[2][o]);
 #pragma unroll
         for (int q = 0; q < CPW; ++q)
           if (wave + 4 * q < NCT) {
