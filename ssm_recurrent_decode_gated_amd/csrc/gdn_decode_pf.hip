@@ -23,7 +23,10 @@ constexpr int pf_rg() {
   return K == 16 ? 1 : (K == 32 ? 2 : (K == 256 ? 1 : 4));
 }
 
-template <int K, int ACT, bool VEC, int RG>
+// VF: the unit's v values are loaded ahead of its state rows, so the
+// conversion of v waits for nothing but v and each row group is computed and
+// stored as it arrives (used where a CU holds a single 1-wave block).
+template <int K, int ACT, bool VEC, int RG, bool VF>
 __global__ __launch_bounds__(512) void gdn_decode_pf_kernel(GdnParams p, int tiles_per_head,
                                                             int rows_per_tile, int n_units) {
   using RL = RowLayout<K>;
@@ -60,10 +63,15 @@ __global__ __launch_bounds__(512) void gdn_decode_pf_kernel(GdnParams p, int til
     U.A_log = p.A_log[U.hv];
     U.dt_bias = p.dt_bias[U.hv];
     const float* S = static_cast<float*>(p.state) + ((int64_t)U.slot * p.HV + U.hv) * (int64_t)p.V * K;
+    if constexpr (VF) {
+#pragma unroll
+      for (int i = 0; i < RG; ++i)
+        U.vv[i] = ld_act<ACT>(p.qkv, vbase + min(U.r0 + (i * nwaves + wave) * RPI + rr, U.r1 - 1));
+    }
 #pragma unroll
     for (int i = 0; i < RG; ++i) {
       const int row = min(U.r0 + (i * nwaves + wave) * RPI + rr, U.r1 - 1);
-      U.vv[i] = ld_act<ACT>(p.qkv, vbase + row);
+      if constexpr (!VF) U.vv[i] = ld_act<ACT>(p.qkv, vbase + row);
 #pragma unroll
       for (int j = 0; j < NV; ++j) U.s[i][j] = ld4<true>(S + (int64_t)row * K + RL::col(c, j));
     }
@@ -142,7 +150,7 @@ __global__ __launch_bounds__(512) void gdn_decode_pf_kernel(GdnParams p, int til
 
 namespace {
 
-template <int K, int ACT, bool VEC, int RG>
+template <int K, int ACT, bool VEC, int RG, bool VF = false>
 hipError_t launch_pf_rg(const GdnParams& p, int wpb, int64_t cap, hipStream_t st) {
   const int wave_rows = RG * RowLayout<K>::RPI;
   const int rows_per_tile = wpb * wave_rows;
@@ -152,8 +160,8 @@ hipError_t launch_pf_rg(const GdnParams& p, int wpb, int64_t cap, hipStream_t st
   if (wpb > need) wpb = need;
   const int64_t units = (int64_t)p.B * p.HV * tiles;
   const int64_t blocks = units < cap ? units : cap;
-  gdn_decode_pf_kernel<K, ACT, VEC, RG><<<dim3((unsigned)blocks), dim3(64 * wpb), 0, st>>>(p, tiles, rows_per_tile,
-                                                                                        (int)units);
+  gdn_decode_pf_kernel<K, ACT, VEC, RG, VF><<<dim3((unsigned)blocks), dim3(64 * wpb), 0, st>>>(
+      p, tiles, rows_per_tile, (int)units);
   return hipGetLastError();
 }
 
@@ -178,14 +186,17 @@ hipError_t launch_pf_k(const GdnParams& p, const Launch& l, int n_cu, hipStream_
   }
   // Small batches (measured at HV = 32, K = V = 128): narrower blocks until
   // every CU has a unit, then, if even 1-wave blocks leave CUs idle, half the
-  // rows per wave (B = 1: 4.1 us against 4.7 with 32-row units and 5.5 with
-  // 4-wave blocks); one block per unit, all state loads in flight at once,
+  // rows per wave, with v loaded ahead of the state (B = 1: 3.6 us; 4.1 with
+  // v loaded beside each row group, 4.7 with 32-row units and 5.5 with 4-wave
+  // blocks); one block per unit, all state loads in flight at once,
   // while that is at most two per CU (B = 16: 12.5 us against 13.9
-  // persistent); beyond that one persistent block per CU (B = 64: 50.2 us
-  // against 52.1 with one block per unit).
+  // persistent; 2-wave or 1-wave blocks, or v ahead of the state, 12.6-13.1);
+  // beyond that one persistent block per CU (B = 64: 50.2 us against 52.1
+  // with one block per unit).
   auto grid_for = [&](int64_t u) { return u <= 2LL * n_cu ? u : (int64_t)n_cu; };
   if constexpr (RG >= 2) {
-    if (units_for(1, RG) < n_cu) return launch_pf_rg<K, ACT, VEC, RG / 2>(p, 1, grid_for(units_for(1, RG / 2)), st);
+    if (units_for(1, RG) < n_cu)
+      return launch_pf_rg<K, ACT, VEC, RG / 2, true>(p, 1, grid_for(units_for(1, RG / 2)), st);
   }
   int wpb = 4;
   while (wpb > 1 && units_for(wpb, RG) < n_cu) wpb /= 2;
