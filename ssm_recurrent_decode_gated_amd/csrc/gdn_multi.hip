@@ -64,11 +64,8 @@ __global__ __launch_bounds__(512) void gdn_multi_kernel(GdnMultiParams mp) {
   const int c = lane % LPR;
   const int rr = lane / LPR;
 
-  int bid = blockIdx.x;
-  const int tile = bid % mp.tiles;
-  bid /= mp.tiles;
-  const int hv = bid % p.HV;
-  const int bi = bid / p.HV;
+  int bi, hv, tile;
+  xcd_unit(blockIdx.x, p.B, p.H, p.HV, mp.tiles, bi, hv, tile);
   const int slot = p.idx[bi];
   if (slot < 0 || slot >= p.num_slots) return;  // padded row: touch nothing
   const int T = mp.T;
