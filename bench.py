@@ -150,6 +150,21 @@ def graph_time_us(calls, reps, stream, min_calls=GRAPH_MIN_CALLS):
 
 
 # ------------------------------------------------------------ legs
+def _settle(call, seconds):
+    """Runs call(0), call(1), ... untimed for `seconds` (synchronising every 64
+    calls), past the clock ramp that follows any idle period; returns the
+    number of calls."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        call(n)
+        n += 1
+        if n % 64 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def headline(dev, steps, warmup, settle_s=0.3):
     """The B=256-of-264 packed step, eager launches over rotated pools.
 
@@ -177,13 +192,7 @@ def headline(dev, steps, warmup, settle_s=0.3):
         torch.cuda.synchronize()
         return ms * 1e3 / steps
     cold = sample()
-    n, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < settle_s:
-        su.call(n)
-        n += 1
-        if n % 64 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
+    n = _settle(su.call, settle_s)
     us = sample()
     sb = gdn_state_bytes(w.B, w.HV, w.V, w.K)
     ab = gdn_alg_bytes(w.B, w.H, w.HV, w.K, w.V)
@@ -191,9 +200,10 @@ def headline(dev, steps, warmup, settle_s=0.3):
             "alg_bytes": ab, "state_bytes": sb, "setup": su, "cold_us": cold, "settle_steps": n}
 
 
-def state16(dev, steps=200, warmup=10):
+def state16(dev, steps=200, warmup=10, settle_s=0.2):
     """The B=256-of-264 step on a bf16 state pool (gdn_decode_step_state16):
-    half the state bytes of the fp32 step."""
+    half the state bytes of the fp32 step. Eager launches over rotated pools,
+    timed after a settle period as the headline is."""
     import torch
     import ssm_recurrent_decode_gated_amd as S
     import workloads as W
@@ -208,6 +218,7 @@ def state16(dev, steps=200, warmup=10):
 
     def call(i):
         S.gdn_decode_step_state16(su.qkv, su.a, su.b, su.A_log, su.dt_bias, pools[i % M], su.idx_d, su.out)
+    _settle(call, settle_s)
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
