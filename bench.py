@@ -132,7 +132,8 @@ def graph_time_us(calls, reps, stream, min_calls=GRAPH_MIN_CALLS):
     launches, as a model step captures all its layers in one graph: a graph
     launch costs about 20 us on this runtime and does not overlap the previous
     replay, so a 2-call graph would charge 10 us to every call. Repeating the
-    list keeps its pool rotation (and each pool's phase order)."""
+    list keeps its pool rotation (and each pool's phase order). Five warm-up
+    replays, then the median of at least 20 timed replays."""
     import torch
     for c in calls:  # warm (and first-touch) outside the capture
         c()
@@ -142,11 +143,20 @@ def graph_time_us(calls, reps, stream, min_calls=GRAPH_MIN_CALLS):
     with torch.cuda.graph(g):
         for c in calls:
             c()
-    for _ in range(3):
+    for _ in range(5):
         g.replay()
     torch.cuda.synchronize()
-    ms = _events_ms(g.replay, reps, torch.cuda.current_stream())
-    return ms * 1e3 / (reps * len(calls))
+    # one event pair per replay, median over the replays
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(max(reps, 20))]
+    for a, b in ev:
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    n = len(ms)
+    med = ms[n // 2] if n % 2 else 0.5 * (ms[n // 2 - 1] + ms[n // 2])
+    return med * 1e3 / len(calls)
 
 
 # ------------------------------------------------------------ legs
