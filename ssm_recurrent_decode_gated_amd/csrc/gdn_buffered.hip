@@ -25,6 +25,10 @@
 
 namespace ssmd {
 
+// 4-element ring loads per thread in the staging pass issued ahead of the
+// state stream
+constexpr int BUF_RU4 = 2;
+
 template <int K>
 constexpr int buf_rg() {
   return K == 16 ? 1 : (K == 32 ? 2 : (K == 256 ? 2 : 4));
@@ -109,7 +113,7 @@ __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tile
   // and kept raw until the LDS stores, so nothing waits on them before the
   // state stream is issued.
   constexpr bool R16 = ACT != SSMD_F32;
-  constexpr int RU4 = 2;
+  constexpr int RU4 = BUF_RU4;
   const bool rvec = R16 && (((reinterpret_cast<uintptr_t>(p.k_cache) | reinterpret_cast<uintptr_t>(p.d_cache)) & 7) == 0) &&
                     V % 4 == 0 && tr % 4 == 0;
   uint2 kt4[RU4], dt4[RU4];
@@ -411,9 +415,11 @@ hipError_t launch_bk_rg(const GdnParams& p, const Launch& l, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Full-height tiles: smaller ones (64 rows) measured a faster flush phase
-// (B = 64, L = 8: 50.0 against 54.0 us) but slower non-flush phases (every
-// tile repeats the ring staging and record dots), a slower cycle overall.
+// Full-height tiles by default (4 waves, or the launch's width): 16-row waves
+// over 64-row tiles measured a faster flush phase (B = 64, L = 8: 50.0
+// against 54.0 us) but slower non-flush phases (every tile repeats the ring
+// staging and record dots), a slower cycle overall. buffered_launch below
+// narrows the block instead where that measured faster.
 template <int K, bool NORM, int ACT, bool VEC>
 hipError_t launch_bk(const GdnParams& p, const Launch& l, hipStream_t st) {
   return launch_bk_rg<K, NORM, ACT, VEC, buf_rg<K>()>(p, l, st);
@@ -441,6 +447,20 @@ hipError_t launch_bnorm(const GdnParams& p, const Launch& l, hipStream_t st) {
 size_t buffered_lds_bytes(int K, int rows, int L) {
   const size_t pm = (size_t)(L - 1);
   return sizeof(float) * (pm * (size_t)K + pm * (size_t)rows + 4 * pm + 1 + 2 * (size_t)rows);
+}
+
+// Block width of a buffered launch. 2-wave blocks (64-row tiles of 32-row
+// waves at K = 128) for large batches (at least four heads per CU) whose ring
+// of L - 1 records fits the staging pass issued ahead of the state stream,
+// 4 x BUF_RU4 elements per thread of 128. Measured on MI355X (HV = 32, K = V
+// = 128, bf16): B = 64, L = 8 cycle mean 29.7 against 30.7 us, B = 256 99.5
+// against 101.4; at L = 16 the ring no longer fits that pass and the wider
+// block stays ahead (30.5 against 33.0 us); B = 16 stays faster with 4 waves.
+Launch buffered_launch(int K, bool norm, int L, int64_t heads, int n_cu, const Launch& l) {
+  if (l.fixed || norm || K != 128) return l;
+  const int64_t first_pass = 4LL * BUF_RU4 * 128;
+  if ((int64_t)(L - 1) * K <= first_pass && heads >= 4LL * n_cu) return Launch{2, 0, 0};
+  return l;
 }
 
 int buffered_rows_per_tile(int K, int V, bool norm, const Launch& l) {

@@ -271,7 +271,11 @@ int gdn_decode_step_buffered(const void* mixed_qkv, int64_t qkv_row_stride, cons
   p.g_cache = g_cache;
   p.write_pos = write_pos;
   p.L = L;
-  return launch_status(ssmd::launch_gdn_buffered(p, l, stream), fn);
+  int n_cu = 0;
+  if (int rc2 = cu_count(&n_cu)) return rc2;
+  // the block width can only narrow here, so the LDS bound checked above holds
+  const ssmd::Launch lb = ssmd::buffered_launch(K, norm_gate != nullptr, L, (int64_t)B * HV, n_cu, l);
+  return launch_status(ssmd::launch_gdn_buffered(p, lb, stream), fn);
 }
 
 int gdn_decode_step_conv(const void* x, int64_t x_row_stride, const float* conv_weight,

@@ -176,6 +176,7 @@ hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, int n_c
 
 // Rows of one buffered-kernel tile, and the LDS its ring staging needs.
 int buffered_rows_per_tile(int K, int V, bool norm, const Launch& l);
+Launch buffered_launch(int K, bool norm, int L, int64_t heads, int n_cu, const Launch& l);
 size_t buffered_lds_bytes(int K, int rows, int L);
 
 
