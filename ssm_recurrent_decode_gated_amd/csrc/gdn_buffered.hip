@@ -34,7 +34,7 @@ constexpr int buf_rg() {
   return K == 16 ? 1 : (K == 32 ? 2 : (K == 256 ? 2 : 4));
 }
 
-template <int K, bool NORM, int ACT, bool VEC, int RG>
+template <int K, bool NORM, int ACT, bool VEC, int RG, int RU4>
 __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tiles_per_head,
                                                            int rows_per_tile) {
   using RL = RowLayout<K>;
@@ -108,12 +108,11 @@ __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tile
   float kt[RING_U], dt[RING_U];
   float gt = 0.f;
   // 16-bit rings with 8-byte aligned bases (the common case): 4 elements per
-  // load, two loads per thread for up to 2048 elements of each, issued
+  // load, RU4 loads per thread (4 RU4 blockDim elements of each), issued
   // unconditionally (indices clamped into record 0 when the ring is empty)
   // and kept raw until the LDS stores, so nothing waits on them before the
   // state stream is issued.
   constexpr bool R16 = ACT != SSMD_F32;
-  constexpr int RU4 = BUF_RU4;
   const bool rvec = R16 && (((reinterpret_cast<uintptr_t>(p.k_cache) | reinterpret_cast<uintptr_t>(p.d_cache)) & 7) == 0) &&
                     V % 4 == 0 && tr % 4 == 0;
   uint2 kt4[RU4], dt4[RU4];
@@ -394,7 +393,7 @@ __global__ __launch_bounds__(512) void gdn_buffered_kernel(GdnParams p, int tile
 
 namespace {
 
-template <int K, bool NORM, int ACT, bool VEC, int RG>
+template <int K, bool NORM, int ACT, bool VEC, int RG, int RU4>
 hipError_t launch_bk_rg(const GdnParams& p, const Launch& l, hipStream_t st) {
   constexpr int RPI = RowLayout<K>::RPI;
   const int wave_rows = RG * RPI;
@@ -411,7 +410,7 @@ hipError_t launch_bk_rg(const GdnParams& p, const Launch& l, hipStream_t st) {
   if (wpb > need) wpb = need;
   const size_t lds = buffered_lds_bytes(K, rows_per_tile, p.L);
   const dim3 grid((unsigned)((int64_t)p.B * p.HV * tiles));
-  gdn_buffered_kernel<K, NORM, ACT, VEC, RG><<<grid, dim3(64 * wpb), lds, st>>>(p, tiles, rows_per_tile);
+  gdn_buffered_kernel<K, NORM, ACT, VEC, RG, RU4><<<grid, dim3(64 * wpb), lds, st>>>(p, tiles, rows_per_tile);
   return hipGetLastError();
 }
 
@@ -422,7 +421,14 @@ hipError_t launch_bk_rg(const GdnParams& p, const Launch& l, hipStream_t st) {
 // narrows the block instead where that measured faster.
 template <int K, bool NORM, int ACT, bool VEC>
 hipError_t launch_bk(const GdnParams& p, const Launch& l, hipStream_t st) {
-  return launch_bk_rg<K, NORM, ACT, VEC, buf_rg<K>()>(p, l, st);
+  constexpr int RG = buf_rg<K>();
+  if constexpr (K == 128 && !NORM) {
+    // 2-wave blocks whose ring outgrows the default staging pass: a pass twice
+    // as deep (the kernel's registers peak elsewhere: 162 VGPRs either way)
+    if (!l.fixed && l.wpb == 2 && (int64_t)(p.L - 1) * K > 4LL * BUF_RU4 * 128)
+      return launch_bk_rg<K, NORM, ACT, VEC, RG, 2 * BUF_RU4>(p, l, st);
+  }
+  return launch_bk_rg<K, NORM, ACT, VEC, RG, BUF_RU4>(p, l, st);
 }
 
 template <int K, bool NORM>
@@ -451,15 +457,18 @@ size_t buffered_lds_bytes(int K, int rows, int L) {
 
 // Block width of a buffered launch. 2-wave blocks (64-row tiles of 32-row
 // waves at K = 128) for large batches (at least four heads per CU) whose ring
-// of L - 1 records fits the staging pass issued ahead of the state stream,
-// 4 x BUF_RU4 elements per thread of 128. Measured on MI355X (HV = 32, K = V
-// = 128, bf16): B = 64, L = 8 cycle mean 29.7 against 30.7 us, B = 256 99.5
-// against 101.4; at L = 16 the ring no longer fits that pass and the wider
-// block stays ahead (30.5 against 33.0 us); B = 16 stays faster with 4 waves.
+// of L - 1 records fits the staging pass issued ahead of the state stream
+// (4 x RU4 elements per thread of 128; RU4 = 2 BUF_RU4 where BUF_RU4 does not
+// suffice). Measured on MI355X (HV = 32, K = V = 128, bf16), cycle means:
+// B = 64, L = 8 29.7 against 30.7 us with 4-wave blocks; L = 16 29.6 against
+// 30.5 (33.0 with 2-wave blocks and a per-element loop for the records past
+// the staging pass); B = 256, L = 8 / 16 99.8 / 96.4 against 101.4 / 99.4.
+// The deeper pass costs a little where it is not needed (B = 64, L = 8: 30.0),
+// and B = 16 stays faster with 4 waves.
 Launch buffered_launch(int K, bool norm, int L, int64_t heads, int n_cu, const Launch& l) {
   if (l.fixed || norm || K != 128) return l;
-  const int64_t first_pass = 4LL * BUF_RU4 * 128;
-  if ((int64_t)(L - 1) * K <= first_pass && heads >= 4LL * n_cu) return Launch{2, 0, 0};
+  const int64_t deepest_pass = 4LL * 2 * BUF_RU4 * 128;
+  if ((int64_t)(L - 1) * K <= deepest_pass && heads >= 4LL * n_cu) return Launch{2, 0, 0};
   return l;
 }
 
