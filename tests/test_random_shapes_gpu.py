@@ -3,6 +3,10 @@ fp64 oracle: head sizes, ragged value dims, GQA ratios, dtypes, gated norm
 on/off, padded rows and (buffered) mixed and out-of-range phases drawn from a
 fixed generator, so every run checks the same cases. Complements the
 hand-picked cases of the per-entry-point tests with combinations nobody chose.
+The `large` tests draw batches with more than four heads per CU of a 256-CU
+part, so the launch shapes chosen for large batches (32-row tiles of the
+packed step, one-unit tiles of the 16-bit-state step, 2-wave buffered blocks,
+one block per conv group) meet ragged shapes too.
 """
 import numpy as np
 import pytest
@@ -39,6 +43,28 @@ def _draw(rng, i):
     return w, idx, norm
 
 
+def _draw_large(rng, i, K=None, G=None, V=None):
+    """A large-batch case: B HV >= 1100 heads, state at most 40 M elements."""
+    K = int(rng.choice([16, 32, 64, 128, 128, 256])) if K is None else K
+    G = int(rng.choice([1, 2, 4])) if G is None else G
+    H = int(rng.choice([2, 4, 8]))
+    HV = G * H
+    B = -(-1100 // HV) + int(rng.integers(0, 40))
+    vs = [v for v in (16, 40, 64, 100, 128, 200) if B * HV * v * K <= 40_000_000]
+    V = int(rng.choice(vs)) if V is None else V
+    slots = B + int(rng.integers(0, 5))
+    act = str(rng.choice(["f32", "bf16", "f16"]))
+    out = str(rng.choice(["f32", "bf16", "f16"]))
+    norm = str(rng.choice(["none", "none", "silu", "sigmoid"]))
+    w = W.GDNWorkload(f"large{i}_k{K}_h{H}_g{G}_v{V}_b{B}_{act}", B=B, H=H, HV=HV, K=K, V=V, num_slots=slots,
+                      act=act, out=out, idx="perm")
+    idx = W.slot_indices(w).clone()
+    for b in range(B):
+        if rng.random() < 0.2:
+            idx[b] = -1 if rng.random() < 0.5 else slots + int(rng.integers(0, 3))
+    return w, idx, norm
+
+
 def _check(out, ref, live, what):
     if not live:
         return
@@ -56,7 +82,17 @@ CASES = list(range(48))
 def test_random_gdn_step(i):
     need_gpu()
     rng = np.random.default_rng(1000 + i)
-    w, idx, norm = _draw(rng, i)
+    _case_gdn_step(i, *_draw(rng, i))
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_large_gdn_step(i):
+    need_gpu()
+    rng = np.random.default_rng(11000 + i)
+    _case_gdn_step(i, *_draw_large(rng, i))
+
+
+def _case_gdn_step(i, w, idx, norm):
     P, x = W.gdn_params(w), W.gdn_step_inputs(w, norm=norm != "none")
     st = W.gdn_state(w)
     st_d = st.to(DEV)
@@ -92,6 +128,19 @@ def test_random_gdn_buffered(i):
     need_gpu()
     rng = np.random.default_rng(2000 + i)
     w, idx, norm = _draw(rng, 100 + i)
+    _case_gdn_buffered(i, rng, w, idx, norm)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_large_gdn_buffered(i):
+    need_gpu()
+    rng = np.random.default_rng(12000 + i)
+    # K = 128 in half the cases: the head size whose large batches take 2-wave blocks
+    w, idx, norm = _draw_large(rng, 100 + i, K=128 if i % 2 == 0 else None)
+    _case_gdn_buffered(i, rng, w, idx, norm)
+
+
+def _case_gdn_buffered(i, rng, w, idx, norm):
     L = int(rng.integers(1, 17))
     phases = [int(rng.integers(0, L)) if rng.random() > 0.1 else L for _ in range(w.B)]
     P, x = W.gdn_params(w), W.gdn_step_inputs(w, norm=norm != "none")
@@ -204,7 +253,25 @@ def test_random_gdn_conv(i):
     need_gpu()
     rng = np.random.default_rng(4000 + i)
     w, idx, norm = _draw(rng, 200 + i)
-    Wd = int(rng.integers(2, 9))
+    _case_gdn_conv(i, rng, w, idx, norm, int(rng.integers(2, 9)))
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_large_gdn_conv(i):
+    """Half the cases have the shape of the one-block-per-group kernel (width
+    4, G V = 256, K = 64 or 128, no norm)."""
+    need_gpu()
+    rng = np.random.default_rng(14000 + i)
+    if i % 2 == 0:
+        G = int(rng.choice([2, 4]))
+        w, idx, norm = _draw_large(rng, 200 + i, K=int(rng.choice([64, 128])), G=G, V=256 // G)
+        _case_gdn_conv(i, rng, w, idx, "none", 4)
+    else:
+        w, idx, norm = _draw_large(rng, 200 + i)
+        _case_gdn_conv(i, rng, w, idx, norm, int(rng.integers(2, 9)))
+
+
+def _case_gdn_conv(i, rng, w, idx, norm, Wd):
     layout = str(rng.choice(["DS", "SD"]))
     P, x = W.gdn_params(w), W.gdn_step_inputs(w, norm=norm != "none")
     st, cv = W.gdn_state(w), W.gdn_conv(w, Wd, layout=layout, bias=bool(rng.random() < 0.5))
@@ -237,6 +304,18 @@ def test_random_gdn_state16(i):
     need_gpu()
     rng = np.random.default_rng(5000 + i)
     w, idx, norm = _draw(rng, 300 + i)
+    _case_gdn_state16(i, rng, w, idx, norm)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_large_gdn_state16(i):
+    need_gpu()
+    rng = np.random.default_rng(15000 + i)
+    w, idx, norm = _draw_large(rng, 300 + i)
+    _case_gdn_state16(i, rng, w, idx, norm)
+
+
+def _case_gdn_state16(i, rng, w, idx, norm):
     sdt = torch.bfloat16 if rng.random() < 0.5 else torch.float16
     P, x = W.gdn_params(w), W.gdn_step_inputs(w, norm=norm != "none")
     st = W.gdn_state(w).to(sdt)
@@ -269,7 +348,18 @@ def test_random_gdn_multi(i):
     need_gpu()
     rng = np.random.default_rng(6000 + i)
     w, idx, norm = _draw(rng, 400 + i)
-    T = int(rng.integers(1, 12))
+    _case_gdn_multi(i, rng, w, idx, int(rng.integers(1, 12)))
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_large_gdn_multi(i):
+    need_gpu()
+    rng = np.random.default_rng(16000 + i)
+    w, idx, norm = _draw_large(rng, 400 + i)
+    _case_gdn_multi(i, rng, w, idx, int(rng.integers(1, 5)))
+
+
+def _case_gdn_multi(i, rng, w, idx, T):
     lengths = torch.tensor([int(rng.integers(0, T + 1)) for _ in range(w.B)], dtype=torch.int32)
     P = W.gdn_params(w)
     g = W.generator(0, w.name, "rand_multi", T)
