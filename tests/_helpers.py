@@ -5,7 +5,10 @@ Acceptance metric for floating point (fp32 kernels against the fp64 oracle):
 where a row is the last axis (a head's V outputs, or a state row of K
 columns). A plain relative error fails spuriously near zero, and a plain
 absolute error is meaningless across magnitudes; the row rms is the natural
-scale of each element.
+scale of each element. A row of fewer than MIN_ROW values has no meaningful
+rms (at V = 1 it is the element itself, so an output produced by cancellation
+would be held to a relative bar no fp32 evaluation meets): its scale is the
+rms over the last two axes, the batch row's heads.
 
 Outputs stored in 16-bit types are the kernel's fp32 result rounded once,
 to nearest even. A kernel within the fp32 bar computes some y with
@@ -28,10 +31,21 @@ def to_np64(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().double().numpy()
 
 
+MIN_ROW = 8  # rows shorter than this take their scale over the last two axes
+
+
+def row_rms(ref: np.ndarray) -> np.ndarray:
+    """rms of ref over its row (the last axis), or over the last two axes
+    where a row holds fewer than MIN_ROW values; broadcastable to ref."""
+    ref = np.asarray(ref, dtype=np.float64)
+    axes = (-2, -1) if ref.ndim >= 2 and ref.shape[-1] < MIN_ROW else -1
+    return np.sqrt(np.mean(ref * ref, axis=axes, keepdims=True))
+
+
 def mixed_err(x: np.ndarray, ref: np.ndarray) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
+    rms = row_rms(ref)
     den = np.maximum(np.maximum(np.abs(ref), rms), 1e-30)
     return np.abs(x - ref) / den
 
@@ -80,8 +94,7 @@ def assert_out16(x: torch.Tensor, exact, tol=FP32_TOL, what=""):
     xv = to_np64(x).reshape(np.shape(exact))
     ex = np.asarray(exact, dtype=np.float64)
     assert np.isfinite(ex).all(), f"{what}: reference not finite"
-    rms = np.sqrt(np.mean(ex * ex, axis=-1, keepdims=True))
-    band = tol * np.maximum(np.abs(ex), rms)
+    band = tol * np.maximum(np.abs(ex), row_rms(ex))
     lo, hi = rne16(ex - band, mant), rne16(ex + band, mant)
     bad = (xv < lo) | (xv > hi) | ~np.isfinite(xv)
     if bad.any():
@@ -114,7 +127,7 @@ def assert_rounded16(got, ref, what, exact, mant_bits=7):
     diff = np.abs(got - ref)
     # fp32 error is measured against the record's scale, as in the fp32 parity
     # metric: delta = beta (v - S k) can cancel, so its error tracks the row, not itself
-    scale = np.maximum(np.abs(exact), np.sqrt(np.mean(exact * exact, axis=-1, keepdims=True)))
+    scale = np.maximum(np.abs(exact), row_rms(exact))
     assert (diff <= ulp16(ref, mant_bits) * 1.0000001 + MIDPOINT_REL * scale).all(), \
         f"{what}: stored value off by more than one ulp"
     flip = diff != 0

@@ -133,3 +133,23 @@ def test_out16_rejects_an_error_above_the_fp32_bar():
     bad = ex * (1 + 3e-3)  # a kernel 3e-3 off, rounded correctly
     with pytest.raises(AssertionError):
         assert_out16(torch.from_numpy(bad).to(torch.float32).to(torch.bfloat16), ex, 1e-4, "3e-3 off")
+
+
+def test_short_rows_take_their_scale_over_the_heads():
+    """A one-value row (V = 1) is scaled by the rms over the batch row's
+    heads, not by itself: an output that cancellation made small keeps the
+    absolute fp32 bar of its neighbours, while a wrong value still fails."""
+    from tests._helpers import MIN_ROW, assert_mixed, mixed_err, row_rms
+    ref = np.random.default_rng(3).standard_normal((4, 12, 1))
+    ref[1, 1, 0] = 1.6e-6  # a cancellation-sized output among normal ones
+    scale = row_rms(ref)[1, 0, 0]
+    x = ref.copy()
+    x[1, 1, 0] += 0.5e-4 * scale  # within the bar of the heads' scale
+    assert_mixed(x, ref, 1e-4, "short row, fp32-sized error")
+    x[1, 1, 0] = ref[1, 1, 0] + 3e-4 * scale
+    with pytest.raises(AssertionError):
+        assert_mixed(x, ref, 1e-4, "short row, wrong value")
+    # rows of MIN_ROW values or more keep their own rms
+    wide = np.random.default_rng(4).standard_normal((2, 3, MIN_ROW))
+    np.testing.assert_allclose(row_rms(wide), np.sqrt(np.mean(wide * wide, axis=-1, keepdims=True)))
+    assert mixed_err(wide, wide).max() == 0.0
