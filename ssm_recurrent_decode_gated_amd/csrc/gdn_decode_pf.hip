@@ -4,9 +4,9 @@
 // state pass in registers while it computes and stores the current one.
 //
 // Launch shape (measured on MI355X, HV = 32, K = V = 128; see the
-// launcher): at large batches one 4-wave block per 32-row tile, one row
-// group per wave, so every block is a single short read-then-write burst
-// (B = 256: 177 us, 6.06 TB/s of state). In-place streams on this part run
+// launcher): at large batches one 1-wave block per 8-row tile, so every block
+// is a single short read-then-write burst (B = 256: 170.6 us, 6.29 TB/s of
+// state). In-place streams on this part run
 // faster the less each block and wave holds: many short bursts in flight at
 // once keep HBM busier than a few long ones (a plain in-place copy: 5.6 TB/s
 // with 64 KB per block, 6.3 with 8 KB, 6.6 with 4 KB). Small batches, with at
@@ -173,16 +173,18 @@ hipError_t launch_pf_k(const GdnParams& p, const Launch& l, int n_cu, hipStream_
     const int rpt = w * rg * RowLayout<K>::RPI;
     return (int64_t)p.B * p.HV * ((p.V + rpt - 1) / rpt);
   };
-  // Large batches (more than two full-height units per CU): one 4-wave block
-  // per tile of 4 x RPI rows, one row group (8 rows of K = 64/128) per wave,
-  // no walk. Many short read-then-write bursts in flight at once keep HBM
-  // busier than a few long streams: at B = 256 (HV = 32, K = V = 128) 177 us,
-  // against 185.5 us for the persistent walk below (32 rows per wave, one
-  // block per CU) and 190.6 us for 16-row waves; B = 64: 46.4 us against
-  // 49.9. The persistent walk at one row group per wave measured 197-272 us,
-  // so small tiles go with one block each.
+  // Large batches (more than two full-height units per CU): one 1-wave block
+  // per tile of one row group (8 rows of K = 64/128, 4 KB), no walk. Many
+  // short read-then-write bursts in flight at once keep HBM busier than a few
+  // long streams: at B = 256 (HV = 32, K = V = 128) 170.6 us, against 171.2
+  // with 2-wave and 171.6 with 4-wave blocks over tiles of 2 and 4 row groups
+  // (all three hold 64 KB of state loads per CU at this kernel's 4 waves per
+  // SIMD; 8-wave blocks 180), 185.5 us for the persistent walk below (32 rows
+  // per wave, one block per CU) and 190.6 us for 16-row waves; B = 64: 45.7 us
+  // against 46.1 (4-wave) and 49.9 (walk). The persistent walk at one row
+  // group per wave measured 197-272 us, so small tiles go with one block each.
   if constexpr (RG > 1) {
-    if (units_for(4, RG) > 2LL * n_cu) return launch_pf_rg<K, ACT, VEC, 1>(p, 4, units_for(4, 1), st);
+    if (units_for(4, RG) > 2LL * n_cu) return launch_pf_rg<K, ACT, VEC, 1>(p, 1, units_for(1, 1), st);
   }
   // Small batches (measured at HV = 32, K = V = 128): narrower blocks until
   // every CU has a unit, then, if even 1-wave blocks leave CUs idle, half the
