@@ -9,7 +9,7 @@
 // e^g S + delta k is rounded (RNE) once, when it is stored. The step's own
 // output comes from the unrounded row.
 //
-// Launch structure: at large batches one 4-wave block per row tile holding a
+// Launch structure: at large batches one 1-wave block per row tile holding a
 // single unit (WALK = false); otherwise persistent blocks, two per CU, each
 // wave holding the next unit's state pass while it computes the current one.
 // Units go in XCD-aware order (xcd_unit). A row of K 16-bit values is spread
@@ -224,9 +224,10 @@ hipError_t launch_s16_rg(const GdnParams& p, const Launch& l, int n_cu, hipStrea
   return hipGetLastError();
 }
 
-// One block of 4 waves per tile of 4 x RG x RPI rows, no walk: the kernel
-// holds a single unit, so its registers admit five waves per SIMD, and the
-// hardware dispatcher refills each CU as its blocks finish.
+// One block per tile (as many waves as the tile has row groups of RG x RPI
+// rows, at most 4), no walk: the kernel holds a single unit, so its registers
+// admit five waves per SIMD, and the hardware dispatcher refills each CU as
+// its blocks finish.
 template <int K, int ST, int ACT, bool VEC, int RG>
 hipError_t launch_s16_tiles(const GdnParams& p, int64_t units, int rows_per_tile, int tiles, hipStream_t st) {
   const int wave_rows = RG * RowLayout16<K>::RPI;
@@ -236,25 +237,30 @@ hipError_t launch_s16_tiles(const GdnParams& p, int64_t units, int rows_per_tile
   return hipGetLastError();
 }
 
-// Large batches (more than four 4-wave tiles per CU): one block per tile of
-// half the walk's rows per wave. Measured on MI355X at HV = 32, K = V = 128,
-// bf16 state, same session: B = 256 94.2 us against 103.9 us for the walk
-// (5.77 TB/s), B = 64 27.3 against 28.8. With no compute at all the walk's
-// loads and stores take 100 us at B = 256: its limit is how its two units per
-// wave issue, not the arithmetic. A third block per CU for the walk, or a
-// capped grid-stride loop over single units (102 us), measured slower. Small
-// batches keep the walk (B = 16: 8.3 against 9.2 us): with few tiles, its
-// register use, two blocks per CU, spreads them evenly over the CUs.
+// Large batches (more than four 4-wave tiles of half the walk's rows per wave
+// per CU): one 1-wave block per tile of one wave's rows (16 at K = 128).
+// Measured on MI355X at HV = 32, K = V = 128, bf16 state, same session: B =
+// 256 94.2 us with 4-wave blocks against 103.9 us for the walk (5.77 TB/s),
+// B = 64 27.3 against 28.8; then 1-wave blocks 93.7 / 27.0 against 94.7 /
+// 27.6 for 4-wave and 95.0 / 27.2 for 2-wave blocks. With no compute at all
+// the walk's loads and stores take 100 us at B = 256: its limit is how its
+// two units per wave issue, not the arithmetic. A third block per CU for the
+// walk, or a capped grid-stride loop over single units (102 us), measured
+// slower. Small batches keep the walk (B = 16: 8.3 against 9.2 us for 4-wave
+// tiles, 9.7 for 1-wave ones): with few tiles, its register use, two blocks
+// per CU, spreads them evenly over the CUs.
 template <int K, int ST, int ACT, bool VEC, bool NORM>
 hipError_t launch_s16_k(const GdnParams& p, const Launch& l, int n_cu, hipStream_t st) {
   constexpr int RG = s16_rg<K>();
   if constexpr (!NORM) {
     constexpr int RG1 = RG / 2 > 1 ? RG / 2 : 1;
-    const int rows_per_tile = 4 * RG1 * RowLayout16<K>::RPI;
-    const int tiles = (p.V + rows_per_tile - 1) / rows_per_tile;
-    const int64_t units = (int64_t)p.B * p.HV * tiles;
-    if (!l.fixed && units > 4LL * n_cu)
-      return launch_s16_tiles<K, ST, ACT, VEC, RG1>(p, units, rows_per_tile, tiles, st);
+    const int rows4 = 4 * RG1 * RowLayout16<K>::RPI;
+    const int64_t units4 = (int64_t)p.B * p.HV * ((p.V + rows4 - 1) / rows4);
+    if (!l.fixed && units4 > 4LL * n_cu) {
+      const int rows_per_tile = RG1 * RowLayout16<K>::RPI;
+      const int tiles = (p.V + rows_per_tile - 1) / rows_per_tile;
+      return launch_s16_tiles<K, ST, ACT, VEC, RG1>(p, (int64_t)p.B * p.HV * tiles, rows_per_tile, tiles, st);
+    }
   }
   return launch_s16_rg<K, ST, ACT, VEC, NORM, RG>(p, l, n_cu, st);
 }
