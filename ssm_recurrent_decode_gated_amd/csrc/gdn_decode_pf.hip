@@ -1,16 +1,17 @@
 // gdn_decode_pf.hip -- packed GDN decode (no output norm). Same arithmetic
-// and row layout as gdn_decode.hip. Blocks walk work units (batch row, value
-// head, row tile) with a grid stride, each wave holding the next unit's
-// state pass in registers while it computes and stores the current one.
+// and row layout as gdn_decode.hip. Blocks take work units (batch row, value
+// head, row tile); where the grid is smaller than the unit count they walk
+// the units with a grid stride, each wave holding the next unit's state pass
+// in registers while it computes and stores the current one.
 //
 // Launch shape (measured on MI355X, HV = 32, K = V = 128; see the
 // launcher): at large batches one 1-wave block per 8-row tile, so every block
 // is a single short read-then-write burst (B = 256: 170.6 us, 6.29 TB/s of
-// state). In-place streams on this part run
-// faster the less each block and wave holds: many short bursts in flight at
-// once keep HBM busier than a few long ones (a plain in-place copy: 5.6 TB/s
-// with 64 KB per block, 6.3 with 8 KB, 6.6 with 4 KB). Small batches, with at
-// most two full-height units per CU, launch one block per 128-row unit.
+// state). In-place streams on this part run faster the less each block and
+// wave holds: many short bursts in flight at once keep HBM busier than a few
+// long ones (a plain in-place copy: 5.6 TB/s with 64 KB per block, 6.3 with
+// 8 KB, 6.6 with 4 KB). Small batches, with at most two full-height units per
+// CU, launch one block per 128-row unit.
 #include "ssmd_device.h"
 #include "ssmd_internal.h"
 
