@@ -1,5 +1,8 @@
 """MI355X (gfx950) single-token recurrent decode for gated linear-attention
-layers: the gated delta rule (GDN / DeltaNet / KDA) over an fp32 state pool.
+and SSM layers: the gated delta rule (GDN / DeltaNet / KDA) over a
+slot-indexed fp32 (or 16-bit) state pool, its buffered and conv-fused forms,
+Mamba-1's selective-scan decode, and the multi-token and chunked prefill
+passes that fill the same pools.
 
 The compute lives in libssmdec.so (hand-written HIP kernels behind the C ABI
 of include/ssmdec.h); this package is its thin ctypes binding. Importing it
