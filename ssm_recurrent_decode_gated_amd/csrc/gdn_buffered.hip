@@ -423,6 +423,9 @@ template <int K, bool NORM, int ACT, bool VEC>
 hipError_t launch_bk(const GdnParams& p, const Launch& l, hipStream_t st) {
   constexpr int RG = buf_rg<K>();
   if constexpr (K == 128 && !NORM) {
+    // L = 1: every step flushes with no record to fold, a plain in-place
+    // stream: 1-wave blocks over 8-row tiles, as the packed step
+    if (!l.fixed && l.wpb == 1 && p.L == 1) return launch_bk_rg<K, NORM, ACT, VEC, 1, BUF_RU4>(p, l, st);
     // 2-wave blocks whose ring outgrows the default staging pass: a pass twice
     // as deep (the kernel's registers peak elsewhere: 162 VGPRs either way)
     if (!l.fixed && l.wpb == 2 && (int64_t)(p.L - 1) * K > 4LL * BUF_RU4 * 128)
@@ -467,6 +470,8 @@ size_t buffered_lds_bytes(int K, int rows, int L) {
 // and B = 16 stays faster with 4 waves.
 Launch buffered_launch(int K, bool norm, int L, int64_t heads, int n_cu, const Launch& l) {
   if (l.fixed || norm || K != 128) return l;
+  // L = 1 (measured: B = 64 47.9 against 50.6 us, B = 256 176.4 against 187.3)
+  if (L == 1 && heads >= 4LL * n_cu) return Launch{1, 0, 0};
   const int64_t deepest_pass = 4LL * 2 * BUF_RU4 * 128;
   if ((int64_t)(L - 1) * K <= deepest_pass && heads >= 4LL * n_cu) return Launch{2, 0, 0};
   return l;
