@@ -210,10 +210,14 @@ __device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-
 __device__ __forceinline__ float silu_f(float x) { return x * sigmoid_f(x); }
 
 // ------------------------------------------------------------- reductions
-// DPP lane moves within a row of 16 lanes (gfx9 encodings).
+// DPP lane moves within a row of 16 lanes (gfx9 encodings). Every pattern
+// below reads a lane of the caller's own group, and groups are active or
+// inactive as a whole, so no lane reads a disabled or out-of-row source and
+// bound_ctrl never takes effect; setting it lets the compiler fold the move
+// into the add that consumes it (one v_add_f32_dpp per step).
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
 }
 constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
 constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
