@@ -470,7 +470,8 @@ size_t buffered_lds_bytes(int K, int rows, int L) {
 // and B = 16 stays faster with 4 waves.
 Launch buffered_launch(int K, bool norm, int L, int64_t heads, int n_cu, const Launch& l) {
   if (l.fixed || norm || K != 128) return l;
-  // L = 1 (measured: B = 64 47.9 against 50.6 us, B = 256 176.4 against 187.3)
+  // L = 1: 1-wave blocks over 8-row tiles (measured: B = 64 46.3 against 50.5 us
+  // with the wide tiles, B = 256 170.8 against 187.3)
   if (L == 1 && heads >= 4LL * n_cu) return Launch{1, 0, 0};
   const int64_t deepest_pass = 4LL * 2 * BUF_RU4 * 128;
   if ((int64_t)(L - 1) * K <= deepest_pass && heads >= 4LL * n_cu) return Launch{2, 0, 0};

@@ -271,3 +271,52 @@ def test_buffered_many_rows_with_padding(K, V, HV, L):
         assert torch.equal(got_st[s], st[s]), f"slot {s} (no live row) changed"
         for k in ring0:
             np.testing.assert_array_equal(got[k][s], ring0[k][s], err_msg=f"{k} slot {s}")
+
+
+@pytest.mark.parametrize("V,act", [(100, "bf16"), (128, "f32"), (20, "f16")])
+def test_buffered_l1_large_batch(V, act):
+    """L = 1 at a large batch (1280 heads: at least four per CU of a 256-CU
+    part), where the launch takes 1-wave blocks over 8-row tiles: ragged last
+    tiles (V = 100, 20), padded slots and out-of-range phases interleaved.
+    Every live row is a flush of an empty ring: outputs and written states
+    match the oracle, padded rows and the ring stay untouched."""
+    need_gpu()
+    B, H, HV, K, L = 40, 16, 32, 128, 1
+    w = W.GDNWorkload(f"buf_l1_large_v{V}_{act}", B=B, H=H, HV=HV, K=K, V=V, num_slots=B + 6, act=act,
+                      out="f32", idx="perm")
+    P, idx, x = W.gdn_params(w), W.slot_indices(w).clone(), W.gdn_step_inputs(w)
+    phases = [0] * B
+    for b in range(B):
+        if b % 7 == 3:
+            idx[b] = -1 if b % 2 else w.num_slots
+        elif b % 9 == 5:
+            phases[b] = 1 if b % 2 else -1
+    st = W.gdn_state(w)
+    ring = W.gdn_ring(w, L)
+    wp = torch.tensor(phases, dtype=torch.int32)
+    st_d = st.to(DEV)
+    ring_d = _ring_on_device(ring, 0)
+    out = torch.full((B, 1, HV, V), float("nan"), device=DEV)
+    _call(w, x, P, st_d, idx, ring_d, wp, out)
+    ref_st = st.double().numpy().copy()
+    ref_ring = {k: v.double().numpy().copy() for k, v in ring.items()}
+    fmt = {"f32": O.FMT_F32, "bf16": O.FMT_BF16, "f16": O.FMT_F16}[act]
+    ro = O.gdn_step_buffered(x["qkv"], x["a"], x["b"], P["A_log"], P["dt_bias"], ref_st, idx,
+                             ref_ring["d_cache"], ref_ring["k_cache"], ref_ring["g_cache"], wp, L,
+                             H=H, HV=HV, K=K, V=V, ring_fmt=fmt)
+    torch.cuda.synchronize()
+    live = [b for b in range(B) if 0 <= int(idx[b]) < w.num_slots and phases[b] == 0]
+    dead = [b for b in range(B) if b not in live]
+    assert len(dead) >= 8
+    o = out.reshape(B, HV, V)
+    assert_mixed(o[live], ro[live], FP32_TOL, "output")
+    assert torch.isnan(o[dead]).all(), "a padded row wrote its output"
+    got_st = st_d.cpu()
+    for b in live:
+        s = int(idx[b])
+        assert_mixed(got_st[s], ref_st[s], FP32_TOL, f"flushed state row {b}")
+    touched = {int(idx[b]) for b in live}
+    for s in set(range(w.num_slots)) - touched:
+        assert torch.equal(got_st[s], st[s]), f"slot {s} (no live row) changed"
+    for k, v in ring_d.items():
+        assert torch.equal(v.cpu(), ring[k]), f"{k} changed: an L = 1 flush appends no record"
