@@ -655,7 +655,7 @@ def test_pin_gdn_multi_lengths_padding_split():
     np.testing.assert_array_equal(st3[4], st[4])
 
 
-# ------------------------------------------------------- fp32 build (Pin-14)
+# ------------------------------------------------------- fp32 build of the oracle
 def test_fp32_build_matches_fp64_on_tiny_chain():
     """The oracle's fp32 build of the packed step against its fp64 one on the
     tiny workload (B = 2, H = HV = 2, K = V = 16, fp32 inputs, q/k L2-normed,
