@@ -142,6 +142,22 @@ def test_graph_gdn_multi_and_chunked():
                                                               d["st"], d["idx"], d["out"], workspace=d["ws"]),
                           lambda d: (d["st"], d["out"]))
 
+    # the static-workspace form, for callers that cannot allocate under capture
+    _replay_matches_eager(make, lambda d: S.gdn_chunk_prefill_noalloc(d["qkv"], d["a"], d["b"], d["A_log"],
+                                                                      d["dt_bias"], d["st"], d["idx"], d["out"]),
+                          lambda d: (d["st"], d["out"]))
+
+
+def test_graph_mamba_decode():
+    need_gpu()
+    w = W.MambaWorkload("graph_mamba", B=8, Dm=1536, N=16, num_slots=8)
+    m = W.mamba_inputs(w)
+
+    def make():
+        return {n: v.to(DEV) for n, v in m.items()} | {"out": torch.zeros(w.B, w.Dm, device=DEV)}
+    _replay_matches_eager(make, lambda d: S.mamba_decode_step(d["x"], d["dt"], d["A"], d["Bm"], d["Cm"], d["Dv"],
+                                                              d["z"], d["h"], d["idx"], d["out"]),
+                          lambda d: (d["h"], d["out"]))
 
 def test_graph_slot_index_check_and_stream_copy():
     """The two helper entry points captured too: the duplicate-slot count
