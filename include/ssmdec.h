@@ -153,6 +153,12 @@ int gdn_decode_step_state16(const void* mixed_qkv, int64_t qkv_row_stride,
  * what gdn_decode_step computes. Ring entries past p, and the whole ring
  * after a flush, are don't-care; a zeroed ring with write_pos = 0 is a cold
  * start.
+ * L is 1..64 (else SSMD_ERR_BAD_SHAPE), and the ring's staging must fit the
+ * kernel's shared memory: 4 ((L-1)(K + R + 4) + 1 + 2R) <= 61440 bytes, with
+ * R = V when norm_gate is given and otherwise the row-tile height (128 rows
+ * for K = 64 and 128, 64 for K = 16, 32 and 256); past it the call returns
+ * SSMD_ERR_UNSUPPORTED (without the norm: L <= 59 at K = 128, L <= 48 at
+ * K = 256).
  * All other arguments are those of gdn_decode_step.
  */
 int gdn_decode_step_buffered(const void* mixed_qkv, int64_t qkv_row_stride,

@@ -86,9 +86,9 @@ def test_gdn_empty_batch_is_a_noop():
 def test_buffered_host_validation():
     L = S.load_library()
 
-    def call(L_=8, d=0x90000, wp=0xA0000, K=128, B=4):
-        return L.gdn_decode_step_buffered(0x10000, 8192, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000, 16,
-                                          0x70000, 0x80000, B, 16, 32, K, 128, 1, 1, 0.088, 1, 1e-6, None,
+    def call(L_=8, d=0x90000, wp=0xA0000, K=128, B=4, V=128, gate=None):
+        return L.gdn_decode_step_buffered(0x10000, 1 << 16, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000, 16,
+                                          0x70000, 0x80000, B, 16, 32, K, V, 1, 1, 0.088, 1, 1e-6, gate,
                                           None, 1e-5, 0, d, 0xB0000, 0xC0000, wp, L_, None)
     assert call(L_=0) == BAD_SHAPE
     assert call(L_=65) == BAD_SHAPE
@@ -96,6 +96,12 @@ def test_buffered_host_validation():
     assert call(wp=None) == NULL_ARG
     assert call(K=48) == UNSUPPORTED
     assert call(B=0, d=None, wp=None) == OK
+    # the ring staging's shared-memory bound, 4 ((L-1)(K + R + 4) + 1 + 2R) <= 61440 bytes
+    # (R: 128-row tiles at K = 128, 64 at K = 256, V with the gated norm), checked
+    # before anything runs (B = 0 launches nothing either way)
+    for K, V, gate, last in ((128, 128, None, 59), (256, 128, None, 48), (128, 1024, 0xD0000, 12)):
+        assert call(B=0, L_=last, K=K, V=V, gate=gate) == OK, (K, V, last)
+        assert call(B=0, L_=last + 1, K=K, V=V, gate=gate) == UNSUPPORTED, (K, V, last + 1)
 
 
 def test_kda_host_validation():
