@@ -77,7 +77,8 @@ def _pin_functions():
 @pytest.mark.parametrize("mutant", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_pins_catch_planted_mistake(mutant, tmp_path, monkeypatch):
     name, old, new = mutant
-    src = open(ob.SRC).read()
+    with open(ob.SRC) as f:
+        src = f.read()
     assert src.count(old) == 1, f"mutation site for '{name}' not unique in the oracle source"
     mpath = tmp_path / "mutant.c"
     mpath.write_text(src.replace(old, new))
