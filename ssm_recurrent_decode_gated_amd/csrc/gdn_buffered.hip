@@ -423,9 +423,19 @@ template <int K, bool NORM, int ACT, bool VEC>
 hipError_t launch_bk(const GdnParams& p, const Launch& l, hipStream_t st) {
   constexpr int RG = buf_rg<K>();
   if constexpr (K == 128 && !NORM) {
-    // L = 1: every step flushes with no record to fold, a plain in-place
-    // stream: 1-wave blocks over 8-row tiles, as the packed step
-    if (!l.fixed && l.wpb == 1 && p.L == 1) return launch_bk_rg<K, NORM, ACT, VEC, 1, BUF_RU4>(p, l, st);
+    if (!l.fixed && l.wpb == 1) {
+      // L = 1: every step flushes with no record to fold, a plain in-place
+      // stream: 1-wave blocks over 8-row tiles, as the packed step
+      if (p.L == 1) return launch_bk_rg<K, NORM, ACT, VEC, 1, BUF_RU4>(p, l, st);
+      // small batches: 1-wave blocks over 16-row tiles, so that a few heads
+      // still spread over every CU; the staging pass ahead of the state
+      // stream is made deep enough for the ring's L - 1 keys (64 threads x
+      // 4 RU4 elements: 512, 1024 or 2048)
+      const int64_t keys = (int64_t)(p.L - 1) * K;
+      if (keys > 4LL * 2 * BUF_RU4 * 64) return launch_bk_rg<K, NORM, ACT, VEC, 2, 4 * BUF_RU4>(p, l, st);
+      if (keys > 4LL * BUF_RU4 * 64) return launch_bk_rg<K, NORM, ACT, VEC, 2, 2 * BUF_RU4>(p, l, st);
+      return launch_bk_rg<K, NORM, ACT, VEC, 2, BUF_RU4>(p, l, st);
+    }
     // 2-wave blocks whose ring outgrows the default staging pass: a pass twice
     // as deep (the kernel's registers peak elsewhere: 162 VGPRs either way)
     if (!l.fixed && l.wpb == 2 && (int64_t)(p.L - 1) * K > 4LL * BUF_RU4 * 128)
@@ -467,12 +477,19 @@ size_t buffered_lds_bytes(int K, int rows, int L) {
 // 30.5 (33.0 with 2-wave blocks and a per-element loop for the records past
 // the staging pass); B = 256, L = 8 / 16 99.8 / 96.4 against 101.4 / 99.4.
 // The deeper pass costs a little where it is not needed (B = 64, L = 8: 30.0),
-// and B = 16 stays faster with 4 waves.
+// and B = 16 stays faster with 4 waves. Below one head per CU, 1-wave blocks
+// over 16-row tiles (8-row at L = 1) spread the few heads over every CU.
 Launch buffered_launch(int K, bool norm, int L, int64_t heads, int n_cu, const Launch& l) {
   if (l.fixed || norm || K != 128) return l;
   // L = 1: 1-wave blocks over 8-row tiles (measured: B = 64 46.3 against 50.5 us
   // with the wide tiles, B = 256 170.8 against 187.3)
   if (L == 1 && heads >= 4LL * n_cu) return Launch{1, 0, 0};
+  // small batches (fewer heads than CUs): 1-wave blocks over 16-row tiles
+  // (8-row at L = 1). HV = 32, B = 1: L = 1 / 8 / 16 cycles 4.2 / 5.5 / 6.4
+  // against 6.3 / 6.9 / 7.2 us with whole-head 4-wave blocks; from one head
+  // per CU up the wider blocks are as fast or faster (B = 8: 8.6 / 8.6 / 8.8
+  // against 9.4 / 8.6 / 10.2)
+  if (heads < n_cu) return Launch{1, 0, 0};
   const int64_t deepest_pass = 4LL * 2 * BUF_RU4 * 128;
   if ((int64_t)(L - 1) * K <= deepest_pass && heads >= 4LL * n_cu) return Launch{2, 0, 0};
   return l;
