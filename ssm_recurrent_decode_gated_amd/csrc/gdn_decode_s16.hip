@@ -248,7 +248,9 @@ hipError_t launch_s16_tiles(const GdnParams& p, int64_t units, int rows_per_tile
 // walk, or a capped grid-stride loop over single units (102 us), measured
 // slower. Small batches keep the walk (B = 16: 8.3 against 9.2 us for 4-wave
 // tiles, 9.7 for 1-wave ones): with few tiles, its register use, two blocks
-// per CU, spreads them evenly over the CUs.
+// per CU, spreads them evenly over the CUs. Below one whole-head tile per CU
+// the walk leaves CUs idle, and the 1-wave tiles spread the few heads over all
+// of them (B = 1 / 2 / 4: 3.9 / 4.3 / 4.7 against 5.0 / 5.3 / 5.6 us).
 template <int K, int ST, int ACT, bool VEC, bool NORM>
 hipError_t launch_s16_k(const GdnParams& p, const Launch& l, int n_cu, hipStream_t st) {
   constexpr int RG = s16_rg<K>();
@@ -256,7 +258,10 @@ hipError_t launch_s16_k(const GdnParams& p, const Launch& l, int n_cu, hipStream
     constexpr int RG1 = RG / 2 > 1 ? RG / 2 : 1;
     const int rows4 = 4 * RG1 * RowLayout16<K>::RPI;
     const int64_t units4 = (int64_t)p.B * p.HV * ((p.V + rows4 - 1) / rows4);
-    if (!l.fixed && units4 > 4LL * n_cu) {
+    // the walk's whole-head tiles (4 waves of RG row groups) per CU
+    const int rows_w = 4 * RG * RowLayout16<K>::RPI;
+    const int64_t units_w = (int64_t)p.B * p.HV * ((p.V + rows_w - 1) / rows_w);
+    if (!l.fixed && (units4 > 4LL * n_cu || units_w < n_cu)) {
       const int rows_per_tile = RG1 * RowLayout16<K>::RPI;
       const int tiles = (p.V + rows_per_tile - 1) / rows_per_tile;
       return launch_s16_tiles<K, ST, ACT, VEC, RG1>(p, (int64_t)p.B * p.HV * tiles, rows_per_tile, tiles, st);
