@@ -21,10 +21,9 @@ constexpr int mamba_rg() {
   return N <= 32 ? 4 : 2;
 }
 
-template <int N, int ACT>
+template <int N, int ACT, int RG>
 __global__ __launch_bounds__(256) void mamba_decode_kernel(MambaParams p, int blocks_per_row) {
   using RL = RowLayout<N>;
-  constexpr int RG = mamba_rg<N>();
   constexpr int LPR = RL::LPR, NV = RL::NV, RPI = RL::RPI;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -93,37 +92,58 @@ __global__ __launch_bounds__(256) void mamba_decode_kernel(MambaParams p, int bl
 
 namespace {
 
-template <int N, int ACT>
-hipError_t launch_m(const MambaParams& p, const Launch& l, hipStream_t st) {
-  const int rows_per_wave = mamba_rg<N>() * RowLayout<N>::RPI;
-  // 2-wave blocks unless a launch shape is forced (measured at N = 16:
-  // B = 256, D = 4096 26.8 us against 27.4 with 4 waves; B = 8, D = 1536 3.36
-  // against 3.45)
-  const int wpb = l.fixed ? min(l.wpb, 4) : 2;
-  const int blocks_per_row = (p.Dm + wpb * rows_per_wave - 1) / (wpb * rows_per_wave);
+template <int N, int ACT, int RG>
+hipError_t launch_m_rg(const MambaParams& p, int wpb, hipStream_t st) {
+  const int rows_per_block = wpb * RG * RowLayout<N>::RPI;
+  const int blocks_per_row = (p.Dm + rows_per_block - 1) / rows_per_block;
   const dim3 grid((unsigned)((int64_t)p.B * blocks_per_row));
-  mamba_decode_kernel<N, ACT><<<grid, dim3(64 * wpb), 0, st>>>(p, blocks_per_row);
+  mamba_decode_kernel<N, ACT, RG><<<grid, dim3(64 * wpb), 0, st>>>(p, blocks_per_row);
   return hipGetLastError();
 }
 
+// 2-wave blocks of mamba_rg row groups per wave where that gives every CU a
+// block (measured at N = 16: B = 256, D = 4096 25.9 us against 26.6 with
+// 1-wave blocks, 26.7 with half the rows per wave and 27.4 with 4 waves);
+// below that, 1-wave blocks and then half and a quarter of the rows per wave
+// until every CU has one (the finest otherwise): B = 1 / 8, D = 1536, N = 16
+// 2.93 / 3.41 us with 2-wave blocks against 2.29 / 2.98 with 1-wave blocks of
+// half the rows.
+template <int N, int ACT>
+hipError_t launch_m(const MambaParams& p, const Launch& l, int n_cu, hipStream_t st) {
+  constexpr int RG = mamba_rg<N>();
+  if (l.fixed) return launch_m_rg<N, ACT, RG>(p, min(l.wpb, 4), st);
+  auto blocks = [&](int wpb, int rg) {
+    const int rows = wpb * rg * RowLayout<N>::RPI;
+    return (int64_t)p.B * ((p.Dm + rows - 1) / rows);
+  };
+  if (blocks(2, RG) >= n_cu) return launch_m_rg<N, ACT, RG>(p, 2, st);
+  if (blocks(1, RG) >= n_cu) return launch_m_rg<N, ACT, RG>(p, 1, st);
+  constexpr int RG2 = RG / 2 > 1 ? RG / 2 : 1;
+  if constexpr (RG2 < RG) {
+    if (blocks(1, RG2) >= n_cu) return launch_m_rg<N, ACT, RG2>(p, 1, st);
+  }
+  constexpr int RG4 = RG2 / 2 > 1 ? RG2 / 2 : 1;
+  return launch_m_rg<N, ACT, RG4>(p, 1, st);
+}
+
 template <int N>
-hipError_t launch_mact(const MambaParams& p, const Launch& l, hipStream_t st) {
+hipError_t launch_mact(const MambaParams& p, const Launch& l, int n_cu, hipStream_t st) {
   switch (p.act_dt) {
-    case SSMD_F32: return launch_m<N, SSMD_F32>(p, l, st);
-    case SSMD_BF16: return launch_m<N, SSMD_BF16>(p, l, st);
-    default: return launch_m<N, SSMD_F16>(p, l, st);
+    case SSMD_F32: return launch_m<N, SSMD_F32>(p, l, n_cu, st);
+    case SSMD_BF16: return launch_m<N, SSMD_BF16>(p, l, n_cu, st);
+    default: return launch_m<N, SSMD_F16>(p, l, n_cu, st);
   }
 }
 
 }  // namespace
 
-hipError_t launch_mamba(const MambaParams& p, const Launch& l, hipStream_t st) {
+hipError_t launch_mamba(const MambaParams& p, const Launch& l, int n_cu, hipStream_t st) {
   switch (p.N) {
-    case 16: return launch_mact<16>(p, l, st);
-    case 32: return launch_mact<32>(p, l, st);
-    case 64: return launch_mact<64>(p, l, st);
-    case 128: return launch_mact<128>(p, l, st);
-    case 256: return launch_mact<256>(p, l, st);
+    case 16: return launch_mact<16>(p, l, n_cu, st);
+    case 32: return launch_mact<32>(p, l, n_cu, st);
+    case 64: return launch_mact<64>(p, l, n_cu, st);
+    case 128: return launch_mact<128>(p, l, n_cu, st);
+    case 256: return launch_mact<256>(p, l, n_cu, st);
     default: return hipErrorInvalidValue;
   }
 }

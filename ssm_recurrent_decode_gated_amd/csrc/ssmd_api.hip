@@ -533,7 +533,9 @@ int mamba_decode_step(const void* x, const void* dt, const float* A, const void*
   p.N = N;
   p.act_dt = act_dtype;
   p.out_dt = out_dtype;
-  return launch_status(ssmd::launch_mamba(p, launch_for(), stream), fn);
+  int n_cu = 0;
+  if (int rc2 = cu_count(&n_cu)) return rc2;
+  return launch_status(ssmd::launch_mamba(p, launch_for(), n_cu, stream), fn);
 }
 
 int64_t mamba_scan_workspace_bytes(int32_t B, int32_t T, int32_t Dm, int32_t N) {

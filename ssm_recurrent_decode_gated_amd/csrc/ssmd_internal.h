@@ -167,7 +167,7 @@ int64_t gdn_chunk_workspace_floats(int B, int T, int HV, int K, int V, bool norm
 hipError_t gdn_chunk_scratch(void** ptr);
 // Largest V the multi-token kernel takes with the gated RMSNorm (one block per head).
 int gdn_multi_max_norm_rows(int K);
-hipError_t launch_mamba(const MambaParams& p, const Launch& l, hipStream_t s);
+hipError_t launch_mamba(const MambaParams& p, const Launch& l, int n_cu, hipStream_t s);
 hipError_t launch_mamba_scan(const MambaScanParams& p, int n_cu, hipStream_t s);
 // Chunking of a Mamba scan on a device of n_cu compute units with ws_bytes of
 // workspace: chunk length *Lc and count *nck (1 when ws_bytes is too small).
