@@ -10,8 +10,8 @@
 // state). In-place streams on this part run faster the less each block and
 // wave holds: many short bursts in flight at once keep HBM busier than a few
 // long ones (a plain in-place copy: 5.6 TB/s with 64 KB per block, 6.3 with
-// 8 KB, 6.6 with 4 KB). Small batches, with at most two full-height units per
-// CU, launch one block per 128-row unit.
+// 8 KB, 6.6 with 4 KB). Small batches launch one block per 16-row tile (up
+// to B = 8 at HV = 32) or per 128-row unit (at most two per CU).
 #include "ssmd_device.h"
 #include "ssmd_internal.h"
 
@@ -26,7 +26,7 @@ constexpr int pf_rg() {
 
 // VF: the unit's v values are loaded ahead of its state rows, so the
 // conversion of v waits for nothing but v and each row group is computed and
-// stored as it arrives (used where a CU holds a single 1-wave block).
+// stored as it arrives (used at small batches, a few 1-wave blocks per CU).
 template <int K, int ACT, bool VEC, int RG, bool VF>
 __global__ __launch_bounds__(512) void gdn_decode_pf_kernel(GdnParams p, int tiles_per_head,
                                                             int rows_per_tile, int n_units) {
@@ -187,19 +187,22 @@ hipError_t launch_pf_k(const GdnParams& p, const Launch& l, int n_cu, hipStream_
   if constexpr (RG > 1) {
     if (units_for(4, RG) > 2LL * n_cu) return launch_pf_rg<K, ACT, VEC, 1>(p, 1, units_for(1, 1), st);
   }
-  // Small batches (measured at HV = 32, K = V = 128): narrower blocks until
-  // every CU has a unit, then, if even 1-wave blocks leave CUs idle, half the
-  // rows per wave, with v loaded ahead of the state (B = 1: 3.6 us; 4.1 with
-  // v loaded beside each row group, 4.7 with 32-row units and 5.5 with 4-wave
-  // blocks); one block per unit, all state loads in flight at once,
-  // while that is at most two per CU (B = 16: 12.5 us against 13.9
+  // Small batches (measured at HV = 32, K = V = 128, graph replay): up to
+  // four 1-wave units of the full row-group depth per CU (B <= 8), 1-wave
+  // blocks of half the rows per wave, one per unit, with v loaded ahead of the
+  // state (B = 1 / 2 / 4 / 8: 3.6 / 4.3 / 5.1 / 7.2 us, against 3.6 / 5.2 /
+  // 5.9 / 7.5 with 32-row 1- or 2-wave blocks; B = 1 with 8-row tiles 3.8,
+  // with v loaded beside each row group 4.1, with 4-wave blocks 5.5; the
+  // same shape at B = 16 15.2 against 12.6). Beyond that, narrower blocks
+  // until every CU has a unit; one block per unit, all state loads in flight
+  // at once, while that is at most two per CU (B = 16: 12.5 us against 13.9
   // persistent; 2-wave or 1-wave blocks, or v ahead of the state, 12.6-13.1);
   // beyond that one persistent block per CU (B = 64: 50.2 us against 52.1
   // with one block per unit).
   auto grid_for = [&](int64_t u) { return u <= 2LL * n_cu ? u : (int64_t)n_cu; };
   if constexpr (RG >= 2) {
-    if (units_for(1, RG) < n_cu)
-      return launch_pf_rg<K, ACT, VEC, RG / 2, true>(p, 1, grid_for(units_for(1, RG / 2)), st);
+    if (units_for(1, RG) <= 4LL * n_cu)
+      return launch_pf_rg<K, ACT, VEC, RG / 2, true>(p, 1, units_for(1, RG / 2), st);
   }
   int wpb = 4;
   while (wpb > 1 && units_for(wpb, RG) < n_cu) wpb /= 2;
